@@ -1,0 +1,326 @@
+/*
+ * dropkv_oracle.c -- plain, slow, float64 CPU reference for DropKV scoring,
+ * selection and compaction.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product path
+ * (libdropkv, HIP kernels) never calls it, and the two share no code.
+ *
+ * What it follows (DropKV: Decoupling Residual-Output Perturbation for
+ * Near-Optimal KV-Cache Eviction, arXiv 2610.22130, as described on the four
+ * pages studied):
+ *   - Section 3.1 / Appendix C.2: deleting token j from one query's softmax
+ *     changes the output a = sum_j p_j v_j by  Delta_j = p_j/(1-p_j) (a - v_j).
+ *   - Section 3.3 and the third-party notes' "Core equation": the score of token j
+ *     is  s_j = sum over the tail-window queries t of ||Delta_j^(t)||^2.
+ *   - The third-party notes' description of "Algorithm 1": query heads that share
+ *     a physical KV head are averaged; MaxPool1D smooths the scores; the recent
+ *     observation window is set to +inf; the smallest scores are evicted; a
+ *     probability that rounds to 1 is rejected rather than epsilon-patched.
+ *   - Section 2.2: eviction removes the tokens from the resident cache
+ *     (compaction keeps the surviving rows).
+ *
+ * Readings taken where the pages leave a step open (all listed in the design doc):
+ *   - q-head h uses KV head g = h / G, G = Hq / Hkv (contiguous groups).
+ *   - aggregation: sum over the w window queries, arithmetic mean over the G
+ *     heads of a group.
+ *   - causality is tail-aligned: window query t sits at position n-w+t and sees
+ *     keys j <= n-w+t (itself included).
+ *   - logits are q.k / sqrt(d), d = head dimension; inputs are already
+ *     position-encoded.
+ *   - MaxPool1D has stride 1, window `pool` (odd), radius r=(pool-1)/2, and
+ *     ignores out-of-range neighbours; it runs over all n raw scores, window
+ *     positions included, and the +inf protection of positions >= n-w comes after.
+ *   - the budget b counts kept tokens per KV head including the window;
+ *     k = n - b are evicted by ascending (score, index), so among equal scores
+ *     the older token goes first; kept indices are listed in ascending order.
+ *   - singular rows: only a row's arg-max j* can have p > 1/2; its probability
+ *     p* = 1/(1 + S_excl) (S_excl = sum over j != j* of exp(l_j - l_j*)) rounds to
+ *     1.0 in binary64 exactly when S_excl <= 2^-53.  Any such row rejects the
+ *     whole call (ORC_ESINGULAR).
+ *   - for j*, the algebraically identical form Delta_j* = p*(abar - v_j*) with
+ *     abar the output over the other tokens is used, which stays accurate as
+ *     p* -> 1; every other token has p_j <= 1/2 and uses the closed form.
+ *   - non-finite inputs reject the call (ENONFINITE); a finite score above
+ *     FLT_MAX, which the fp32 output cannot hold, rejects it with ERANGE.
+ *
+ * Inputs are bf16 bit patterns (uint16), widened exactly to double.
+ * Layouts: q [Hq][w][d], k and v [Hkv][n][d], scores [Hkv][n].
+ */
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_EINVAL 1
+#define ORC_ESINGULAR 2
+#define ORC_ENONFINITE 3
+#define ORC_ERANGE 4
+#define ORC_ENOMEM 6
+
+static double bf16_to_double(uint16_t b) {
+    uint32_t u = ((uint32_t)b) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static int bf16_is_finite(uint16_t b) { return (b & 0x7F80u) != 0x7F80u; }
+
+static int check_shapes(int64_t n, int w, int hq, int hkv, int d) {
+    if (n < 1 || w < 1 || w > n || hq < 1 || hkv < 1 || d < 1) return ORC_EINVAL;
+    if (hq % hkv != 0) return ORC_EINVAL;
+    return ORC_OK;
+}
+
+/*
+ * One window query (one row): softmax over the keys it sees, its output a, and
+ * the per-token contributions ||Delta_j||^2 added into raw[0..P].
+ * Returns ORC_ESINGULAR if p* rounds to 1.
+ */
+static int score_one_row(const double *q, const double *K, const double *V, int64_t P, int d,
+                         double *l, double *a, double *abar, double *raw) {
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+    /* logits l_j = q . k_j / sqrt(d), j = 0..P */
+    for (int64_t j = 0; j <= P; ++j) {
+        double s = 0.0;
+        for (int i = 0; i < d; ++i) s += q[i] * K[j * d + i];
+        l[j] = s * inv_sqrt_d;
+    }
+    /* maximum and its first position j* */
+    int64_t jstar = 0;
+    for (int64_t j = 1; j <= P; ++j)
+        if (l[j] > l[jstar]) jstar = j;
+    const double m = l[jstar];
+    /* e_j = exp(l_j - m); S = sum e_j; S_excl = sum over j != j* (e_j* = 1) */
+    double S = 0.0, S_excl = 0.0;
+    for (int64_t j = 0; j <= P; ++j) {
+        l[j] = exp(l[j] - m); /* l now holds e_j */
+        S += l[j];
+        if (j != jstar) S_excl += l[j];
+    }
+    if (S_excl <= ldexp(1.0, -53)) return ORC_ESINGULAR;
+    /* a = sum_j p_j v_j ;  abar = sum_{j != j*} e_j v_j / S_excl */
+    for (int i = 0; i < d; ++i) { a[i] = 0.0; abar[i] = 0.0; }
+    for (int64_t j = 0; j <= P; ++j) {
+        const double pj = l[j] / S;
+        for (int i = 0; i < d; ++i) a[i] += pj * V[j * d + i];
+        if (j != jstar) {
+            const double wj = l[j] / S_excl;
+            for (int i = 0; i < d; ++i) abar[i] += wj * V[j * d + i];
+        }
+    }
+    /* ||Delta_j||^2 for every visible token */
+    for (int64_t j = 0; j <= P; ++j) {
+        const double pj = l[j] / S;
+        double dist2 = 0.0, c;
+        if (j == jstar) {
+            /* Delta_j* = p* (abar - v_j*) */
+            for (int i = 0; i < d; ++i) {
+                const double r = abar[i] - V[j * d + i];
+                dist2 += r * r;
+            }
+            c = pj * pj * dist2;
+        } else {
+            /* Delta_j = p_j / (1 - p_j) (a - v_j), with 1 - p_j = (S - e_j) / S */
+            const double one_minus = (S - l[j]) / S;
+            const double odds = pj / one_minus;
+            for (int i = 0; i < d; ++i) {
+                const double r = a[i] - V[j * d + i];
+                dist2 += r * r;
+            }
+            c = odds * odds * dist2;
+        }
+        raw[j] += c;
+    }
+    return ORC_OK;
+}
+
+/*
+ * Raw (un-pooled, un-protected) head-averaged scores:
+ *   raw[g][j] = (1/G) * sum_{h in group g} sum_{t} ||Delta_j^(h,t)||^2,
+ * with Delta = 0 for keys a query does not see.
+ */
+int oracle_raw_scores(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t n, int w,
+                      int hq, int hkv, int d, int nthreads, double *raw) {
+    int rc = check_shapes(n, w, hq, hkv, d);
+    if (rc) return rc;
+    const int G = hq / hkv;
+    /* non-finite inputs reject the call */
+    for (int64_t i = 0; i < (int64_t)hq * w * d; ++i)
+        if (!bf16_is_finite(q[i])) return ORC_ENONFINITE;
+    for (int64_t i = 0; i < (int64_t)hkv * n * d; ++i)
+        if (!bf16_is_finite(k[i]) || !bf16_is_finite(v[i])) return ORC_ENONFINITE;
+
+    int status = ORC_OK;
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int g = 0; g < hkv; ++g) {
+        double *K = malloc(sizeof(double) * (size_t)n * d);
+        double *V = malloc(sizeof(double) * (size_t)n * d);
+        double *l = malloc(sizeof(double) * (size_t)n);
+        double *a = malloc(sizeof(double) * (size_t)d);
+        double *abar = malloc(sizeof(double) * (size_t)d);
+        double *qq = malloc(sizeof(double) * (size_t)d);
+        double *rg = raw + (size_t)g * n;
+        int local = ORC_OK;
+        if (!K || !V || !l || !a || !abar || !qq) local = ORC_ENOMEM;
+        if (local == ORC_OK) {
+            for (int64_t i = 0; i < n * d; ++i) {
+                K[i] = bf16_to_double(k[(size_t)g * n * d + i]);
+                V[i] = bf16_to_double(v[(size_t)g * n * d + i]);
+            }
+            for (int64_t j = 0; j < n; ++j) rg[j] = 0.0;
+            for (int h = g * G; h < (g + 1) * G && local == ORC_OK; ++h) {
+                for (int t = 0; t < w && local == ORC_OK; ++t) {
+                    for (int i = 0; i < d; ++i)
+                        qq[i] = bf16_to_double(q[((size_t)h * w + t) * d + i]);
+                    const int64_t P = n - w + t; /* last key this query sees */
+                    local = score_one_row(qq, K, V, P, d, l, a, abar, rg);
+                }
+            }
+            for (int64_t j = 0; j < n; ++j) rg[j] /= (double)G;
+        }
+        free(K); free(V); free(l); free(a); free(abar); free(qq);
+        if (local != ORC_OK) {
+#pragma omp critical
+            { if (local > status) status = local; }
+        }
+    }
+    return status;
+}
+
+/* MaxPool1D (stride 1, odd window, out-of-range neighbours ignored), then +inf
+ * on the last w positions of every head.  ERANGE if a raw score exceeds FLT_MAX. */
+int oracle_pool_protect(const double *raw, int64_t n, int hkv, int w, int pool, double *scores) {
+    if (n < 1 || hkv < 1 || w < 1 || w > n || pool < 1 || pool % 2 == 0) return ORC_EINVAL;
+    const int64_t r = (pool - 1) / 2;
+    for (int64_t i = 0; i < (int64_t)hkv * n; ++i)
+        if (raw[i] > (double)FLT_MAX) return ORC_ERANGE;
+    for (int g = 0; g < hkv; ++g) {
+        const double *x = raw + (size_t)g * n;
+        double *y = scores + (size_t)g * n;
+        for (int64_t j = 0; j < n; ++j) {
+            const int64_t lo = j - r < 0 ? 0 : j - r;
+            const int64_t hi = j + r > n - 1 ? n - 1 : j + r;
+            double mx = x[lo];
+            for (int64_t i = lo + 1; i <= hi; ++i)
+                if (x[i] > mx) mx = x[i];
+            y[j] = (j >= n - w) ? INFINITY : mx;
+        }
+    }
+    return ORC_OK;
+}
+
+/* Full scoring: raw scores, pooling, protection. */
+int oracle_score(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t n, int w, int hq,
+                 int hkv, int d, int pool, int nthreads, double *scores) {
+    if (pool < 1 || pool % 2 == 0) return ORC_EINVAL;
+    double *raw = malloc(sizeof(double) * (size_t)hkv * n);
+    if (!raw) return ORC_ENOMEM;
+    int rc = oracle_raw_scores(q, k, v, n, w, hq, hkv, d, nthreads, raw);
+    if (rc == ORC_OK) rc = oracle_pool_protect(raw, n, hkv, w, pool, scores);
+    free(raw);
+    return rc;
+}
+
+/* ---- selection: evict the k = n - budget smallest by (score, index) ---- */
+typedef struct { double s; int64_t j; } keyed;
+
+static int keyed_cmp(const void *x, const void *y) {
+    const keyed *a = x, *b = y;
+    if (a->s < b->s) return -1;
+    if (a->s > b->s) return 1;
+    return (a->j > b->j) - (a->j < b->j);
+}
+
+static int index_cmp(const void *x, const void *y) {
+    const int32_t a = *(const int32_t *)x, b = *(const int32_t *)y;
+    return (a > b) - (a < b);
+}
+
+/* keep[g][0..budget) = indices that survive, ascending.  Scores must not be NaN. */
+int oracle_select(const double *scores, int hkv, int64_t n, int64_t budget, int32_t *keep) {
+    if (hkv < 1 || n < 1 || budget < 0 || budget > n) return ORC_EINVAL;
+    keyed *tmp = malloc(sizeof(keyed) * (size_t)n);
+    if (!tmp) return ORC_ENOMEM;
+    const int64_t evict = n - budget;
+    for (int g = 0; g < hkv; ++g) {
+        for (int64_t j = 0; j < n; ++j) {
+            tmp[j].s = scores[(size_t)g * n + j];
+            if (tmp[j].s != tmp[j].s) { free(tmp); return ORC_ENONFINITE; }
+            tmp[j].j = j;
+        }
+        qsort(tmp, (size_t)n, sizeof(keyed), keyed_cmp);
+        int32_t *kg = keep + (size_t)g * budget;
+        for (int64_t i = evict; i < n; ++i) kg[i - evict] = (int32_t)tmp[i].j;
+        qsort(kg, (size_t)budget, sizeof(int32_t), index_cmp);
+    }
+    free(tmp);
+    return ORC_OK;
+}
+
+/* Compaction: out[g][r][:] = in[g][keep[g][r]][:] as exact bit copies. */
+int oracle_compact(const uint16_t *in, int hkv, int64_t n, int d, const int32_t *keep,
+                   int64_t budget, uint16_t *out) {
+    for (int g = 0; g < hkv; ++g)
+        for (int64_t r = 0; r < budget; ++r) {
+            const int64_t j = keep[(size_t)g * budget + r];
+            if (j < 0 || j >= n) return ORC_EINVAL;
+            memcpy(out + ((size_t)g * budget + r) * d, in + ((size_t)g * n + j) * d,
+                   sizeof(uint16_t) * (size_t)d);
+        }
+    return ORC_OK;
+}
+
+/*
+ * Diagnostics for the tests: per window query (h, t), the probabilities over
+ * keys (zero for unseen keys), the output a and S_excl.
+ * p [hq][w][n], a [hq][w][d], s_excl [hq][w].
+ */
+int oracle_window_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t n,
+                            int w, int hq, int hkv, int d, double *p, double *a, double *s_excl) {
+    int rc = check_shapes(n, w, hq, hkv, d);
+    if (rc) return rc;
+    const int G = hq / hkv;
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+    double *l = malloc(sizeof(double) * (size_t)n);
+    if (!l) return ORC_ENOMEM;
+    for (int h = 0; h < hq; ++h) {
+        const int g = h / G;
+        for (int t = 0; t < w; ++t) {
+            const int64_t P = n - w + t;
+            const uint16_t *qr = q + ((size_t)h * w + t) * d;
+            for (int64_t j = 0; j <= P; ++j) {
+                double s = 0.0;
+                for (int i = 0; i < d; ++i)
+                    s += bf16_to_double(qr[i]) * bf16_to_double(k[((size_t)g * n + j) * d + i]);
+                l[j] = s * inv_sqrt_d;
+            }
+            int64_t jstar = 0;
+            for (int64_t j = 1; j <= P; ++j)
+                if (l[j] > l[jstar]) jstar = j;
+            const double m = l[jstar];
+            double S = 0.0, Sx = 0.0;
+            for (int64_t j = 0; j <= P; ++j) {
+                l[j] = exp(l[j] - m);
+                S += l[j];
+                if (j != jstar) Sx += l[j];
+            }
+            double *pr = p + ((size_t)h * w + t) * n;
+            double *ar = a + ((size_t)h * w + t) * d;
+            for (int i = 0; i < d; ++i) ar[i] = 0.0;
+            for (int64_t j = 0; j < n; ++j) {
+                pr[j] = j <= P ? l[j] / S : 0.0;
+                if (j <= P)
+                    for (int i = 0; i < d; ++i)
+                        ar[i] += pr[j] * bf16_to_double(v[((size_t)g * n + j) * d + i]);
+            }
+            s_excl[(size_t)h * w + t] = Sx;
+        }
+    }
+    free(l);
+    return ORC_OK;
+}

@@ -1,0 +1,105 @@
+"""Independent float64 brute force used to pin the oracle.
+
+Nothing here uses the perturbation closed form: every perturbation is obtained
+by actually deleting tokens and recomputing the softmax over the remaining keys
+(DropKV, Section 3.1 and Appendix C.2 define Delta as exactly this change of
+the attention output).  K/V heads are expanded to query heads with
+``np.repeat`` (the repeat_kv layout) instead of the oracle's h // G indexing.
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+
+from attention_perturbation_scoring_amd.workload import bf16_to_f32
+
+
+def widen(b):
+    return bf16_to_f32(b).astype(np.float64)
+
+
+def expand_heads(q, k, v):
+    """bf16 bits -> float64 with K/V repeated to every query head."""
+    qf, kf, vf = widen(q), widen(k), widen(v)
+    G = qf.shape[0] // kf.shape[0]
+    return qf, np.repeat(kf, G, axis=0), np.repeat(vf, G, axis=0), G
+
+
+def attend(qrow, K, V, keys):
+    """softmax(K[keys] q / sqrt(d)) and the output, over the listed keys only."""
+    d = qrow.shape[0]
+    l = K[keys] @ qrow / np.sqrt(d)
+    e = np.exp(l - l.max())
+    p = e / e.sum()
+    return p, p @ V[keys]
+
+
+def deletion_raw(q, k, v):
+    """raw[g][j] = mean over the G heads of sum over t of ||a_without_j - a||^2."""
+    qf, Kh, Vh, G = expand_heads(q, k, v)
+    Hq, w, d = qf.shape
+    n = Kh.shape[1]
+    raw = np.zeros((Hq // G, n))
+    for h in range(Hq):
+        for t in range(w):
+            P = n - w + t
+            keys = np.arange(P + 1)
+            _, a = attend(qf[h, t], Kh[h], Vh[h], keys)
+            for j in range(P + 1):
+                _, a_del = attend(qf[h, t], Kh[h], Vh[h], keys[keys != j])
+                raw[h // G, j] += np.sum((a_del - a) ** 2)
+    return raw / G
+
+
+def joint_objective_sq(q, k, v, g, J):
+    """F(J)^2 = sum over the group's (h, t) of ||a_without_J - a||^2 (KV head g)."""
+    qf, Kh, Vh, G = expand_heads(q, k, v)
+    Hq, w, d = qf.shape
+    n = Kh.shape[1]
+    J = set(int(x) for x in J)
+    tot = 0.0
+    for h in range(g * G, (g + 1) * G):
+        for t in range(w):
+            P = n - w + t
+            keys = np.arange(P + 1)
+            _, a = attend(qf[h, t], Kh[h], Vh[h], keys)
+            kept = np.array([j for j in keys if j not in J])
+            _, a_del = attend(qf[h, t], Kh[h], Vh[h], kept)
+            tot += np.sum((a_del - a) ** 2)
+    return tot
+
+
+def all_subsets_objective_sq(q, k, v, g, cand, kk):
+    """F(J)^2 for every kk-subset J of cand (vectorised), with the subsets."""
+    qf, Kh, Vh, G = expand_heads(q, k, v)
+    Hq, w, d = qf.shape
+    n = Kh.shape[1]
+    cand = np.asarray(cand)
+    subsets = np.array(list(itertools.combinations(range(len(cand)), kk)), dtype=np.int64)
+    mask = np.zeros((len(subsets), n))
+    mask[np.arange(len(subsets))[:, None], cand[subsets]] = 1.0
+    keepm = 1.0 - mask
+    tot = np.zeros(len(subsets))
+    for h in range(g * G, (g + 1) * G):
+        for t in range(w):
+            P = n - w + t
+            l = np.full(n, -np.inf)
+            l[:P + 1] = Kh[h, :P + 1] @ qf[h, t] / np.sqrt(d)
+            e = np.exp(l - l.max())
+            a = (e @ Vh[h]) / e.sum()
+            num = (keepm * e) @ Vh[h]
+            den = keepm @ e
+            a_del = num / den[:, None]
+            tot += np.sum((a_del - a) ** 2, axis=1)
+    return cand[subsets], tot
+
+
+def sort_select(scores, budget):
+    """Keep list by a full sort on (score, index); evict the n - budget first."""
+    Hkv, n = scores.shape
+    out = np.zeros((Hkv, budget), dtype=np.int32)
+    for g in range(Hkv):
+        order = sorted(range(n), key=lambda j: (float(scores[g, j]), j))
+        out[g] = np.sort(np.array(order[n - budget:], dtype=np.int32))
+    return out
