@@ -1,0 +1,273 @@
+// libdropkv host side: argument checks, scratch ownership, launch sequencing,
+// the device error latch and optional per-kernel event timing.  The C ABI is
+// declared (and documented) in include/dropkv.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/dropkv.h"
+#include "common.h"
+
+using namespace dropkv;
+
+struct ProfRec {
+  std::string name;
+  hipEvent_t start, stop;
+};
+
+struct dropkv_ctx {
+  int device = 0;
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  uint32_t* latch = nullptr;       // device word
+  uint32_t* latch_host = nullptr;  // pinned read-back
+  bool prof = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> free_events;
+  hipEvent_t pending_start = nullptr;
+};
+
+namespace {
+
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) { ok = false; return; }
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+hipEvent_t get_event(dropkv_ctx* c) {
+  if (!c->free_events.empty()) {
+    hipEvent_t e = c->free_events.back();
+    c->free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+int to_status(hipError_t e) {
+  if (e == hipSuccess) return DROPKV_OK;
+  if (e == hipErrorOutOfMemory) return DROPKV_ENOMEM;
+  return DROPKV_EDEVICE;
+}
+
+}  // namespace
+
+namespace dropkv {
+void prof_begin(void* ctx, const char* name, hipStream_t s) {
+  (void)name;
+  auto* c = static_cast<dropkv_ctx*>(ctx);
+  if (!c || !c->prof) return;
+  c->pending_start = get_event(c);
+  if (c->pending_start) (void)hipEventRecord(c->pending_start, s);
+}
+void prof_end(void* ctx, const char* name, hipStream_t s) {
+  auto* c = static_cast<dropkv_ctx*>(ctx);
+  if (!c || !c->prof || !c->pending_start) return;
+  hipEvent_t stop = get_event(c);
+  if (!stop) return;
+  (void)hipEventRecord(stop, s);
+  c->recs.push_back(ProfRec{name, c->pending_start, stop});
+  c->pending_start = nullptr;
+}
+}  // namespace dropkv
+
+extern "C" {
+
+int dropkv_create(dropkv_ctx** out, int device) {
+  if (!out) return DROPKV_EINVAL;
+  *out = nullptr;
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || device < 0 || device >= count) return DROPKV_EINVAL;
+  DeviceGuard guard(device);
+  if (!guard.ok) return DROPKV_EDEVICE;
+  auto* c = new dropkv_ctx();
+  c->device = device;
+  hipError_t e = hipMalloc(&c->latch, 256);
+  if (e == hipSuccess) e = hipMemset(c->latch, 0, 256);
+  if (e == hipSuccess) e = hipHostMalloc(&c->latch_host, sizeof(uint32_t));
+  if (e != hipSuccess) {
+    if (c->latch) (void)hipFree(c->latch);
+    delete c;
+    return to_status(e);
+  }
+  *out = c;
+  return DROPKV_OK;
+}
+
+int dropkv_destroy(dropkv_ctx* c) {
+  if (!c) return DROPKV_EINVAL;
+  DeviceGuard guard(c->device);
+  (void)hipDeviceSynchronize();
+  for (auto& r : c->recs) { (void)hipEventDestroy(r.start); (void)hipEventDestroy(r.stop); }
+  for (auto e : c->free_events) (void)hipEventDestroy(e);
+  if (c->scratch) (void)hipFree(c->scratch);
+  if (c->latch) (void)hipFree(c->latch);
+  if (c->latch_host) (void)hipHostFree(c->latch_host);
+  delete c;
+  return DROPKV_OK;
+}
+
+int dropkv_plan_splits(int64_t n, int32_t Hkv, int32_t* splits) {
+  if (!splits || n < 1 || Hkv < 1) return DROPKV_EINVAL;
+  int64_t len = 0;
+  *splits = plan_splits(n, Hkv, &len);
+  return DROPKV_OK;
+}
+
+int dropkv_score(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
+                 const uint16_t* v_cache, int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int32_t d,
+                 int32_t pool, float* scores, void* stream) {
+  if (!c) return DROPKV_EINVAL;
+  if (!aligned16(q_win) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(scores))
+    return DROPKV_EINVAL;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return DROPKV_EINVAL;
+  if (n < 1 || n >= (int64_t(1) << 31)) return DROPKV_EINVAL;
+  if (w < 1 || w > n) return DROPKV_EINVAL;
+  if (pool < 1 || pool % 2 == 0 || pool > 129) return DROPKV_EINVAL;
+  if (d < 8 || d % 8 != 0 || d > 256) return DROPKV_EINVAL;
+  const int G = Hq / Hkv;
+  if ((int64_t)G * w > kRows) return DROPKV_EINVAL;
+  DeviceGuard guard(c->device);
+  if (!guard.ok) return DROPKV_EDEVICE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  ScoreArgs a{};
+  a.q = q_win; a.k = k_cache; a.v = v_cache; a.scores = scores;
+  a.n = n; a.w = w; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.G = G; a.M = G * w; a.pool = pool;
+  a.DP = (d + 31) / 32 * 32;
+  a.splits = plan_splits(n, Hkv, &a.split_len);
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+  a.latch = c->latch;
+  const size_t need = score_scratch_bytes(Hkv, a.splits, a.DP);
+  if (need > c->scratch_bytes) {
+    if (c->scratch) {
+      (void)hipStreamSynchronize(s);
+      (void)hipDeviceSynchronize();
+      (void)hipFree(c->scratch);
+      c->scratch = nullptr;
+      c->scratch_bytes = 0;
+    }
+    hipError_t e = hipMalloc(&c->scratch, need);
+    if (e != hipSuccess) { c->scratch = nullptr; return DROPKV_ENOMEM; }
+    c->scratch_bytes = need;
+  }
+  carve_scratch(c->scratch, Hkv, a.splits, a.DP, &a.part, &a.rs);
+  return to_status(launch_score(c, a, s));
+}
+
+int dropkv_select(dropkv_ctx* c, const float* scores, int32_t Hkv, int64_t n, int64_t budget,
+                  int32_t* keep, void* stream) {
+  if (!c || !aligned16(scores)) return DROPKV_EINVAL;
+  if (Hkv < 1 || n < 1 || n >= (int64_t(1) << 31) || budget < 0 || budget > n) return DROPKV_EINVAL;
+  if (budget == 0) return DROPKV_OK;  // nothing to write
+  if (!aligned16(keep)) return DROPKV_EINVAL;
+  DeviceGuard guard(c->device);
+  if (!guard.ok) return DROPKV_EDEVICE;
+  return to_status(
+      launch_select(c, scores, Hkv, n, budget, keep, c->latch, static_cast<hipStream_t>(stream)));
+}
+
+int dropkv_compact(dropkv_ctx* c, const uint16_t* k, const uint16_t* v, int32_t Hkv, int64_t n,
+                   int32_t d, const int32_t* keep, int64_t budget, uint16_t* k_out,
+                   uint16_t* v_out, void* stream) {
+  if (!c) return DROPKV_EINVAL;
+  if (Hkv < 1 || n < 1 || n >= (int64_t(1) << 31) || d < 8 || d % 8 != 0 || d > 256)
+    return DROPKV_EINVAL;
+  if (budget < 0 || budget > n) return DROPKV_EINVAL;
+  if (budget == 0) return DROPKV_OK;  // nothing to write
+  if (!aligned16(k) || !aligned16(v) || !aligned16(keep) || !aligned16(k_out) || !aligned16(v_out))
+    return DROPKV_EINVAL;
+  DeviceGuard guard(c->device);
+  if (!guard.ok) return DROPKV_EDEVICE;
+  return to_status(launch_compact(c, k, v, Hkv, n, d, keep, budget, k_out, v_out, c->latch,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+int dropkv_sync(dropkv_ctx* c, void* stream) {
+  if (!c) return DROPKV_EINVAL;
+  DeviceGuard guard(c->device);
+  if (!guard.ok) return DROPKV_EDEVICE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(c->latch_host, c->latch, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return to_status(e);
+  const uint32_t bits = *c->latch_host;
+  if (bits) {
+    e = hipMemsetAsync(c->latch, 0, sizeof(uint32_t), s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return to_status(e);
+  }
+  if (bits & LATCH_NONFINITE) return DROPKV_ENONFINITE;
+  if (bits & LATCH_SINGULAR) return DROPKV_ESINGULAR;
+  if (bits & LATCH_RANGE) return DROPKV_ERANGE;
+  return DROPKV_OK;
+}
+
+const char* dropkv_strerror(int code) {
+  switch (code) {
+    case DROPKV_OK: return "ok";
+    case DROPKV_EINVAL: return "invalid argument";
+    case DROPKV_ESINGULAR: return "a window query puts probability that rounds to 1 on one key";
+    case DROPKV_ENONFINITE: return "non-finite input";
+    case DROPKV_ERANGE: return "value out of range";
+    case DROPKV_EDEVICE: return "HIP runtime error";
+    case DROPKV_ENOMEM: return "out of device memory";
+    default: return "unknown status";
+  }
+}
+
+int dropkv_profile_enable(dropkv_ctx* c, int on) {
+  if (!c) return DROPKV_EINVAL;
+  c->prof = on != 0;
+  return DROPKV_OK;
+}
+
+int dropkv_profile_reset(dropkv_ctx* c) {
+  if (!c) return DROPKV_EINVAL;
+  DeviceGuard guard(c->device);
+  for (auto& r : c->recs) {
+    (void)hipEventSynchronize(r.stop);
+    c->free_events.push_back(r.start);
+    c->free_events.push_back(r.stop);
+  }
+  c->recs.clear();
+  return DROPKV_OK;
+}
+
+int dropkv_profile_read(dropkv_ctx* c, const char* name, double* total_ms, int64_t* launches) {
+  if (!c || !name || !total_ms || !launches) return DROPKV_EINVAL;
+  DeviceGuard guard(c->device);
+  double tot = 0.0;
+  int64_t cnt = 0;
+  for (auto& r : c->recs) {
+    if (r.name != name) continue;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e != hipSuccess) return to_status(e);
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) return to_status(e);
+    tot += ms;
+    ++cnt;
+  }
+  *total_ms = tot;
+  *launches = cnt;
+  return DROPKV_OK;
+}
+
+}  // extern "C"

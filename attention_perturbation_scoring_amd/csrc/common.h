@@ -1,0 +1,84 @@
+// Internal declarations shared by libdropkv's translation units (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dropkv {
+
+typedef uint16_t u16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Device error latch bits (OR-ed by kernels, decoded by dropkv_sync).
+enum : uint32_t {
+  LATCH_NONFINITE = 1u,
+  LATCH_SINGULAR = 2u,
+  LATCH_RANGE = 4u,
+};
+
+constexpr int kRows = 32;        // window-query rows per KV head handled by one MFMA tile (G*w <= 32)
+constexpr int kTile = 32;        // tokens per MFMA tile
+constexpr int kWaves = 4;        // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kChunk2 = 512;     // tokens per pass-2 workgroup (before the pooling halo)
+
+// S_excl below this (argmax probability above ~0.94) routes the arg-max term
+// through the exact exclusion kernel instead of the fp32 output a.
+constexpr float kFixupThreshold = 0.0625f;
+
+// Per-row (window query) state produced by the merge, consumed by pass 2.
+struct RowState {
+  float* m2;      // [Hkv][32] running max of the logits, log2 units
+  float* lse2;    // [Hkv][32] log2 of the softmax normaliser
+  float* S;       // [Hkv][32] normaliser in units of the max
+  float* an2;     // [Hkv][32] ||a||^2
+  float* cstar;   // [Hkv][32] arg-max token's contribution ||Delta_j*||^2
+  int* jstar;     // [Hkv][32] arg-max token index (lowest on ties)
+  int* fix;       // [Hkv][32] 1 if the arg-max term needs the exclusion kernel
+  u16* a_hi;      // [Hkv][32][DP] bf16 high part of a
+  u16* a_lo;      // [Hkv][32][DP] bf16 remainder a - a_hi
+};
+
+struct Partials {
+  float* m2;      // [Hkv][splits][32]
+  float* S;       // [Hkv][splits][32]
+  float* Sx;      // [Hkv][splits][32]
+  int* jstar;     // [Hkv][splits][32]
+  int* bad;       // [Hkv][splits][32]
+  float* a;       // [Hkv][splits][32][DP] un-normalised output
+};
+
+struct ScoreArgs {
+  const u16* q;
+  const u16* k;
+  const u16* v;
+  float* scores;
+  int64_t n;
+  int w, Hq, Hkv, d, G, M, pool, DP;
+  int splits;
+  int64_t split_len;
+  float scale_log2;   // log2(e) / sqrt(d)
+  Partials part;
+  RowState rs;
+  uint32_t* latch;
+};
+
+// Profiling hooks implemented by the host library (no-ops unless enabled).
+struct ProfScope;
+void prof_begin(void* ctx, const char* name, hipStream_t s);
+void prof_end(void* ctx, const char* name, hipStream_t s);
+
+hipError_t launch_score(void* ctx, const ScoreArgs& a, hipStream_t s);
+hipError_t launch_select(void* ctx, const float* scores, int Hkv, int64_t n, int64_t budget,
+                         int32_t* keep, uint32_t* latch, hipStream_t s);
+hipError_t launch_compact(void* ctx, const u16* k, const u16* v, int Hkv, int64_t n, int d,
+                          const int32_t* keep, int64_t budget, u16* k_out, u16* v_out,
+                          uint32_t* latch, hipStream_t s);
+
+// Bytes of scratch the scoring pass needs for these sizes.
+size_t score_scratch_bytes(int Hkv, int splits, int DP);
+void carve_scratch(void* base, int Hkv, int splits, int DP, Partials* p, RowState* rs);
+int plan_splits(int64_t n, int Hkv, int64_t* split_len);
+
+}  // namespace dropkv

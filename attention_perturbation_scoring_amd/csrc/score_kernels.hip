@@ -1,0 +1,655 @@
+// DropKV scoring kernels for gfx950 (MI355X, CDNA4).
+//
+// What is computed (DropKV, arXiv 2610.22130: Section 3.1 / Appendix C.2 for the
+// single-token perturbation Delta_j = p_j/(1-p_j) (a - v_j); Section 3.3 and the
+// implementation notes' "Core equation" for the window sum of ||Delta_j||^2; the
+// notes' "Algorithm 1" for head averaging, MaxPool1D, +inf protection and the
+// rejection of probabilities that round to 1):
+//
+//   pass1  : per (KV head, sequence split) stream K and V once.  For the G*w = M
+//            window-query rows of the group: logits S^T = K Q^T on bf16 MFMA, an
+//            online softmax (running max, normaliser S, and S_excl = mass off the
+//            running arg-max, kept without cancellation) and the un-normalised
+//            output a^T += V^T P^T on MFMA with P split into bf16 hi + lo parts.
+//   merge  : per row, combine the split partials: final max, S, S_excl, arg-max
+//            j*, a = a_un / S, ||a||^2, a as bf16 hi + lo, the arg-max token's
+//            own term from a, and the singular / non-finite decisions.
+//   fixup  : (only rows whose arg-max holds probability above ~0.94) recompute
+//            the output over the other tokens exactly and take the arg-max term
+//            as p*^2 ||abar - v_j*||^2, which stays accurate as p* -> 1.
+//   pass2  : per (KV head, 512-token chunk + pooling halo) stream K and V again:
+//            logits Q K^T and A V^T (a as hi + lo) on MFMA, then per element
+//            p = 2^(l - lse), odds = p/(1-p), ||a - v||^2 = ||a||^2 - 2 a.v + ||v||^2,
+//            contribution odds^2 ||a - v||^2, summed over the M rows, divided by
+//            G; then max-pool over the chunk, +inf on the last w positions.
+//
+// Nothing of size O(n) besides the caller's score buffer is ever written.
+#include <float.h>
+#include <limits.h>
+
+#include "common.h"
+
+namespace dropkv {
+
+__device__ __forceinline__ bf16x8 load8(const u16* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ bf16x8 zero8() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, z);
+}
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float bf2f(u16 b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ int wave_min_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = min(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ int wave_or_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x |= __shfl_xor(x, o);
+  return x;
+}
+
+// ---------------------------------------------------------------- pass 1 --
+// Lane layout of the 32x32x16 bf16 MFMA (checked on gfx950): A[i][k] sits in
+// lane i + 32*(k/8), element k%8; B[k][j] in lane j + 32*(k/8), element k%8;
+// D[i][j] in lane j + 32*h, register v, with i = 8*(v/4) + 4*h + v%4.
+//
+// Pass 1 computes S^T = K Q^T (tokens x rows), so lane l owns query row l%32
+// and 16 of the tile's 32 tokens; the softmax statistics of a row stay within
+// the lane pair (l, l^32).  For PV it computes a^T = V^T P^T: P^T's operand is
+// taken straight from S^T's registers by ordering the MFMA's reduction slots as
+// token(kc, h, e) = 16*kc + 8*(e/4) + 4*h + e%4, and V^T's operand is gathered
+// from a per-wave LDS copy of the V tile in that same order.
+template <int DP>
+__global__ __launch_bounds__(kThreads) void pass1_kernel(ScoreArgs a) {
+  constexpr int NC = DP / 16;
+  constexpr int DB = DP / 32;
+  constexpr int LS = DP + 8;  // LDS row stride (u16): rows 4 apart land 16 banks apart
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  u16* lds = reinterpret_cast<u16*>(smem_raw);
+  __shared__ float sm_m[kWaves][kRows], sm_S[kWaves][kRows], sm_Sx[kWaves][kRows];
+  __shared__ int sm_j[kWaves][kRows], sm_bad[kWaves][kRows];
+
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int r = lane & 31, hh = lane >> 5;
+  const int g = blockIdx.x / a.splits, s = blockIdx.x % a.splits;
+  const int64_t jbeg = (int64_t)s * a.split_len;
+  const int64_t jend = min(a.n, jbeg + a.split_len);
+  const int ntiles = (int)((jend - jbeg + kTile - 1) / kTile);
+  const int d = a.d;
+  const u16* kg = a.k + (size_t)g * a.n * d;
+  const u16* vg = a.v + (size_t)g * a.n * d;
+  const bool row_ok = r < a.M;
+  const int64_t causal = row_ok ? a.n - a.w + (r % a.w) : -1;
+
+  bf16x8 qB[NC];
+  const u16* qrow = a.q + ((size_t)g * a.M + (row_ok ? r : 0)) * d;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int col = 16 * c + 8 * hh;
+    qB[c] = (row_ok && col < d) ? load8(qrow + col) : zero8();
+  }
+
+  float m = -INFINITY, S = 0.f, Sx = 0.f;
+  int jst = INT_MAX, bad = 0;
+  bool has = false;
+  f32x16 acc[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
+
+  u16* my = lds + wid * kTile * LS;
+  for (int t = wid; t < ntiles; t += kWaves) {
+    const int64_t j0 = jbeg + (int64_t)t * kTile;
+    const int64_t tok = j0 + r;
+    const bool tok_ok = tok < jend;
+    bf16x8 kA[NC], vv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int col = 16 * c + 8 * hh;
+      const bool ok = tok_ok && col < d;
+      kA[c] = ok ? load8(kg + tok * d + col) : zero8();
+      vv[c] = ok ? load8(vg + tok * d + col) : zero8();
+    }
+    f32x16 st;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) st[v] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) st = mfma32(kA[c], qB[c], st);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      *reinterpret_cast<u32x4*>(my + r * LS + 16 * c + 8 * hh) = __builtin_bit_cast(u32x4, vv[c]);
+
+    // online softmax for row r over this lane's 16 tokens + the partner lane's 16
+    float s2[16];
+    float lm = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t tv = j0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+      const bool valid = row_ok && tv < jend && tv <= causal;
+      const float x = st[v];
+      if (valid && !(fabsf(x) <= FLT_MAX)) bad = 1;
+      s2[v] = valid ? x * a.scale_log2 : -INFINITY;
+      lm = fmaxf(lm, s2[v]);
+    }
+    lm = fmaxf(lm, __shfl_xor(lm, 32));
+    int lj = INT_MAX;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int tv = (int)(j0 + 8 * (v >> 2) + 4 * hh + (v & 3));
+      if (s2[v] == lm && lm > -INFINITY) lj = min(lj, tv);
+    }
+    lj = min(lj, __shfl_xor(lj, 32));
+    const bool newmax = lm > m;
+    const float mn = newmax ? lm : m;
+    const bool live = mn > -INFINITY;
+    const float alpha = live ? ex2(m - mn) : 1.f;
+    float p[16];
+    float ts = 0.f, tx = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int tv = (int)(j0 + 8 * (v >> 2) + 4 * hh + (v & 3));
+      p[v] = live ? ex2(s2[v] - mn) : 0.f;
+      ts += p[v];
+      tx += (tv == lj) ? 0.f : p[v];
+    }
+    ts += __shfl_xor(ts, 32);
+    tx += __shfl_xor(tx, 32);
+    if (newmax) {
+      Sx = (Sx + (has ? 1.f : 0.f)) * alpha + tx;
+      jst = lj;
+      has = true;
+    } else {
+      Sx = Sx + ts;
+    }
+    S = S * alpha + ts;
+    m = mn;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[b][v] *= alpha;
+
+    bf16x8 ph[2], pl[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = p[8 * kc + e];
+        const __bf16 hi = (__bf16)x;
+        ph[kc][e] = hi;
+        pl[kc][e] = (__bf16)(x - (float)hi);
+      }
+    wave_sync_lds();
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        bf16x8 va;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tl = 16 * kc + 8 * (e >> 2) + 4 * hh + (e & 3);
+          va[e] = __builtin_bit_cast(__bf16, my[tl * LS + 32 * b + r]);
+        }
+        acc[b] = mfma32(va, ph[kc], acc[b]);
+        acc[b] = mfma32(va, pl[kc], acc[b]);
+      }
+    wave_sync_lds();
+  }
+
+  // ---- combine the four waves' states for each row (fixed order) ----
+  bad |= __shfl_xor(bad, 32);
+  if (hh == 0) {
+    sm_m[wid][r] = m;
+    sm_S[wid][r] = S;
+    sm_Sx[wid][r] = Sx;
+    sm_j[wid][r] = has ? jst : INT_MAX;
+    sm_bad[wid][r] = bad;
+  }
+  __syncthreads();
+  float Mf = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) Mf = fmaxf(Mf, sm_m[w][r]);
+  int wstar = -1, jbest = INT_MAX, badf = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    if (Mf > -INFINITY && sm_m[w][r] == Mf && sm_j[w][r] < jbest) {
+      jbest = sm_j[w][r];
+      wstar = w;
+    }
+    badf |= sm_bad[w][r];
+  }
+  float Sf = 0.f, Sxf = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float f = (sm_m[w][r] > -INFINITY) ? ex2(sm_m[w][r] - Mf) : 0.f;
+    Sf += sm_S[w][r] * f;
+    Sxf += (w == wstar) ? sm_Sx[w][r] * f : sm_S[w][r] * f;
+  }
+  const float myf = (m > -INFINITY) ? ex2(m - Mf) : 0.f;
+  __syncthreads();  // every wave is done with its V tile; reuse LDS as a float buffer
+  float* red = reinterpret_cast<float*>(smem_raw);
+  for (int w = 0; w < kWaves; ++w) {
+    if (wid == w) {
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int dd = 32 * b + 8 * (v >> 2) + 4 * hh + (v & 3);
+          const float x = acc[b][v] * myf;
+          float* dst = red + r * DP + dd;
+          *dst = (w == 0) ? x : *dst + x;
+        }
+    }
+    __syncthreads();
+  }
+  const size_t pb = ((size_t)g * a.splits + s) * kRows;
+  if (tid < kRows) {
+    a.part.m2[pb + r] = Mf;
+    a.part.S[pb + r] = Sf;
+    a.part.Sx[pb + r] = Sxf;
+    a.part.jstar[pb + r] = jbest;
+    a.part.bad[pb + r] = badf;
+  }
+  for (int i = tid; i < a.M * DP; i += kThreads) a.part.a[pb * DP + i] = red[i];
+}
+
+// ----------------------------------------------------------------- merge --
+// One wave per (KV head, row); 4 rows per workgroup, 8 workgroups per head.
+constexpr int kMaxSplits = 1024;
+
+template <int DP>
+__global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
+  __shared__ float sm_f[kWaves][kMaxSplits];
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = blockIdx.x / (kRows / kWaves);
+  const int r = (blockIdx.x % (kRows / kWaves)) * kWaves + wid;
+  const size_t ro = (size_t)g * kRows + r;
+  if (r >= a.M) {  // padded rows: zero operands so pass 2's MFMA rows stay inert
+    for (int dd = lane; dd < DP; dd += 64) {
+      a.rs.a_hi[ro * DP + dd] = 0;
+      a.rs.a_lo[ro * DP + dd] = 0;
+    }
+    if (lane == 0) {
+      a.rs.m2[ro] = 0.f; a.rs.lse2[ro] = 0.f; a.rs.S[ro] = 1.f; a.rs.an2[ro] = 0.f;
+      a.rs.cstar[ro] = 0.f; a.rs.jstar[ro] = -1; a.rs.fix[ro] = 0;
+    }
+    return;
+  }
+  const int S = a.splits;
+  const size_t base = (size_t)g * S * kRows;
+  float M = -INFINITY;
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, a.part.m2[base + (size_t)s * kRows + r]);
+  M = wave_max(M);
+  int sstar = INT_MAX;
+  for (int s = lane; s < S; s += 64)
+    if (M > -INFINITY && a.part.m2[base + (size_t)s * kRows + r] == M) sstar = min(sstar, s);
+  sstar = wave_min_i(sstar);
+  float Sf = 0.f, Sxo = 0.f;
+  int bad = 0;
+  for (int s = lane; s < S; s += 64) {
+    const size_t o = base + (size_t)s * kRows + r;
+    const float ms = a.part.m2[o];
+    const float f = (ms > -INFINITY) ? ex2(ms - M) : 0.f;
+    sm_f[wid][s] = f;
+    Sf += a.part.S[o] * f;
+    if (s != sstar) Sxo += a.part.S[o] * f;
+    bad |= a.part.bad[o];
+  }
+  Sf = wave_sum(Sf);
+  Sxo = wave_sum(Sxo);
+  bad = wave_or_i(bad);
+  const bool have = (sstar != INT_MAX);
+  const float Sx = have ? a.part.Sx[base + (size_t)sstar * kRows + r] + Sxo : 0.f;
+  int jst = have ? a.part.jstar[base + (size_t)sstar * kRows + r] : -1;
+  if (jst < 0 || jst >= a.n) { jst = -1; bad = 1; }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+
+  const float invS = 1.f / Sf;
+  float an2 = 0.f, dist = 0.f;
+  int nonfin = 0;
+  const u16* vs = a.v + ((size_t)g * a.n + (jst >= 0 ? jst : 0)) * a.d;
+  for (int dd = lane; dd < DP; dd += 64) {
+    float t = 0.f;
+    for (int s = 0; s < S; ++s) t += a.part.a[(base + (size_t)s * kRows + r) * DP + dd] * sm_f[wid][s];
+    const float av = t * invS;
+    if (!(fabsf(av) <= FLT_MAX)) nonfin = 1;
+    an2 += av * av;
+    const __bf16 hi = (__bf16)av;
+    const __bf16 lo = (__bf16)(av - (float)hi);
+    a.rs.a_hi[ro * DP + dd] = __builtin_bit_cast(u16, hi);
+    a.rs.a_lo[ro * DP + dd] = __builtin_bit_cast(u16, lo);
+    if (dd < a.d && jst >= 0) {
+      const float df = av - bf2f(vs[dd]);
+      dist += df * df;
+    }
+  }
+  an2 = wave_sum(an2);
+  dist = wave_sum(dist);
+  nonfin = wave_or_i(nonfin) | bad | (!(Sf <= FLT_MAX) ? 1 : 0) | (!(M > -INFINITY) ? 1 : 0);
+  const bool singular = !nonfin && !(Sx > 0x1p-53f);
+  if (lane == 0) {
+    a.rs.m2[ro] = M;
+    a.rs.S[ro] = Sf;
+    a.rs.lse2[ro] = M + log2f(Sf);
+    a.rs.an2[ro] = an2;
+    a.rs.jstar[ro] = jst;
+    const bool fix = !nonfin && !singular && Sx < kFixupThreshold;
+    a.rs.fix[ro] = fix ? 1 : 0;
+    a.rs.cstar[ro] = (nonfin || singular) ? 0.f : dist / (Sx * Sx);
+    uint32_t bits = (nonfin ? LATCH_NONFINITE : 0u) | (singular ? LATCH_SINGULAR : 0u);
+    if (bits) atomicOr(a.latch, bits);
+  }
+}
+
+// ----------------------------------------------------------------- fixup --
+// Rows whose arg-max token carries probability p* > ~0.94: recompute
+// abar = sum_{j != j*} e_j v_j / sum_{j != j*} e_j directly and take the arg-max
+// token's contribution as p*^2 ||abar - v_j*||^2 (algebraically identical to the
+// closed form, but free of the cancellation in a - v_j* as p* -> 1).
+// One workgroup per row; 16 token groups x 16 d-slices.  Early exit otherwise.
+template <int DP>
+__global__ __launch_bounds__(kThreads) void fixup_kernel(ScoreArgs a) {
+  constexpr int SL = DP / 16;
+  __shared__ float red[16][DP + 1];
+  __shared__ float rsx[16];
+  __shared__ float part[kWaves];
+  const int g = blockIdx.x / kRows, r = blockIdx.x % kRows;
+  if (r >= a.M) return;
+  const size_t ro = (size_t)g * kRows + r;
+  if (!a.rs.fix[ro]) return;
+  const int tid = threadIdx.x, tg = tid >> 4, ds = tid & 15;
+  const int d = a.d;
+  const int jst = a.rs.jstar[ro];
+  const float m2 = a.rs.m2[ro];
+  const int64_t P = a.n - a.w + (r % a.w);
+  const u16* kg = a.k + (size_t)g * a.n * d;
+  const u16* vg = a.v + (size_t)g * a.n * d;
+  const u16* qrow = a.q + ((size_t)g * a.M + r) * d;
+  float qv[SL], acc[SL];
+#pragma unroll
+  for (int i = 0; i < SL; ++i) {
+    const int dd = ds * SL + i;
+    qv[i] = dd < d ? bf2f(qrow[dd]) : 0.f;
+    acc[i] = 0.f;
+  }
+  float sx = 0.f;
+  for (int64_t j = tg; j <= P; j += 16) {
+    const u16* kr = kg + j * d;
+    const u16* vr = vg + j * d;
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < SL; ++i) {
+      const int dd = ds * SL + i;
+      if (dd < d) dot += qv[i] * bf2f(kr[dd]);
+    }
+    dot += __shfl_xor(dot, 1, 16);
+    dot += __shfl_xor(dot, 2, 16);
+    dot += __shfl_xor(dot, 4, 16);
+    dot += __shfl_xor(dot, 8, 16);
+    const float e = (j == jst) ? 0.f : ex2(dot * a.scale_log2 - m2);
+#pragma unroll
+    for (int i = 0; i < SL; ++i) {
+      const int dd = ds * SL + i;
+      if (dd < d) acc[i] += e * bf2f(vr[dd]);
+    }
+    sx += e;
+  }
+#pragma unroll
+  for (int i = 0; i < SL; ++i) red[tg][ds * SL + i] = acc[i];
+  if (ds == 0) rsx[tg] = sx;
+  __syncthreads();
+  float tot_sx = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) tot_sx += rsx[k];
+  float dist = 0.f;
+  if (tid < d) {
+    float t = 0.f;
+    for (int k = 0; k < 16; ++k) t += red[k][tid];
+    const float abar = t / tot_sx;
+    const float df = abar - bf2f(vg[(size_t)jst * d + tid]);
+    dist = df * df;
+  }
+  dist = wave_sum(dist);
+  if ((tid & 63) == 0) part[tid >> 6] = dist;
+  __syncthreads();
+  if (tid == 0) {
+    const float total = part[0] + part[1] + part[2] + part[3];
+    const float pstar = 1.f / a.rs.S[ro];
+    a.rs.cstar[ro] = pstar * pstar * total;
+  }
+}
+
+// ----------------------------------------------------------------- pass 2 --
+// S = Q K^T and A V^T (rows x tokens): lane l owns token l%32 and 16 rows; the
+// sum over rows stays within the lane pair.  Raw scores of the chunk and its
+// pooling halo go to LDS, then the workgroup pools and protects them.
+constexpr int kMaxRadius = 64;
+
+template <int DP>
+__global__ __launch_bounds__(kThreads) void pass2_kernel(ScoreArgs a) {
+  constexpr int NC = DP / 16;
+  __shared__ float rawbuf[kChunk2 + 2 * kMaxRadius + kTile];
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int r = lane & 31, hh = lane >> 5;
+  const int64_t n = a.n;
+  const int nchunks = (int)((n + kChunk2 - 1) / kChunk2);
+  const int g = blockIdx.x / nchunks, ch = blockIdx.x % nchunks;
+  const int64_t c0 = (int64_t)ch * kChunk2, c1 = min(n, c0 + kChunk2);
+  const int rad = (a.pool - 1) / 2;
+  const int64_t e0 = max((int64_t)0, c0 - rad), e1 = min(n, c1 + rad);
+  const int next = (int)((e1 - e0 + kTile - 1) / kTile);
+  const int d = a.d;
+  const u16* kg = a.k + (size_t)g * n * d;
+  const u16* vg = a.v + (size_t)g * n * d;
+  const size_t ro0 = (size_t)g * kRows;
+
+  bf16x8 qA[NC], hA[NC], lA[NC];
+  const bool qrow_ok = r < a.M;
+  const u16* qrow = a.q + ((size_t)g * a.M + (qrow_ok ? r : 0)) * d;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int col = 16 * c + 8 * hh;
+    qA[c] = (qrow_ok && col < d) ? load8(qrow + col) : zero8();
+    hA[c] = load8(a.rs.a_hi + (ro0 + r) * DP + col);
+    lA[c] = load8(a.rs.a_lo + (ro0 + r) * DP + col);
+  }
+  float lse[16], an2[16];
+  int lim[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int rv = 8 * (v >> 2) + 4 * hh + (v & 3);
+    lse[v] = a.rs.lse2[ro0 + rv];
+    an2[v] = a.rs.an2[ro0 + rv];
+    lim[v] = rv < a.M ? (int)(n - a.w + (rv % a.w)) : -1;
+  }
+  const int jsl = (lane < kRows) ? a.rs.jstar[ro0 + lane] : -1;
+  const float csl = (lane < kRows) ? a.rs.cstar[ro0 + lane] : 0.f;
+  const float invG = 1.f / (float)a.G;
+  uint32_t flags = 0;
+
+  for (int t = wid; t < next; t += kWaves) {
+    const int64_t j0 = e0 + (int64_t)t * kTile;
+    const int64_t tok = j0 + r;
+    const bool tok_ok = tok < e1;
+    bf16x8 kB[NC], vB[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int col = 16 * c + 8 * hh;
+      const bool ok = tok_ok && col < d;
+      kB[c] = ok ? load8(kg + tok * d + col) : zero8();
+      vB[c] = ok ? load8(vg + tok * d + col) : zero8();
+    }
+    f32x16 sacc, av;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; av[v] = 0.f; }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) sacc = mfma32(qA[c], kB[c], sacc);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      av = mfma32(hA[c], vB[c], av);
+      av = mfma32(lA[c], vB[c], av);
+    }
+    float vn = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = (float)vB[c][e];
+        vn += x * x;
+      }
+    vn += __shfl_xor(vn, 32);
+    float cc[16];
+    const int itok = (int)tok;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float p = ex2(sacc[v] * a.scale_log2 - lse[v]);
+      const float odds = p * __builtin_amdgcn_rcpf(1.f - p);
+      const float dist = fmaxf(an2[v] - 2.f * av[v] + vn, 0.f);
+      const float c = odds * odds * dist;
+      cc[v] = (tok_ok && itok <= lim[v]) ? c : 0.f;
+    }
+    // the arg-max token of a row takes the merge/fixup value instead
+    const bool hit = (jsl >= j0) && (jsl < j0 + kTile);
+    uint64_t bal = __ballot(hit);
+    while (bal) {
+      const int rr = __ffsll((unsigned long long)bal) - 1;
+      bal &= bal - 1;
+      const int js = __shfl(jsl, rr);
+      const float cs = __shfl(csl, rr);
+      const int L = (int)(js - j0) + 32 * ((rr >> 2) & 1);
+      const int vr = 4 * (rr >> 3) + (rr & 3);
+      if (lane == L && tok_ok) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (v == vr) cc[v] = cs;
+      }
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sum += cc[v];
+    sum += __shfl_xor(sum, 32);
+    const float raw = sum * invG;
+    if (tok_ok && !(raw <= FLT_MAX)) flags |= (raw != raw) ? LATCH_NONFINITE : LATCH_RANGE;
+    if (hh == 0 && tok_ok) rawbuf[tok - e0] = raw;
+  }
+  __syncthreads();
+  for (int64_t j = c0 + tid; j < c1; j += kThreads) {
+    const int64_t lo = max((int64_t)0, j - rad), hi = min(n - 1, j + rad);
+    float mx = rawbuf[lo - e0];
+    for (int64_t i = lo + 1; i <= hi; ++i) mx = fmaxf(mx, rawbuf[i - e0]);
+    a.scores[(size_t)g * n + j] = (j >= n - a.w) ? INFINITY : mx + 0.f;
+  }
+  if (flags) atomicOr(a.latch, flags);
+}
+
+// ------------------------------------------------------------- host side --
+int plan_splits(int64_t n, int Hkv, int64_t* split_len) {
+  // ~1024 workgroups over the chip (4 per CU), at least 256 tokens each.
+  int64_t want = (1024 + Hkv - 1) / Hkv;
+  const int64_t max_by_len = (n + 255) / 256;
+  if (want > max_by_len) want = max_by_len;
+  if (want > kMaxSplits) want = kMaxSplits;
+  if (want < 1) want = 1;
+  int64_t len = (n + want - 1) / want;
+  len = (len + kTile - 1) / kTile * kTile;
+  *split_len = len;
+  return (int)((n + len - 1) / len);
+}
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t score_scratch_bytes(int Hkv, int splits, int DP) {
+  const size_t prow = (size_t)Hkv * splits * kRows;
+  const size_t rrow = (size_t)Hkv * kRows;
+  return align256(prow * 4) * 5 + align256(prow * DP * 4) + align256(rrow * 4) * 7 +
+         align256(rrow * DP * 2) * 2;
+}
+
+void carve_scratch(void* base, int Hkv, int splits, int DP, Partials* p, RowState* rs) {
+  char* c = static_cast<char*>(base);
+  const size_t prow = (size_t)Hkv * splits * kRows;
+  const size_t rrow = (size_t)Hkv * kRows;
+  auto take = [&](size_t bytes) { char* x = c; c += align256(bytes); return x; };
+  p->m2 = (float*)take(prow * 4);
+  p->S = (float*)take(prow * 4);
+  p->Sx = (float*)take(prow * 4);
+  p->jstar = (int*)take(prow * 4);
+  p->bad = (int*)take(prow * 4);
+  p->a = (float*)take(prow * DP * 4);
+  rs->m2 = (float*)take(rrow * 4);
+  rs->lse2 = (float*)take(rrow * 4);
+  rs->S = (float*)take(rrow * 4);
+  rs->an2 = (float*)take(rrow * 4);
+  rs->cstar = (float*)take(rrow * 4);
+  rs->jstar = (int*)take(rrow * 4);
+  rs->fix = (int*)take(rrow * 4);
+  rs->a_hi = (u16*)take(rrow * DP * 2);
+  rs->a_lo = (u16*)take(rrow * DP * 2);
+}
+
+template <int DP>
+static hipError_t launch_score_dp(void* ctx, const ScoreArgs& a, hipStream_t s) {
+  const size_t lds1 = (size_t)kWaves * kTile * (DP + 8) * 2;
+  const size_t red = (size_t)kRows * DP * 4;
+  const size_t lds = lds1 > red ? lds1 : red;
+  static bool attr_done = false;
+  if (!attr_done && lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)pass1_kernel<DP>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  prof_begin(ctx, "pass1", s);
+  hipLaunchKernelGGL(pass1_kernel<DP>, dim3(a.Hkv * a.splits), dim3(kThreads), lds, s, a);
+  prof_end(ctx, "pass1", s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  prof_begin(ctx, "merge", s);
+  hipLaunchKernelGGL(merge_kernel<DP>, dim3(a.Hkv * (kRows / kWaves)), dim3(kThreads), 0, s, a);
+  prof_end(ctx, "merge", s);
+  prof_begin(ctx, "fixup", s);
+  hipLaunchKernelGGL(fixup_kernel<DP>, dim3(a.Hkv * kRows), dim3(kThreads), 0, s, a);
+  prof_end(ctx, "fixup", s);
+  const int nchunks = (int)((a.n + kChunk2 - 1) / kChunk2);
+  prof_begin(ctx, "pass2", s);
+  hipLaunchKernelGGL(pass2_kernel<DP>, dim3((unsigned)a.Hkv * nchunks), dim3(kThreads), 0, s, a);
+  prof_end(ctx, "pass2", s);
+  return hipGetLastError();
+}
+
+hipError_t launch_score(void* ctx, const ScoreArgs& a, hipStream_t s) {
+  switch (a.DP) {
+    case 32: return launch_score_dp<32>(ctx, a, s);
+    case 64: return launch_score_dp<64>(ctx, a, s);
+    case 96: return launch_score_dp<96>(ctx, a, s);
+    case 128: return launch_score_dp<128>(ctx, a, s);
+    case 160: return launch_score_dp<160>(ctx, a, s);
+    case 192: return launch_score_dp<192>(ctx, a, s);
+    case 224: return launch_score_dp<224>(ctx, a, s);
+    case 256: return launch_score_dp<256>(ctx, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dropkv

@@ -1,0 +1,139 @@
+/*
+ * dropkv.h -- C ABI of libdropkv: DropKV per-token output-perturbation scoring,
+ * eviction selection and cache compaction on AMD Instinct MI355X (gfx950).
+ *
+ * The method (DropKV: Decoupling Residual-Output Perturbation for Near-Optimal
+ * KV-Cache Eviction, arXiv 2610.22130):
+ *   - Section 3.1 / Appendix C.2: deleting token j from the softmax of one query
+ *     changes the attention output a = sum_j p_j v_j by
+ *         Delta_j = p_j / (1 - p_j) * (a - v_j).
+ *   - Section 3.3, and the "Core equation" of the third-party implementation
+ *     notes: over the observation window of w tail queries the score is
+ *         s_j = sum_t || Delta_j^(t) ||^2 .
+ *   - The notes' description of "Algorithm 1": query heads sharing one physical
+ *     KV head are averaged, MaxPool1D smooths the scores, the recent window is
+ *     set to +inf, the smallest scores are evicted, and a probability that
+ *     rounds to 1 is rejected instead of being epsilon-patched.
+ *   - Section 2.2: eviction shrinks the resident cache (compaction).
+ *
+ * Conventions shared by every call:
+ *   - bf16 tensors are passed as uint16_t bit patterns in device memory.
+ *   - q_win  [Hq][w][d]  : the w tail queries of every query head; window query t
+ *                          sits at position n-w+t and sees keys 0..n-w+t.
+ *   - k, v   [Hkv][n][d] : the cache of every KV head, rows contiguous.
+ *     Layers and batch entries fold into the head dimension ([L][B][H] is
+ *     Hkv = L*B*H heads), as long as q_win folds the same way.
+ *   - query head h belongs to KV head g = h / G, G = Hq / Hkv.
+ *   - every pointer is caller-owned device memory, 16-byte aligned; outputs are
+ *     preallocated by the caller; the library never frees or retains them.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call is
+ *     asynchronous on that stream except dropkv_sync.
+ *   - Host-side argument checks happen before any launch and return EINVAL
+ *     synchronously.  Conditions found on the device (ESINGULAR, ENONFINITE,
+ *     ERANGE) are latched in the context and returned by dropkv_sync; while a
+ *     condition is latched, dropkv_select does not produce a keep list.
+ *   - On any error the contents of the outputs are unspecified.
+ *   - A context is bound to one device and must not be used from two host
+ *     threads at once.
+ */
+#ifndef DROPKV_H
+#define DROPKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    DROPKV_OK = 0,
+    DROPKV_EINVAL = 1,     /* bad argument, found on the host before any launch */
+    DROPKV_ESINGULAR = 2,  /* some window query puts probability that rounds to 1 on one key */
+    DROPKV_ENONFINITE = 3, /* a non-finite input element */
+    DROPKV_ERANGE = 4,     /* a score beyond FLT_MAX, or a keep index outside [0, n) */
+    DROPKV_EDEVICE = 5,    /* a HIP runtime error */
+    DROPKV_ENOMEM = 6      /* scratch allocation failed */
+};
+
+typedef struct dropkv_ctx dropkv_ctx;
+
+/* Create a context on `device` (a HIP device ordinal).  The context owns the
+ * scratch used by dropkv_score (split partial states and per-query state,
+ * O(Hq * w * d * splits) bytes, grown on demand) and the device error latch. */
+int dropkv_create(dropkv_ctx **out, int device);
+
+/* Release the context and its scratch.  Synchronises the device first. */
+int dropkv_destroy(dropkv_ctx *ctx);
+
+/*
+ * Score every cached token of every KV head.
+ *   scores [Hkv][n] fp32 (out): for each KV head g and position j,
+ *       raw_g[j]   = (1/G) * sum_{h in group g} sum_{t < w} ||Delta_j^(h,t)||^2
+ *                    (Delta = 0 where query t does not see key j),
+ *       scores[g][j] = max over i in [j - r, j + r] and [0, n) of raw_g[i],
+ *                    r = (pool - 1)/2, then +inf for j >= n - w.
+ *   No attention weights, distances or per-token intermediates are materialised:
+ *   scratch is O(Hq * w * d * splits).
+ * EINVAL if: a pointer is NULL or not 16-byte aligned; Hq % Hkv != 0; w < 1 or
+ *   w > n; n < 1 or n >= 2^31; pool < 1 or pool even; d % 8 != 0 or d > 256;
+ *   G * w > 32.
+ * Latched: ESINGULAR if for some window query the mass off its arg-max key,
+ *   relative to the arg-max, is <= 2^-53 (so p_max rounds to 1 in binary64);
+ *   ENONFINITE if an input element is not finite; ERANGE if a score exceeds
+ *   FLT_MAX.
+ */
+int dropkv_score(dropkv_ctx *ctx, const uint16_t *q_win, const uint16_t *k_cache,
+                 const uint16_t *v_cache, int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int32_t d,
+                 int32_t pool, float *scores, void *stream);
+
+/*
+ * Keep `budget` tokens per KV head: evict the k = n - budget smallest scores by
+ * the total order (score, index) ascending -- among equal scores the older token
+ * goes first -- and write the survivors' indices in ascending order.
+ *   scores [Hkv][n] fp32 (in), keep [Hkv][budget] int32 (out).
+ * Scores are compared as floats with -0 == +0; NaN orders above +inf.
+ * EINVAL if: a pointer is NULL or misaligned; Hkv < 1; n < 1 or n >= 2^31;
+ *   budget < 0 or budget > n.  (dropkv_score's protected window survives any
+ *   budget >= w.)
+ * If the context has a latched device error, nothing is written.
+ */
+int dropkv_select(dropkv_ctx *ctx, const float *scores, int32_t Hkv, int64_t n, int64_t budget,
+                  int32_t *keep, void *stream);
+
+/*
+ * Gather the kept rows into a packed cache (exact bit copies):
+ *   k_out[g][r][:] = k[g][keep[g][r]][:],  v_out likewise;  [Hkv][budget][d] bf16.
+ * Inputs and outputs must not overlap.
+ * EINVAL as for dropkv_score's shape checks, plus budget < 0 or budget > n.
+ * Latched: ERANGE if some keep index lies outside [0, n) (that row is zero-filled).
+ */
+int dropkv_compact(dropkv_ctx *ctx, const uint16_t *k, const uint16_t *v, int32_t Hkv, int64_t n,
+                   int32_t d, const int32_t *keep, int64_t budget, uint16_t *k_out,
+                   uint16_t *v_out, void *stream);
+
+/* Wait for `stream`, then return and clear the latched device condition
+ * (ENONFINITE before ESINGULAR before ERANGE), or DROPKV_OK. */
+int dropkv_sync(dropkv_ctx *ctx, void *stream);
+
+/* Static string naming a status code. */
+const char *dropkv_strerror(int code);
+
+/*
+ * Per-kernel timing for measurement.  While enabled, every kernel the library
+ * launches is bracketed by HIP events on the caller's stream; dropkv_profile_read
+ * returns, for the kernel family `name` ("pass1", "merge", "fixup", "pass2",
+ * "select", "compact"), the summed milliseconds and launch count since the last
+ * reset (it synchronises on the recorded events).  Disabled by default.
+ */
+int dropkv_profile_enable(dropkv_ctx *ctx, int on);
+int dropkv_profile_reset(dropkv_ctx *ctx);
+int dropkv_profile_read(dropkv_ctx *ctx, const char *name, double *total_ms, int64_t *launches);
+
+/* Launch geometry dropkv_score would use for these sizes (for tests/diagnostics):
+ * number of sequence splits of the first pass. */
+int dropkv_plan_splits(int64_t n, int32_t Hkv, int32_t *splits);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DROPKV_H */
