@@ -92,12 +92,13 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     NaN stays NaN (quiet), +-inf stays +-inf.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    out = rounded.astype(np.uint16)
+    u = x.view(np.uint32)
     nan = np.isnan(x)
+    # NaN bit patterns near 0xFFFFFFFF would wrap in uint32; they are fixed below
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    out = rounded.astype(np.uint16)
     if nan.any():
-        out[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+        out[nan] = ((u[nan] >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16)
     return out
 
 

@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Benchmark of the DropKV eviction path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = the whole path over one synthetic single-layer batch:
+dropkv_score (pass 1, merge, arg-max fix-up, pass 2 with pooling/protection)
+-> dropkv_select -> dropkv_compact, with the inputs already resident in HBM.
+The workload is the Llama-3.1-8B-shaped layer at n = 131072 (Hq=32, Hkv=8,
+d=128, w=8, pool 7, 5 % budget), bf16 inputs drawn by the seeded generator.
+
+Prints ONE JSON line on stdout; everything else goes to stderr.
+
+Also:
+  --summarize-pmc FETCH.csv WRITE.csv   turn two rocprofv3 --pmc runs (FETCH_SIZE,
+                                        WRITE_SIZE) into profiles/traffic_<workload>.json
+  --copy-calibration                    run one 1 GiB device-to-device copy after the
+                                        timed steps (the counters' scale reference)
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["attention_perturbation_scoring_amd/csrc/score_kernels.hip",
+                  "attention_perturbation_scoring_amd/csrc/select_compact.hip"]
+COPY_BYTES = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# Algorithmic HBM bytes per (token, KV head) of each kernel; the whole score +
+# select path moves 8d + 8 bytes per (token, KV head): two bf16 reads of K and V,
+# one fp32 score write and one fp32 score read.
+def algorithmic_bytes(kernel: str, Hkv: int, n: int, d: int, budget: int) -> float:
+    th = Hkv * n
+    if kernel == "pass1":
+        return th * 4.0 * d
+    if kernel == "pass2":
+        return th * (4.0 * d + 4.0)
+    if kernel == "select":
+        return th * 4.0
+    if kernel == "compact":
+        return 2.0 * 2.0 * Hkv * budget * d * 2.0
+    return 0.0
+
+
+def traffic_for(workload: str, kernel: str):
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None  # counters were taken on different kernels
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp):
+    """Time the float64 oracle (score + select) on the host, on the full
+    single-layer workload; one thread per KV head (its parallel unit)."""
+    from oracle import oracle as orc
+    threads = min(cfg.Hkv, orc.default_threads())
+    t0 = time.perf_counter()
+    s = orc.score(inp["q"], inp["k"], inp["v"], cfg.pool, nthreads=threads)
+    orc.select(s, cfg.budget)
+    dt = time.perf_counter() - t0
+    return {"value": cfg.n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"full {cfg.name} layer (all {cfg.Hkv} KV heads, n={cfg.n}); "
+                      f"float64 score + select, {dt:.2f} s wall on {threads} threads"}
+
+
+def run(args):
+    import numpy as np
+    import torch
+    from attention_perturbation_scoring_amd import dropkv, workload as wl
+
+    cfg = wl.CONFIGS[args.workload]
+    if cfg.layers != 1:
+        raise SystemExit("bench runs single-layer workloads")
+    torch.cuda.set_device(0)
+    log(f"[bench] generating {cfg.name} inputs (seed {cfg.seed})")
+    inp = wl.make_layer(cfg, cfg.seed)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda")
+
+    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    Hq, Hkv, d, n, w, pool, budget = cfg.Hq, cfg.Hkv, cfg.d, cfg.n, cfg.w, cfg.pool, cfg.budget
+    scores = torch.empty((Hkv, n), dtype=torch.float32, device="cuda")
+    keep = torch.empty((Hkv, budget), dtype=torch.int32, device="cuda")
+    k_out = torch.empty((Hkv, budget, d), dtype=torch.int16, device="cuda")
+    v_out = torch.empty((Hkv, budget, d), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+    ctx = dropkv.Context(0)
+
+    def step():
+        ctx.score(q, k, v, n, w, Hq, Hkv, d, pool, scores, stream)
+        ctx.select(scores, Hkv, n, budget, keep, stream)
+        ctx.compact(k, v, Hkv, n, d, keep, budget, k_out, v_out, stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    ctx.check(stream)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps ----
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    status = ctx.sync(stream)
+    if status != dropkv.OK:
+        raise SystemExit(f"device status {dropkv.strerror(status)}")
+    ms_per_step = wall * 1e3 / args.steps
+
+    # ---- per-kernel HIP-event timing over K more steps on the same stream ----
+    ctx.profile(True)
+    ctx.profile_reset()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    prof_wall = time.perf_counter() - t1
+    kern = {}
+    for name in dropkv.KERNELS:
+        tot, cnt = ctx.profile_read(name)
+        if cnt:
+            kern[name] = {"avg_us": 1e3 * tot / cnt, "launches": cnt}
+    ctx.profile(False)
+    ctx.check(stream)
+
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.int16, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {COPY_BYTES} bytes done")
+
+    score_select_us = sum(kern[x]["avg_us"] for x in ("pass1", "merge", "fixup", "pass2", "select")
+                          if x in kern)
+    dom = max(("pass1", "pass2"), key=lambda x: kern[x]["avg_us"])
+    alg = algorithmic_bytes(dom, Hkv, n, d, budget)
+    achieved = alg / (kern[dom]["avg_us"] * 1e-6) / 1e9
+    path_bytes = Hkv * n * (8.0 * d + 8.0)
+    path_gbs = path_bytes / (score_select_us * 1e-6) / 1e9
+    traffic = traffic_for(cfg.name, dom)
+
+    out = {
+        "metric": "KV tokens scored/s + achieved HBM GB/s (% of peak), n=128K, Hkv=8, d=128, w=8",
+        "value": n / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "Hq": Hq, "Hkv": Hkv, "d": d, "n": n, "w": w,
+                   "pool": pool, "budget": budget, "batch": 1, "layers": 1,
+                   "input_dtype": "bf16", "step": "score+select+compact"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+        "kernel_us": {k_: round(v_["avg_us"], 2) for k_, v_ in kern.items()},
+        "score_select_us": score_select_us,
+        "score_select_algorithmic_GBs": path_gbs,
+        "score_select_frac_of_peak": path_gbs / HBM_PEAK_GBS,
+        "token_heads_per_s": Hkv * n / (ms_per_step * 1e-3),
+        "profiled_ms_per_step": prof_wall * 1e3 / args.steps,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the float64 oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(cfg, inp)
+    ctx.close()
+    return out
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, workload: str):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) from rocprofv3 counter CSVs,
+    scaled by the same counters on the 1 GiB calibration copy."""
+    def load(path, counter):
+        rows = {}
+        files = sorted(glob.glob(path)) if any(c in path for c in "*?[") else [path]
+        for p in files:
+            with open(p) as f:
+                for r in csv.DictReader(f):
+                    if r.get("Counter_Name") != counter:
+                        continue
+                    name = r.get("Kernel_Name", "")
+                    rows.setdefault(name, []).append(float(r["Counter_Value"]))
+        return rows
+
+    fetch = load(fetch_csv, "FETCH_SIZE")
+    write = load(write_csv, "WRITE_SIZE")
+
+    def pick(rows, key):
+        vals = [v for name, vs in rows.items() if key in name for v in vs]
+        return sum(vals) / len(vals) if vals else None
+
+    def largest(rows, key):
+        vals = [v for name, vs in rows.items() if key in name for v in vs]
+        return max(vals) if vals else None
+
+    # the calibration copy is the runtime's device-to-device blit of COPY_BYTES,
+    # the largest copyBuffer dispatch of the run (the others are small uploads)
+    copy_fetch = largest(fetch, "copyBuffer")
+    copy_write = largest(write, "copyBuffer")
+    f_scale = COPY_BYTES / (copy_fetch * 1024.0) if copy_fetch else None
+    w_scale = COPY_BYTES / (copy_write * 1024.0) if copy_write else None
+    kernels = {}
+    for short, key in (("pass1", "pass1_kernel"), ("merge", "merge_kernel"),
+                       ("fixup", "fixup_kernel"), ("pass2", "pass2_kernel"),
+                       ("select", "select_kernel"), ("compact", "compact_kernel")):
+        fk, wk = pick(fetch, key), pick(write, key)
+        if fk is None or wk is None or f_scale is None or w_scale is None:
+            continue
+        kernels[short] = {"fetch_kib": fk, "write_kib": wk,
+                          "bytes_per_launch": fk * 1024.0 * f_scale + wk * 1024.0 * w_scale}
+    out = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+           "copy_bytes": COPY_BYTES, "copy_fetch_kib": copy_fetch, "copy_write_kib": copy_write,
+           "fetch_scale": f_scale, "write_scale": w_scale, "kernels": kernels,
+           "made_by": f"python bench.py --summarize-pmc {fetch_csv} {write_csv}"}
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    log(f"[bench] wrote {path}")
+
+
+def summarize_kt(stats_csv: str, workload: str, command: str):
+    """rocprofv3 --kernel-trace --stats CSV -> profiles/kernel_stats_<workload>.txt."""
+    with open(stats_csv) as f:
+        rows = list(csv.DictReader(f))
+    lines = [f"rocprofv3 kernel statistics, workload {workload}",
+             f"kernel sources sha256[:16] {kernel_source_hash()}",
+             f"command: {command}", "",
+             f"{'kernel':<34}{'calls':>7}{'avg_us':>11}{'min_us':>11}{'max_us':>11}{'share%':>9}"]
+    for r in rows:
+        name = r["Name"]
+        short = name.split("(")[0].replace("void ", "").replace("dropkv::", "")
+        lines.append(f"{short[:33]:<34}{int(r['Calls']):>7}{float(r['AverageNs']) / 1e3:>11.2f}"
+                     f"{float(r['MinNs']) / 1e3:>11.2f}{float(r['MaxNs']) / 1e3:>11.2f}"
+                     f"{float(r['Percentage']):>9.2f}")
+    path = os.path.join(ROOT, "profiles", f"kernel_stats_{workload}.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log(f"[bench] wrote {path}")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-kt", nargs=2, metavar=("STATS_CSV", "COMMAND"))
+    args = ap.parse_args()
+    if args.summarize_kt:
+        summarize_kt(args.summarize_kt[0], args.workload, args.summarize_kt[1])
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the DropKV path here runs on a single device "
+              "(no inter-GPU collectives); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    out = run(args)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
