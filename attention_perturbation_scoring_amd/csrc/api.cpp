@@ -24,6 +24,9 @@ struct dropkv_ctx {
   int device = 0;
   void* scratch = nullptr;
   size_t scratch_bytes = 0;
+  void* sel_scratch = nullptr;     // selection scratch (see carve_select)
+  size_t sel_bytes = 0;
+  int sel_hkv = 0;                 // head count the zeroed prefix was laid out for
   uint32_t* latch = nullptr;       // device word
   uint32_t* latch_host = nullptr;  // pinned read-back
   bool prof = false;
@@ -117,6 +120,7 @@ int dropkv_destroy(dropkv_ctx* c) {
   for (auto& r : c->recs) { (void)hipEventDestroy(r.start); (void)hipEventDestroy(r.stop); }
   for (auto e : c->free_events) (void)hipEventDestroy(e);
   if (c->scratch) (void)hipFree(c->scratch);
+  if (c->sel_scratch) (void)hipFree(c->sel_scratch);
   if (c->latch) (void)hipFree(c->latch);
   if (c->latch_host) (void)hipHostFree(c->latch_host);
   delete c;
@@ -179,8 +183,32 @@ int dropkv_select(dropkv_ctx* c, const float* scores, int32_t Hkv, int64_t n, in
   if (!aligned16(keep)) return DROPKV_EINVAL;
   DeviceGuard guard(c->device);
   if (!guard.ok) return DROPKV_EDEVICE;
-  return to_status(
-      launch_select(c, scores, Hkv, n, budget, keep, c->latch, static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t need = select_scratch_bytes(Hkv, n);
+  if (need > c->sel_bytes || Hkv != c->sel_hkv) {
+    // (re)allocate; the histogram and candidate counters start zeroed and every
+    // selection leaves them zeroed again
+    if (c->sel_scratch) {
+      (void)hipStreamSynchronize(s);
+      (void)hipDeviceSynchronize();
+      if (need > c->sel_bytes) {
+        (void)hipFree(c->sel_scratch);
+        c->sel_scratch = nullptr;
+        c->sel_bytes = 0;
+      }
+    }
+    if (!c->sel_scratch) {
+      hipError_t e = hipMalloc(&c->sel_scratch, need);
+      if (e != hipSuccess) { c->sel_scratch = nullptr; return DROPKV_ENOMEM; }
+      c->sel_bytes = need;
+    }
+    hipError_t e = hipMemset(c->sel_scratch, 0, select_zero_prefix_bytes(Hkv));
+    if (e != hipSuccess) return to_status(e);
+    c->sel_hkv = Hkv;
+  }
+  SelScratch sc{};
+  carve_select(c->sel_scratch, Hkv, n, &sc);
+  return to_status(launch_select(c, scores, Hkv, n, budget, keep, c->latch, sc, s));
 }
 
 int dropkv_compact(dropkv_ctx* c, const uint16_t* k, const uint16_t* v, int32_t Hkv, int64_t n,

@@ -21,7 +21,8 @@ constexpr int kRows = 32;        // window-query rows per KV head handled by one
 constexpr int kTile = 32;        // tokens per MFMA tile
 constexpr int kWaves = 4;        // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kChunk2 = 512;     // tokens per pass-2 workgroup (before the pooling halo)
+constexpr int kChunk2 = 2048;    // tokens per pass-2 workgroup (before the pooling halo)
+constexpr int kTargetWG1 = 512;  // pass-1 workgroups aimed for over all heads (2 per CU)
 
 // S_excl below this (argmax probability above ~0.94) routes the arg-max term
 // through the exact exclusion kernel instead of the fp32 output a.
@@ -64,6 +65,26 @@ struct ScoreArgs {
   uint32_t* latch;
 };
 
+// Scratch of the selection kernels (owned by the context; hist1 and cand_cnt
+// must be zero between calls -- the last selection kernel leaves them zeroed).
+struct SelScratch {
+  uint32_t* hist1;         // [Hkv][4096]
+  uint32_t* cand_cnt;      // [Hkv]
+  uint32_t* cand_key;      // [Hkv][8192]
+  int32_t* cand_idx;       // [Hkv][8192]
+  uint32_t* b1;            // [Hkv]
+  uint32_t* krem1;         // [Hkv]
+  uint32_t* T;             // [Hkv]
+  uint32_t* blk_above;     // [Hkv][nblk]
+  uint32_t* blk_above_in;  // [Hkv][nblk]
+  uint32_t* blk_ties;      // [Hkv][nblk]
+  uint32_t* blk_off;       // [Hkv][nblk]
+  uint32_t* blk_evt;       // [Hkv][nblk]
+};
+size_t select_scratch_bytes(int Hkv, int64_t n);
+void carve_select(void* base, int Hkv, int64_t n, SelScratch* sc);
+size_t select_zero_prefix_bytes(int Hkv);
+
 // Profiling hooks implemented by the host library (no-ops unless enabled).
 struct ProfScope;
 void prof_begin(void* ctx, const char* name, hipStream_t s);
@@ -71,7 +92,7 @@ void prof_end(void* ctx, const char* name, hipStream_t s);
 
 hipError_t launch_score(void* ctx, const ScoreArgs& a, hipStream_t s);
 hipError_t launch_select(void* ctx, const float* scores, int Hkv, int64_t n, int64_t budget,
-                         int32_t* keep, uint32_t* latch, hipStream_t s);
+                         int32_t* keep, uint32_t* latch, const SelScratch& sc, hipStream_t s);
 hipError_t launch_compact(void* ctx, const u16* k, const u16* v, int Hkv, int64_t n, int d,
                           const int32_t* keep, int64_t budget, u16* k_out, u16* v_out,
                           uint32_t* latch, hipStream_t s);

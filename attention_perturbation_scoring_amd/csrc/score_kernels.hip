@@ -14,10 +14,10 @@
 //   merge  : per row, combine the split partials: final max, S, S_excl, arg-max
 //            j*, a = a_un / S, ||a||^2, a as bf16 hi + lo, the arg-max token's
 //            own term from a, and the singular / non-finite decisions.
-//   fixup  : (only rows whose arg-max holds probability above ~0.94) recompute
-//            the output over the other tokens exactly and take the arg-max term
-//            as p*^2 ||abar - v_j*||^2, which stays accurate as p* -> 1.
-//   pass2  : per (KV head, 512-token chunk + pooling halo) stream K and V again:
+//            Rows whose arg-max holds probability above ~0.94 recompute the
+//            output over the other tokens exactly and take the arg-max term as
+//            p*^2 ||abar - v_j*||^2, which stays accurate as p* -> 1.
+//   pass2  : per (KV head, 2048-token chunk + pooling halo) stream K and V again:
 //            logits Q K^T and A V^T (a as hi + lo) on MFMA, then per element
 //            p = 2^(l - lse), odds = p/(1-p), ||a - v||^2 = ||a||^2 - 2 a.v + ||v||^2,
 //            contribution odds^2 ||a - v||^2, summed over the M rows, divided by
@@ -79,7 +79,33 @@ __device__ __forceinline__ int wave_or_i(int x) {
 // taken straight from S^T's registers by ordering the MFMA's reduction slots as
 // token(kc, h, e) = 16*kc + 8*(e/4) + 4*h + e%4, and V^T's operand is gathered
 // from a per-wave LDS copy of the V tile in that same order.
-template <int DP>
+// One 32-token K/V tile in MFMA operand layout: lane l holds 8 consecutive d
+// values (16 bytes) of token l%32.  Interior tiles load unconditionally; only a
+// ragged tile (tokens past the range end) or a head dimension below the padded
+// width masks lanes to zero.
+template <int NC, bool FULLD>
+__device__ __forceinline__ void load_kv_tile(const u16* kg, const u16* vg, int64_t tok, bool tok_ok,
+                                             bool ragged, int hh, int d, bf16x8 (&kk)[NC],
+                                             bf16x8 (&vv)[NC]) {
+  if (FULLD && !ragged) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int col = 16 * c + 8 * hh;
+      kk[c] = load8(kg + tok * d + col);
+      vv[c] = load8(vg + tok * d + col);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int col = 16 * c + 8 * hh;
+      const bool ok = tok_ok && (FULLD || col < d);
+      kk[c] = ok ? load8(kg + tok * d + col) : zero8();
+      vv[c] = ok ? load8(vg + tok * d + col) : zero8();
+    }
+  }
+}
+
+template <int DP, bool FULLD>
 __global__ __launch_bounds__(kThreads) void pass1_kernel(ScoreArgs a) {
   constexpr int NC = DP / 16;
   constexpr int DB = DP / 32;
@@ -100,6 +126,7 @@ __global__ __launch_bounds__(kThreads) void pass1_kernel(ScoreArgs a) {
   const u16* vg = a.v + (size_t)g * a.n * d;
   const bool row_ok = r < a.M;
   const int64_t causal = row_ok ? a.n - a.w + (r % a.w) : -1;
+  const int64_t all_see = a.n - a.w;   // every window query sees keys 0..n-w
 
   bf16x8 qB[NC];
   const u16* qrow = a.q + ((size_t)g * a.M + (row_ok ? r : 0)) * d;
@@ -109,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void pass1_kernel(ScoreArgs a) {
     qB[c] = (row_ok && col < d) ? load8(qrow + col) : zero8();
   }
 
-  float m = -INFINITY, S = 0.f, Sx = 0.f;
+  float m = -INFINITY, S = 0.f, Sx = 0.f, chk = 0.f;
   int jst = INT_MAX, bad = 0;
   bool has = false;
   f32x16 acc[DB];
@@ -119,17 +146,20 @@ __global__ __launch_bounds__(kThreads) void pass1_kernel(ScoreArgs a) {
     for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
 
   u16* my = lds + wid * kTile * LS;
+  // the next tile of this wave is in flight while the current one is processed
+  bf16x8 kN[NC], vN[NC];
+  if (wid < ntiles) {
+    const int64_t t0 = jbeg + (int64_t)wid * kTile;
+    load_kv_tile<NC, FULLD>(kg, vg, t0 + r, t0 + r < jend, t0 + kTile > jend, hh, d, kN, vN);
+  }
   for (int t = wid; t < ntiles; t += kWaves) {
     const int64_t j0 = jbeg + (int64_t)t * kTile;
-    const int64_t tok = j0 + r;
-    const bool tok_ok = tok < jend;
     bf16x8 kA[NC], vv[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int col = 16 * c + 8 * hh;
-      const bool ok = tok_ok && col < d;
-      kA[c] = ok ? load8(kg + tok * d + col) : zero8();
-      vv[c] = ok ? load8(vg + tok * d + col) : zero8();
+    for (int c = 0; c < NC; ++c) { kA[c] = kN[c]; vv[c] = vN[c]; }
+    if (t + kWaves < ntiles) {
+      const int64_t t0 = j0 + (int64_t)kWaves * kTile;
+      load_kv_tile<NC, FULLD>(kg, vg, t0 + r, t0 + r < jend, t0 + kTile > jend, hh, d, kN, vN);
     }
     f32x16 st;
 #pragma unroll
@@ -140,54 +170,80 @@ __global__ __launch_bounds__(kThreads) void pass1_kernel(ScoreArgs a) {
     for (int c = 0; c < NC; ++c)
       *reinterpret_cast<u32x4*>(my + r * LS + 16 * c + 8 * hh) = __builtin_bit_cast(u32x4, vv[c]);
 
-    // online softmax for row r over this lane's 16 tokens + the partner lane's 16
+    // logits in log2 units; masks only on tiles that reach past the split end
+    // or into the window (rows >= M have zero queries and are never read)
+    const bool interior = (j0 + kTile <= jend) && (j0 + kTile - 1 <= all_see);
     float s2[16];
     float lm = -INFINITY;
+    if (interior) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t tv = j0 + 8 * (v >> 2) + 4 * hh + (v & 3);
-      const bool valid = row_ok && tv < jend && tv <= causal;
-      const float x = st[v];
-      if (valid && !(fabsf(x) <= FLT_MAX)) bad = 1;
-      s2[v] = valid ? x * a.scale_log2 : -INFINITY;
-      lm = fmaxf(lm, s2[v]);
+      for (int v = 0; v < 16; ++v) {
+        chk = fmaf(st[v], 0.f, chk);          // becomes NaN on any inf / NaN logit
+        s2[v] = st[v] * a.scale_log2;
+        lm = fmaxf(lm, s2[v]);
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t tv = j0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+        const bool valid = row_ok && tv < jend && tv <= causal;
+        if (valid) chk = fmaf(st[v], 0.f, chk);
+        s2[v] = valid ? st[v] * a.scale_log2 : -INFINITY;
+        lm = fmaxf(lm, s2[v]);
+      }
     }
     lm = fmaxf(lm, __shfl_xor(lm, 32));
-    int lj = INT_MAX;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int tv = (int)(j0 + 8 * (v >> 2) + 4 * hh + (v & 3));
-      if (s2[v] == lm && lm > -INFINITY) lj = min(lj, tv);
-    }
-    lj = min(lj, __shfl_xor(lj, 32));
     const bool newmax = lm > m;
-    const float mn = newmax ? lm : m;
-    const bool live = mn > -INFINITY;
-    const float alpha = live ? ex2(m - mn) : 1.f;
     float p[16];
-    float ts = 0.f, tx = 0.f;
+    if (__any(newmax)) {
+      // some row's running maximum moves: find the tile arg-max (lowest index)
+      // and rescale; the old arg-max's unit mass joins S_excl
+      int lj = INT_MAX;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int tv = (int)(j0 + 8 * (v >> 2) + 4 * hh + (v & 3));
-      p[v] = live ? ex2(s2[v] - mn) : 0.f;
-      ts += p[v];
-      tx += (tv == lj) ? 0.f : p[v];
-    }
-    ts += __shfl_xor(ts, 32);
-    tx += __shfl_xor(tx, 32);
-    if (newmax) {
-      Sx = (Sx + (has ? 1.f : 0.f)) * alpha + tx;
-      jst = lj;
-      has = true;
+      for (int v = 0; v < 16; ++v) {
+        const int tv = (int)(j0 + 8 * (v >> 2) + 4 * hh + (v & 3));
+        if (s2[v] == lm && lm > -INFINITY) lj = min(lj, tv);
+      }
+      lj = min(lj, __shfl_xor(lj, 32));
+      const float mn = newmax ? lm : m;
+      const bool live = mn > -INFINITY;
+      const float alpha = live ? ex2(m - mn) : 1.f;
+      float ts = 0.f, tx = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int tv = (int)(j0 + 8 * (v >> 2) + 4 * hh + (v & 3));
+        p[v] = live ? ex2(s2[v] - mn) : 0.f;
+        ts += p[v];
+        tx += (tv == lj) ? 0.f : p[v];
+      }
+      ts += __shfl_xor(ts, 32);
+      tx += __shfl_xor(tx, 32);
+      if (newmax) {
+        Sx = (Sx + (has ? 1.f : 0.f)) * alpha + tx;
+        jst = lj;
+        has = true;
+      } else {
+        Sx = Sx + ts;
+      }
+      S = S * alpha + ts;
+      m = mn;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[b][v] *= alpha;
     } else {
-      Sx = Sx + ts;
+      // no maximum moved: every token of the tile joins S and S_excl
+      const float mref = (m > -INFINITY) ? m : 0.f;
+      float ts = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        p[v] = ex2(s2[v] - mref);
+        ts += p[v];
+      }
+      ts += __shfl_xor(ts, 32);
+      S += ts;
+      Sx += ts;
     }
-    S = S * alpha + ts;
-    m = mn;
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[b][v] *= alpha;
 
     bf16x8 ph[2], pl[2];
 #pragma unroll
@@ -215,6 +271,7 @@ __global__ __launch_bounds__(kThreads) void pass1_kernel(ScoreArgs a) {
       }
     wave_sync_lds();
   }
+  if (!(chk == 0.f)) bad = 1;
 
   // ---- combine the four waves' states for each row (fixed order) ----
   bad |= __shfl_xor(bad, 32);
@@ -274,114 +331,48 @@ __global__ __launch_bounds__(kThreads) void pass1_kernel(ScoreArgs a) {
 }
 
 // ----------------------------------------------------------------- merge --
-// One wave per (KV head, row); 4 rows per workgroup, 8 workgroups per head.
+// One workgroup per (KV head, row).  Split statistics are combined with a
+// fixed-order reduction (bitwise reproducible); a is summed by column with the
+// splits partitioned over NG thread groups.  Rows whose arg-max holds
+// probability above ~0.94 then get their arg-max term from the exact
+// exclusion sum, computed by the same workgroup.
 constexpr int kMaxSplits = 1024;
 
-template <int DP>
-__global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
-  __shared__ float sm_f[kWaves][kMaxSplits];
-  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = blockIdx.x / (kRows / kWaves);
-  const int r = (blockIdx.x % (kRows / kWaves)) * kWaves + wid;
-  const size_t ro = (size_t)g * kRows + r;
-  if (r >= a.M) {  // padded rows: zero operands so pass 2's MFMA rows stay inert
-    for (int dd = lane; dd < DP; dd += 64) {
-      a.rs.a_hi[ro * DP + dd] = 0;
-      a.rs.a_lo[ro * DP + dd] = 0;
-    }
-    if (lane == 0) {
-      a.rs.m2[ro] = 0.f; a.rs.lse2[ro] = 0.f; a.rs.S[ro] = 1.f; a.rs.an2[ro] = 0.f;
-      a.rs.cstar[ro] = 0.f; a.rs.jstar[ro] = -1; a.rs.fix[ro] = 0;
-    }
-    return;
-  }
-  const int S = a.splits;
-  const size_t base = (size_t)g * S * kRows;
-  float M = -INFINITY;
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, a.part.m2[base + (size_t)s * kRows + r]);
-  M = wave_max(M);
-  int sstar = INT_MAX;
-  for (int s = lane; s < S; s += 64)
-    if (M > -INFINITY && a.part.m2[base + (size_t)s * kRows + r] == M) sstar = min(sstar, s);
-  sstar = wave_min_i(sstar);
-  float Sf = 0.f, Sxo = 0.f;
-  int bad = 0;
-  for (int s = lane; s < S; s += 64) {
-    const size_t o = base + (size_t)s * kRows + r;
-    const float ms = a.part.m2[o];
-    const float f = (ms > -INFINITY) ? ex2(ms - M) : 0.f;
-    sm_f[wid][s] = f;
-    Sf += a.part.S[o] * f;
-    if (s != sstar) Sxo += a.part.S[o] * f;
-    bad |= a.part.bad[o];
-  }
-  Sf = wave_sum(Sf);
-  Sxo = wave_sum(Sxo);
-  bad = wave_or_i(bad);
-  const bool have = (sstar != INT_MAX);
-  const float Sx = have ? a.part.Sx[base + (size_t)sstar * kRows + r] + Sxo : 0.f;
-  int jst = have ? a.part.jstar[base + (size_t)sstar * kRows + r] : -1;
-  if (jst < 0 || jst >= a.n) { jst = -1; bad = 1; }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-
-  const float invS = 1.f / Sf;
-  float an2 = 0.f, dist = 0.f;
-  int nonfin = 0;
-  const u16* vs = a.v + ((size_t)g * a.n + (jst >= 0 ? jst : 0)) * a.d;
-  for (int dd = lane; dd < DP; dd += 64) {
-    float t = 0.f;
-    for (int s = 0; s < S; ++s) t += a.part.a[(base + (size_t)s * kRows + r) * DP + dd] * sm_f[wid][s];
-    const float av = t * invS;
-    if (!(fabsf(av) <= FLT_MAX)) nonfin = 1;
-    an2 += av * av;
-    const __bf16 hi = (__bf16)av;
-    const __bf16 lo = (__bf16)(av - (float)hi);
-    a.rs.a_hi[ro * DP + dd] = __builtin_bit_cast(u16, hi);
-    a.rs.a_lo[ro * DP + dd] = __builtin_bit_cast(u16, lo);
-    if (dd < a.d && jst >= 0) {
-      const float df = av - bf2f(vs[dd]);
-      dist += df * df;
-    }
-  }
-  an2 = wave_sum(an2);
-  dist = wave_sum(dist);
-  nonfin = wave_or_i(nonfin) | bad | (!(Sf <= FLT_MAX) ? 1 : 0) | (!(M > -INFINITY) ? 1 : 0);
-  const bool singular = !nonfin && !(Sx > 0x1p-53f);
-  if (lane == 0) {
-    a.rs.m2[ro] = M;
-    a.rs.S[ro] = Sf;
-    a.rs.lse2[ro] = M + log2f(Sf);
-    a.rs.an2[ro] = an2;
-    a.rs.jstar[ro] = jst;
-    const bool fix = !nonfin && !singular && Sx < kFixupThreshold;
-    a.rs.fix[ro] = fix ? 1 : 0;
-    a.rs.cstar[ro] = (nonfin || singular) ? 0.f : dist / (Sx * Sx);
-    uint32_t bits = (nonfin ? LATCH_NONFINITE : 0u) | (singular ? LATCH_SINGULAR : 0u);
-    if (bits) atomicOr(a.latch, bits);
-  }
+__device__ __forceinline__ float block_sum256(float x, float* red) {
+  x = wave_sum(x);
+  const int wid = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wid] = x;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+__device__ __forceinline__ float block_max256(float x, float* red) {
+  x = wave_max(x);
+  const int wid = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wid] = x;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+__device__ __forceinline__ int block_min256(int x, int* red) {
+  x = wave_min_i(x);
+  const int wid = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wid] = x;
+  __syncthreads();
+  return min(min(red[0], red[1]), min(red[2], red[3]));
 }
 
-// ----------------------------------------------------------------- fixup --
-// Rows whose arg-max token carries probability p* > ~0.94: recompute
-// abar = sum_{j != j*} e_j v_j / sum_{j != j*} e_j directly and take the arg-max
-// token's contribution as p*^2 ||abar - v_j*||^2 (algebraically identical to the
-// closed form, but free of the cancellation in a - v_j* as p* -> 1).
-// One workgroup per row; 16 token groups x 16 d-slices.  Early exit otherwise.
+// abar = sum_{j != j*} e_j v_j / sum_{j != j*} e_j over the keys row r sees,
+// then the arg-max token's contribution p*^2 ||abar - v_j*||^2 (algebraically
+// equal to the closed form, without the cancellation in a - v_j* as p* -> 1).
+// 16 token groups x 16 d-slices per workgroup.
 template <int DP>
-__global__ __launch_bounds__(kThreads) void fixup_kernel(ScoreArgs a) {
+__device__ float exclusion_term(const ScoreArgs& a, int g, int r, int jst, float m2, float S,
+                                float* red /* [16][DP+1] */, float* rsx /* [16] */, float* tmp) {
   constexpr int SL = DP / 16;
-  __shared__ float red[16][DP + 1];
-  __shared__ float rsx[16];
-  __shared__ float part[kWaves];
-  const int g = blockIdx.x / kRows, r = blockIdx.x % kRows;
-  if (r >= a.M) return;
-  const size_t ro = (size_t)g * kRows + r;
-  if (!a.rs.fix[ro]) return;
   const int tid = threadIdx.x, tg = tid >> 4, ds = tid & 15;
   const int d = a.d;
-  const int jst = a.rs.jstar[ro];
-  const float m2 = a.rs.m2[ro];
   const int64_t P = a.n - a.w + (r % a.w);
   const u16* kg = a.k + (size_t)g * a.n * d;
   const u16* vg = a.v + (size_t)g * a.n * d;
@@ -415,8 +406,9 @@ __global__ __launch_bounds__(kThreads) void fixup_kernel(ScoreArgs a) {
     }
     sx += e;
   }
+  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < SL; ++i) red[tg][ds * SL + i] = acc[i];
+  for (int i = 0; i < SL; ++i) red[tg * (DP + 1) + ds * SL + i] = acc[i];
   if (ds == 0) rsx[tg] = sx;
   __syncthreads();
   float tot_sx = 0.f;
@@ -425,18 +417,113 @@ __global__ __launch_bounds__(kThreads) void fixup_kernel(ScoreArgs a) {
   float dist = 0.f;
   if (tid < d) {
     float t = 0.f;
-    for (int k = 0; k < 16; ++k) t += red[k][tid];
-    const float abar = t / tot_sx;
-    const float df = abar - bf2f(vg[(size_t)jst * d + tid]);
+    for (int k = 0; k < 16; ++k) t += red[k * (DP + 1) + tid];
+    const float df = t / tot_sx - bf2f(vg[(size_t)jst * d + tid]);
     dist = df * df;
   }
-  dist = wave_sum(dist);
-  if ((tid & 63) == 0) part[tid >> 6] = dist;
+  dist = block_sum256(dist, tmp);
+  const float pstar = 1.f / S;
+  return pstar * pstar * dist;
+}
+
+template <int DP>
+__global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
+  constexpr int NG = kThreads / DP;   // thread groups over the splits when summing a
+  __shared__ float sm_f[kMaxSplits];
+  __shared__ float red[16 * (DP + 1)];
+  __shared__ float rsx[16];
+  __shared__ float tmp[kWaves];
+  __shared__ int tmpi[kWaves];
+  const int tid = threadIdx.x;
+  const int g = blockIdx.x / kRows, r = blockIdx.x % kRows;
+  const size_t ro = (size_t)g * kRows + r;
+  if (r >= a.M) {  // padded rows: zero operands so pass 2's MFMA rows stay inert
+    for (int dd = tid; dd < DP; dd += kThreads) {
+      a.rs.a_hi[ro * DP + dd] = 0;
+      a.rs.a_lo[ro * DP + dd] = 0;
+    }
+    if (tid == 0) {
+      a.rs.m2[ro] = 0.f; a.rs.lse2[ro] = INFINITY; a.rs.S[ro] = 1.f; a.rs.an2[ro] = 0.f;
+      a.rs.cstar[ro] = 0.f; a.rs.jstar[ro] = -1; a.rs.fix[ro] = 0;
+    }
+    return;
+  }
+  const int S = a.splits;
+  const size_t base = (size_t)g * S * kRows;
+  float M = -INFINITY;
+  for (int s = tid; s < S; s += kThreads) M = fmaxf(M, a.part.m2[base + (size_t)s * kRows + r]);
+  M = block_max256(M, tmp);
+  int sstar = INT_MAX;
+  for (int s = tid; s < S; s += kThreads)
+    if (M > -INFINITY && a.part.m2[base + (size_t)s * kRows + r] == M) sstar = min(sstar, s);
+  sstar = block_min256(sstar, tmpi);
+  float Sf = 0.f, Sxo = 0.f;
+  int bad = 0;
+  for (int s = tid; s < S; s += kThreads) {
+    const size_t o = base + (size_t)s * kRows + r;
+    const float ms = a.part.m2[o];
+    const float f = (ms > -INFINITY) ? ex2(ms - M) : 0.f;
+    sm_f[s] = f;
+    Sf += a.part.S[o] * f;
+    if (s != sstar) Sxo += a.part.S[o] * f;
+    bad |= a.part.bad[o];
+  }
+  Sf = block_sum256(Sf, tmp);
+  Sxo = block_sum256(Sxo, tmp);
+  bad = (int)block_max256(bad ? 1.f : 0.f, tmp);
+  const bool have = (sstar != INT_MAX);
+  const float Sx = have ? a.part.Sx[base + (size_t)sstar * kRows + r] + Sxo : 0.f;
+  int jst = have ? a.part.jstar[base + (size_t)sstar * kRows + r] : -1;
+  if (jst < 0 || jst >= a.n) { jst = -1; bad = 1; }
+
+  // a = sum_s f_s a_s / S : column dd, splits s = grp, grp + NG, ...
+  const int dd = tid % DP, grp = tid / DP;
+  float t = 0.f;
+  if (grp < NG) {
+    const float* pa = a.part.a + (base + r) * DP + dd;
+#pragma unroll 16
+    for (int s = grp; s < S; s += NG) t += pa[(size_t)s * kRows * DP] * sm_f[s];
+  }
   __syncthreads();
+  if (grp < NG) red[grp * (DP + 1) + dd] = t;
+  __syncthreads();
+  const float invS = 1.f / Sf;
+  float an2 = 0.f, dist = 0.f;
+  int nonfin = 0;
+  if (tid < DP) {
+    float tt = 0.f;
+#pragma unroll
+    for (int k = 0; k < NG; ++k) tt += red[k * (DP + 1) + tid];
+    const float av = tt * invS;
+    if (!(fabsf(av) <= FLT_MAX)) nonfin = 1;
+    an2 = av * av;
+    const __bf16 hi = (__bf16)av;
+    const __bf16 lo = (__bf16)(av - (float)hi);
+    a.rs.a_hi[ro * DP + tid] = __builtin_bit_cast(u16, hi);
+    a.rs.a_lo[ro * DP + tid] = __builtin_bit_cast(u16, lo);
+    if (tid < a.d && jst >= 0) {
+      const float df = av - bf2f(a.v[((size_t)g * a.n + jst) * a.d + tid]);
+      dist = df * df;
+    }
+  }
+  an2 = block_sum256(an2, tmp);
+  dist = block_sum256(dist, tmp);
+  nonfin = (int)block_max256(nonfin ? 1.f : 0.f, tmp);
+  nonfin |= bad | (!(Sf <= FLT_MAX) ? 1 : 0) | (!(M > -INFINITY) ? 1 : 0);
+  const bool singular = !nonfin && !(Sx > 0x1p-53f);
+  const bool fix = !nonfin && !singular && Sx < kFixupThreshold;
+  float cstar = (nonfin || singular) ? 0.f : dist / (Sx * Sx);
+  if (fix) cstar = exclusion_term<DP>(a, g, r, jst, M, Sf, red, rsx, tmp);
   if (tid == 0) {
-    const float total = part[0] + part[1] + part[2] + part[3];
-    const float pstar = 1.f / a.rs.S[ro];
-    a.rs.cstar[ro] = pstar * pstar * total;
+    a.rs.m2[ro] = M;
+    a.rs.S[ro] = Sf;
+    a.rs.lse2[ro] = M + log2f(Sf);
+    a.rs.an2[ro] = an2;
+    a.rs.jstar[ro] = jst;
+    a.rs.fix[ro] = fix ? 1 : 0;
+    a.rs.cstar[ro] = cstar;
+    const uint32_t bits = (nonfin ? LATCH_NONFINITE : 0u) | (singular ? LATCH_SINGULAR : 0u);
+    if (bits) atomicOr(a.latch, bits);
   }
 }
 
@@ -446,7 +533,9 @@ __global__ __launch_bounds__(kThreads) void fixup_kernel(ScoreArgs a) {
 // pooling halo go to LDS, then the workgroup pools and protects them.
 constexpr int kMaxRadius = 64;
 
-template <int DP>
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <int DP, bool FULLD>
 __global__ __launch_bounds__(kThreads) void pass2_kernel(ScoreArgs a) {
   constexpr int NC = DP / 16;
   __shared__ float rawbuf[kChunk2 + 2 * kMaxRadius + kTile];
@@ -463,6 +552,7 @@ __global__ __launch_bounds__(kThreads) void pass2_kernel(ScoreArgs a) {
   const u16* kg = a.k + (size_t)g * n * d;
   const u16* vg = a.v + (size_t)g * n * d;
   const size_t ro0 = (size_t)g * kRows;
+  const int64_t all_see = n - a.w;
 
   bf16x8 qA[NC], hA[NC], lA[NC];
   const bool qrow_ok = r < a.M;
@@ -474,6 +564,8 @@ __global__ __launch_bounds__(kThreads) void pass2_kernel(ScoreArgs a) {
     hA[c] = load8(a.rs.a_hi + (ro0 + r) * DP + col);
     lA[c] = load8(a.rs.a_lo + (ro0 + r) * DP + col);
   }
+  // per-lane row constants; rows >= M carry lse = +inf, so their p and
+  // contribution are exactly 0
   float lse[16], an2[16];
   int lim[16];
 #pragma unroll
@@ -488,17 +580,21 @@ __global__ __launch_bounds__(kThreads) void pass2_kernel(ScoreArgs a) {
   const float invG = 1.f / (float)a.G;
   uint32_t flags = 0;
 
+  bf16x8 kN[NC], vN[NC];
+  if (wid < next) {
+    const int64_t t0 = e0 + (int64_t)wid * kTile;
+    load_kv_tile<NC, FULLD>(kg, vg, t0 + r, t0 + r < e1, t0 + kTile > e1, hh, d, kN, vN);
+  }
   for (int t = wid; t < next; t += kWaves) {
     const int64_t j0 = e0 + (int64_t)t * kTile;
     const int64_t tok = j0 + r;
     const bool tok_ok = tok < e1;
     bf16x8 kB[NC], vB[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int col = 16 * c + 8 * hh;
-      const bool ok = tok_ok && col < d;
-      kB[c] = ok ? load8(kg + tok * d + col) : zero8();
-      vB[c] = ok ? load8(vg + tok * d + col) : zero8();
+    for (int c = 0; c < NC; ++c) { kB[c] = kN[c]; vB[c] = vN[c]; }
+    if (t + kWaves < next) {
+      const int64_t t0 = j0 + (int64_t)kWaves * kTile;
+      load_kv_tile<NC, FULLD>(kg, vg, t0 + r, t0 + r < e1, t0 + kTile > e1, hh, d, kN, vN);
     }
     f32x16 sacc, av;
 #pragma unroll
@@ -512,24 +608,33 @@ __global__ __launch_bounds__(kThreads) void pass2_kernel(ScoreArgs a) {
     }
     float vn = 0.f;
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+    for (int c = 0; c < NC; ++c) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = (float)vB[c][e];
-        vn += x * x;
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 x2 = {vB[c][2 * e], vB[c][2 * e + 1]};
+        vn = __builtin_amdgcn_fdot2_f32_bf16(x2, x2, vn, false);
       }
+    }
     vn += __shfl_xor(vn, 32);
     float cc[16];
-    const int itok = (int)tok;
+    float ovf = 0.f;   // becomes NaN if an expansion term overflowed fp32
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const float p = ex2(sacc[v] * a.scale_log2 - lse[v]);
       const float odds = p * __builtin_amdgcn_rcpf(1.f - p);
-      const float dist = fmaxf(an2[v] - 2.f * av[v] + vn, 0.f);
-      const float c = odds * odds * dist;
-      cc[v] = (tok_ok && itok <= lim[v]) ? c : 0.f;
+      const float d0 = an2[v] - 2.f * av[v] + vn;
+      ovf = fmaf(d0, 0.f, ovf);
+      const float dist = fmaxf(d0, 0.f);
+      cc[v] = odds * odds * dist;
     }
-    // the arg-max token of a row takes the merge/fixup value instead
+    if (tok_ok && !(ovf == 0.f)) flags |= LATCH_RANGE;
+    const bool interior = (j0 + kTile <= e1) && (j0 + kTile - 1 <= all_see);
+    if (!interior) {
+      const int itok = (int)tok;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) cc[v] = (tok_ok && itok <= lim[v]) ? cc[v] : 0.f;
+    }
+    // the arg-max token of a row takes the value computed by the merge instead
     const bool hit = (jsl >= j0) && (jsl < j0 + kTile);
     uint64_t bal = __ballot(hit);
     while (bal) {
@@ -550,7 +655,9 @@ __global__ __launch_bounds__(kThreads) void pass2_kernel(ScoreArgs a) {
     for (int v = 0; v < 16; ++v) sum += cc[v];
     sum += __shfl_xor(sum, 32);
     const float raw = sum * invG;
-    if (tok_ok && !(raw <= FLT_MAX)) flags |= (raw != raw) ? LATCH_NONFINITE : LATCH_RANGE;
+    // inputs were checked finite by pass 1 / merge, so an inf or NaN here is an
+    // fp32 overflow of a score or of its terms
+    if (tok_ok && !(raw <= FLT_MAX)) flags |= LATCH_RANGE;
     if (hh == 0 && tok_ok) rawbuf[tok - e0] = raw;
   }
   __syncthreads();
@@ -565,8 +672,8 @@ __global__ __launch_bounds__(kThreads) void pass2_kernel(ScoreArgs a) {
 
 // ------------------------------------------------------------- host side --
 int plan_splits(int64_t n, int Hkv, int64_t* split_len) {
-  // ~1024 workgroups over the chip (4 per CU), at least 256 tokens each.
-  int64_t want = (1024 + Hkv - 1) / Hkv;
+  // about kTargetWG1 workgroups over the chip, at least 256 tokens each.
+  int64_t want = (kTargetWG1 + Hkv - 1) / Hkv;
   const int64_t max_by_len = (n + 255) / 256;
   if (want > max_by_len) want = max_by_len;
   if (want > kMaxSplits) want = kMaxSplits;
@@ -608,46 +715,48 @@ void carve_scratch(void* base, int Hkv, int splits, int DP, Partials* p, RowStat
   rs->a_lo = (u16*)take(rrow * DP * 2);
 }
 
-template <int DP>
+template <int DP, bool FULLD>
 static hipError_t launch_score_dp(void* ctx, const ScoreArgs& a, hipStream_t s) {
   const size_t lds1 = (size_t)kWaves * kTile * (DP + 8) * 2;
   const size_t red = (size_t)kRows * DP * 4;
   const size_t lds = lds1 > red ? lds1 : red;
   static bool attr_done = false;
   if (!attr_done && lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)pass1_kernel<DP>,
+    hipError_t e = hipFuncSetAttribute((const void*)pass1_kernel<DP, FULLD>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
   prof_begin(ctx, "pass1", s);
-  hipLaunchKernelGGL(pass1_kernel<DP>, dim3(a.Hkv * a.splits), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((pass1_kernel<DP, FULLD>), dim3(a.Hkv * a.splits), dim3(kThreads), lds, s, a);
   prof_end(ctx, "pass1", s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   prof_begin(ctx, "merge", s);
-  hipLaunchKernelGGL(merge_kernel<DP>, dim3(a.Hkv * (kRows / kWaves)), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(merge_kernel<DP>, dim3(a.Hkv * kRows), dim3(kThreads), 0, s, a);
   prof_end(ctx, "merge", s);
-  prof_begin(ctx, "fixup", s);
-  hipLaunchKernelGGL(fixup_kernel<DP>, dim3(a.Hkv * kRows), dim3(kThreads), 0, s, a);
-  prof_end(ctx, "fixup", s);
   const int nchunks = (int)((a.n + kChunk2 - 1) / kChunk2);
   prof_begin(ctx, "pass2", s);
-  hipLaunchKernelGGL(pass2_kernel<DP>, dim3((unsigned)a.Hkv * nchunks), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((pass2_kernel<DP, FULLD>), dim3((unsigned)a.Hkv * nchunks), dim3(kThreads), 0, s, a);
   prof_end(ctx, "pass2", s);
   return hipGetLastError();
 }
 
+template <int DP>
+static hipError_t launch_score_d(void* ctx, const ScoreArgs& a, hipStream_t s) {
+  return a.d == DP ? launch_score_dp<DP, true>(ctx, a, s) : launch_score_dp<DP, false>(ctx, a, s);
+}
+
 hipError_t launch_score(void* ctx, const ScoreArgs& a, hipStream_t s) {
   switch (a.DP) {
-    case 32: return launch_score_dp<32>(ctx, a, s);
-    case 64: return launch_score_dp<64>(ctx, a, s);
-    case 96: return launch_score_dp<96>(ctx, a, s);
-    case 128: return launch_score_dp<128>(ctx, a, s);
-    case 160: return launch_score_dp<160>(ctx, a, s);
-    case 192: return launch_score_dp<192>(ctx, a, s);
-    case 224: return launch_score_dp<224>(ctx, a, s);
-    case 256: return launch_score_dp<256>(ctx, a, s);
+    case 32: return launch_score_d<32>(ctx, a, s);
+    case 64: return launch_score_d<64>(ctx, a, s);
+    case 96: return launch_score_d<96>(ctx, a, s);
+    case 128: return launch_score_d<128>(ctx, a, s);
+    case 160: return launch_score_d<160>(ctx, a, s);
+    case 192: return launch_score_d<192>(ctx, a, s);
+    case 224: return launch_score_d<224>(ctx, a, s);
+    case 256: return launch_score_d<256>(ctx, a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdropkv.so")
 
 OK, EINVAL, ESINGULAR, ENONFINITE, ERANGE, EDEVICE, ENOMEM = range(7)
-KERNELS = ("pass1", "merge", "fixup", "pass2", "select", "compact")
+KERNELS = ("pass1", "merge", "pass2", "select", "compact")
 
 
 class DropKVError(RuntimeError):

@@ -4,7 +4,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 One step = the whole path over one synthetic single-layer batch:
-dropkv_score (pass 1, merge, arg-max fix-up, pass 2 with pooling/protection)
+dropkv_score (pass 1, merge, pass 2 with pooling/protection)
 -> dropkv_select -> dropkv_compact, with the inputs already resident in HBM.
 The workload is the Llama-3.1-8B-shaped layer at n = 131072 (Hq=32, Hkv=8,
 d=128, w=8, pool 7, 5 % budget), bf16 inputs drawn by the seeded generator.
@@ -165,7 +165,7 @@ def run(args):
         torch.cuda.synchronize()
         log(f"[bench] calibration copy of {COPY_BYTES} bytes done")
 
-    score_select_us = sum(kern[x]["avg_us"] for x in ("pass1", "merge", "fixup", "pass2", "select")
+    score_select_us = sum(kern[x]["avg_us"] for x in ("pass1", "merge", "pass2", "select")
                           if x in kern)
     dom = max(("pass1", "pass2"), key=lambda x: kern[x]["avg_us"])
     alg = algorithmic_bytes(dom, Hkv, n, d, budget)
@@ -241,7 +241,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str):
     w_scale = COPY_BYTES / (copy_write * 1024.0) if copy_write else None
     kernels = {}
     for short, key in (("pass1", "pass1_kernel"), ("merge", "merge_kernel"),
-                       ("fixup", "fixup_kernel"), ("pass2", "pass2_kernel"),
+                       ("pass2", "pass2_kernel"),
                        ("select", "select_kernel"), ("compact", "compact_kernel")):
         fk, wk = pick(fetch, key), pick(write, key)
         if fk is None or wk is None or f_scale is None or w_scale is None:

@@ -121,7 +121,7 @@ const char *dropkv_strerror(int code);
 /*
  * Per-kernel timing for measurement.  While enabled, every kernel the library
  * launches is bracketed by HIP events on the caller's stream; dropkv_profile_read
- * returns, for the kernel family `name` ("pass1", "merge", "fixup", "pass2",
+ * returns, for the kernel family `name` ("pass1", "merge", "pass2",
  * "select", "compact"), the summed milliseconds and launch count since the last
  * reset (it synchronises on the recorded events).  Disabled by default.
  */

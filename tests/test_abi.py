@@ -42,7 +42,7 @@ def test_host_only_entry_points():
         pytest.skip("libdropkv.so not built")
     assert dropkv.strerror(dropkv.ESINGULAR).startswith("a window query")
     assert dropkv.strerror(12345) == "unknown status"
-    assert dropkv.plan_splits(131072, 8) == 128
+    assert dropkv.plan_splits(131072, 8) == 64
     assert dropkv.plan_splits(22, 2) == 1
     assert dropkv.plan_splits(4096, 8) == 16
     L = dropkv.lib()

@@ -121,6 +121,30 @@ def test_select_exact_on_oracle_scores(ctx):
             np.testing.assert_array_equal(got, want, err_msg=f"n={n} budget={budget}")
 
 
+@pytest.mark.parametrize("kind", ["all_zero", "all_equal", "two_values", "negatives"])
+def test_select_heavy_ties_and_signs(ctx, kind):
+    """Threshold bins holding more than the candidate buffer, and negative keys."""
+    n, Hkv = 20000, 2
+    rng = np.random.default_rng(11)
+    if kind == "all_zero":
+        s = np.zeros((Hkv, n), np.float32)
+    elif kind == "all_equal":
+        s = np.full((Hkv, n), 3.25, np.float32)
+    elif kind == "two_values":
+        s = np.where(rng.random((Hkv, n)) < 0.5, 1.0, 2.0).astype(np.float32)
+    else:
+        s = (rng.standard_normal((Hkv, n)) * 100).astype(np.float32)
+        s[0, :50] = -0.0
+    s[:, -8:] = np.inf
+    sd = torch.from_numpy(s).cuda()
+    for budget in (8, 100, 9999, 19999):
+        keep = torch.full((Hkv, budget), -9, dtype=torch.int32, device="cuda")
+        ctx.select(sd, Hkv, n, budget, keep)
+        assert ctx.sync() == dropkv.OK
+        np.testing.assert_array_equal(keep.cpu().numpy(), orc.select(s.astype(np.float64), budget),
+                                      err_msg=f"{kind} budget={budget}")
+
+
 def test_singular_rejected_and_select_withheld(ctx):
     n, d = 40, 8
     q = np.zeros((1, 1, d), np.float32); q[0, 0, 0] = 1.0
