@@ -47,6 +47,12 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
 }
+// Direct global->LDS loads complete on the vector-memory counter, and the
+// compiler does not order later LDS reads after them: wait for all of them.
+__device__ __forceinline__ void wait_lds_dma() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
@@ -79,6 +85,40 @@ __device__ __forceinline__ int wave_or_i(int x) {
 // taken straight from S^T's registers by ordering the MFMA's reduction slots as
 // token(kc, h, e) = 16*kc + 8*(e/4) + 4*h + e%4, and V^T's operand is gathered
 // from a per-wave LDS copy of the V tile in that same order.
+
+// LDS rows that MFMA operands are read from: a row of DP bf16 is CH = DP/8
+// 16-byte chunks, chunk c stored at position c ^ (row & MASK) of a row of CHP
+// (CH rounded up to a power of two) chunks.  Lanes reading the same chunk of 16
+// consecutive rows, or 64 bytes of two rows four apart, then hit distinct banks.
+template <int DP>
+struct RowLayout {
+  static constexpr int CH = DP / 8;
+  static constexpr int CHP = CH <= 4 ? 4 : CH <= 8 ? 8 : CH <= 16 ? 16 : 32;
+  static constexpr int ROWB = CHP * 16;
+  static constexpr int MASK = CHP < 16 ? CHP - 1 : 15;
+  __device__ __forceinline__ static int off(int row, int chunk) {
+    return row * ROWB + ((chunk ^ (row & MASK)) << 4);
+  }
+};
+
+template <int DP>
+__device__ __forceinline__ bf16x8 lds8(const unsigned char* base, int row, int chunk) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + RowLayout<DP>::off(row, chunk)));
+}
+
+// Stage rows [0, 32) of a row-major bf16 matrix (rows >= nrows and columns >= d
+// are zero) into LDS with the swizzled layout.  Whole workgroup.
+template <int DP>
+__device__ __forceinline__ void stage_rows(unsigned char* dst, const u16* src, int nrows, int ld, int d) {
+  using L = RowLayout<DP>;
+  for (int i = threadIdx.x; i < kRows * L::CH; i += kThreads) {
+    const int row = i / L::CH, ch = i % L::CH;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (row < nrows && ch * 8 < d) x = *reinterpret_cast<const u32x4*>(src + (size_t)row * ld + ch * 8);
+    *reinterpret_cast<u32x4*>(dst + L::off(row, ch)) = x;
+  }
+}
+
 // One 32-token K/V tile in MFMA operand layout: lane l holds 8 consecutive d
 // values (16 bytes) of token l%32.  Interior tiles load unconditionally; only a
 // ragged tile (tokens past the range end) or a head dimension below the padded
@@ -105,13 +145,55 @@ __device__ __forceinline__ void load_kv_tile(const u16* kg, const u16* vg, int64
   }
 }
 
+template <int DP>
+constexpr size_t pass1_lds_bytes() {
+  return (size_t)kRows * RowLayout<DP>::ROWB * (1 + kWaves);
+}
+
+// K tile into registers (operand layout as load_kv_tile).
+template <int NC, bool FULLD>
+__device__ __forceinline__ void load_k_tile(const u16* kg, int64_t tok, bool tok_ok, bool ragged, int hh,
+                                            int d, bf16x8 (&kk)[NC]) {
+  if (FULLD && !ragged) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kk[c] = load8(kg + tok * d + 16 * c + 8 * hh);
+  } else {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int col = 16 * c + 8 * hh;
+      kk[c] = (tok_ok && (FULLD || col < d)) ? load8(kg + tok * d + col) : zero8();
+    }
+  }
+}
+
+// V tile of tokens [t0, t0+32) straight into an LDS slot (direct global->LDS
+// loads, no registers), in RowLayout order: instruction i fills bytes
+// [1024 i, 1024 i + 1024) of the slot, lane l the 16 bytes at 1024 i + 16 l.
+// Padding chunks (column >= d) and tokens past `end` read some in-range row of
+// the tile instead; they are multiplied by p = 0 or never used.
+template <int DP>
+__device__ __forceinline__ void dma_v_tile(const u16* vg, int64_t t0, int64_t end, int d,
+                                           unsigned char* slot, int lane) {
+  using L = RowLayout<DP>;
+#pragma unroll
+  for (int i = 0; i < L::CHP / 2; ++i) {
+    const int P = 64 * i + lane;
+    const int row = P / L::CHP, pc = P % L::CHP;
+    int c = pc ^ (row & L::MASK);
+    int64_t tok = t0 + row;
+    if (tok >= end) tok = t0;
+    if (c * 8 >= d) c = 0;
+    __builtin_amdgcn_global_load_lds((const void*)(vg + tok * d + c * 8),
+                                     (__attribute__((address_space(3))) void*)(slot + 1024 * i), 16, 0, 0);
+  }
+}
+
 template <int DP, bool FULLD>
-__global__ __launch_bounds__(kThreads) void pass1_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kThreads, (DP <= 128 ? 2 : 1)) void pass1_kernel(ScoreArgs a) {
+  using L = RowLayout<DP>;
   constexpr int NC = DP / 16;
   constexpr int DB = DP / 32;
-  constexpr int LS = DP + 8;  // LDS row stride (u16): rows 4 apart land 16 banks apart
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  u16* lds = reinterpret_cast<u16*>(smem_raw);
   __shared__ float sm_m[kWaves][kRows], sm_S[kWaves][kRows], sm_Sx[kWaves][kRows];
   __shared__ int sm_j[kWaves][kRows], sm_bad[kWaves][kRows];
 
@@ -127,14 +209,11 @@ __global__ __launch_bounds__(kThreads) void pass1_kernel(ScoreArgs a) {
   const bool row_ok = r < a.M;
   const int64_t causal = row_ok ? a.n - a.w + (r % a.w) : -1;
   const int64_t all_see = a.n - a.w;   // every window query sees keys 0..n-w
+  unsigned char* qs = smem_raw;                                  // Q rows of the group
+  unsigned char* vs = smem_raw + (size_t)kRows * L::ROWB * (1 + wid);   // this wave's V tile
 
-  bf16x8 qB[NC];
-  const u16* qrow = a.q + ((size_t)g * a.M + (row_ok ? r : 0)) * d;
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int col = 16 * c + 8 * hh;
-    qB[c] = (row_ok && col < d) ? load8(qrow + col) : zero8();
-  }
+  stage_rows<DP>(qs, a.q + (size_t)g * a.M * d, a.M, d, d);
+  __syncthreads();
 
   float m = -INFINITY, S = 0.f, Sx = 0.f, chk = 0.f;
   int jst = INT_MAX, bad = 0;
@@ -145,30 +224,18 @@ __global__ __launch_bounds__(kThreads) void pass1_kernel(ScoreArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
 
-  u16* my = lds + wid * kTile * LS;
-  // the next tile of this wave is in flight while the current one is processed
-  bf16x8 kN[NC], vN[NC];
-  if (wid < ntiles) {
-    const int64_t t0 = jbeg + (int64_t)wid * kTile;
-    load_kv_tile<NC, FULLD>(kg, vg, t0 + r, t0 + r < jend, t0 + kTile > jend, hh, d, kN, vN);
-  }
+  // Each wave walks its tiles one at a time; the memory latency of one wave is
+  // covered by the other waves of the CU (two workgroups per CU).
   for (int t = wid; t < ntiles; t += kWaves) {
     const int64_t j0 = jbeg + (int64_t)t * kTile;
-    bf16x8 kA[NC], vv[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) { kA[c] = kN[c]; vv[c] = vN[c]; }
-    if (t + kWaves < ntiles) {
-      const int64_t t0 = j0 + (int64_t)kWaves * kTile;
-      load_kv_tile<NC, FULLD>(kg, vg, t0 + r, t0 + r < jend, t0 + kTile > jend, hh, d, kN, vN);
-    }
+    bf16x8 kk[NC];
+    load_k_tile<NC, FULLD>(kg, j0 + r, j0 + r < jend, j0 + kTile > jend, hh, d, kk);
+    dma_v_tile<DP>(vg, j0, jend, d, vs, lane);
     f32x16 st;
 #pragma unroll
     for (int v = 0; v < 16; ++v) st[v] = 0.f;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) st = mfma32(kA[c], qB[c], st);
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      *reinterpret_cast<u32x4*>(my + r * LS + 16 * c + 8 * hh) = __builtin_bit_cast(u32x4, vv[c]);
+    for (int c = 0; c < NC; ++c) st = mfma32(kk[c], lds8<DP>(qs, r, 2 * c + hh), st);
 
     // logits in log2 units; masks only on tiles that reach past the split end
     // or into the window (rows >= M have zero queries and are never read)
@@ -255,16 +322,18 @@ __global__ __launch_bounds__(kThreads) void pass1_kernel(ScoreArgs a) {
         ph[kc][e] = hi;
         pl[kc][e] = (__bf16)(x - (float)hi);
       }
+    wait_lds_dma();
     wave_sync_lds();
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
         bf16x8 va;
+        const int dch = 4 * b + (r >> 3);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int tl = 16 * kc + 8 * (e >> 2) + 4 * hh + (e & 3);
-          va[e] = __builtin_bit_cast(__bf16, my[tl * LS + 32 * b + r]);
+          va[e] = *reinterpret_cast<const __bf16*>(vs + L::off(tl, dch) + (r & 7) * 2);
         }
         acc[b] = mfma32(va, ph[kc], acc[b]);
         acc[b] = mfma32(va, pl[kc], acc[b]);
@@ -494,7 +563,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
     float tt = 0.f;
 #pragma unroll
     for (int k = 0; k < NG; ++k) tt += red[k * (DP + 1) + tid];
-    const float av = tt * invS;
+    // columns >= d hold products with padding rows of V: they are zero by definition
+    const float av = tid < a.d ? tt * invS : 0.f;
     if (!(fabsf(av) <= FLT_MAX)) nonfin = 1;
     an2 = av * av;
     const __bf16 hi = (__bf16)av;
@@ -535,10 +605,23 @@ constexpr int kMaxRadius = 64;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+template <int DP>
+constexpr size_t pass2_lds_bytes() {
+  return (size_t)3 * kRows * RowLayout<DP>::ROWB + 2 * kRows * 4 +
+         (size_t)(kChunk2 + 2 * kMaxRadius + kTile) * 4;
+}
+
 template <int DP, bool FULLD>
-__global__ __launch_bounds__(kThreads) void pass2_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kThreads, (DP <= 128 ? 2 : 1)) void pass2_kernel(ScoreArgs a) {
+  using L = RowLayout<DP>;
   constexpr int NC = DP / 16;
-  __shared__ float rawbuf[kChunk2 + 2 * kMaxRadius + kTile];
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  unsigned char* qs = smem_raw;                       // Q rows
+  unsigned char* hs = qs + kRows * L::ROWB;           // a (bf16 high part) rows
+  unsigned char* ls = hs + kRows * L::ROWB;           // a (bf16 remainder) rows
+  float* lse_s = reinterpret_cast<float*>(ls + kRows * L::ROWB);
+  float* an2_s = lse_s + kRows;
+  float* rawbuf = an2_s + kRows;
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
   const int64_t n = a.n;
@@ -554,85 +637,78 @@ __global__ __launch_bounds__(kThreads) void pass2_kernel(ScoreArgs a) {
   const size_t ro0 = (size_t)g * kRows;
   const int64_t all_see = n - a.w;
 
-  bf16x8 qA[NC], hA[NC], lA[NC];
-  const bool qrow_ok = r < a.M;
-  const u16* qrow = a.q + ((size_t)g * a.M + (qrow_ok ? r : 0)) * d;
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int col = 16 * c + 8 * hh;
-    qA[c] = (qrow_ok && col < d) ? load8(qrow + col) : zero8();
-    hA[c] = load8(a.rs.a_hi + (ro0 + r) * DP + col);
-    lA[c] = load8(a.rs.a_lo + (ro0 + r) * DP + col);
-  }
-  // per-lane row constants; rows >= M carry lse = +inf, so their p and
-  // contribution are exactly 0
-  float lse[16], an2[16];
-  int lim[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int rv = 8 * (v >> 2) + 4 * hh + (v & 3);
-    lse[v] = a.rs.lse2[ro0 + rv];
-    an2[v] = a.rs.an2[ro0 + rv];
-    lim[v] = rv < a.M ? (int)(n - a.w + (rv % a.w)) : -1;
+  stage_rows<DP>(qs, a.q + (size_t)g * a.M * d, a.M, d, d);
+  stage_rows<DP>(hs, a.rs.a_hi + ro0 * DP, kRows, DP, DP);
+  stage_rows<DP>(ls, a.rs.a_lo + ro0 * DP, kRows, DP, DP);
+  // rows >= M carry lse = +inf (set by the merge): their p and contribution are 0
+  if (tid < kRows) {
+    lse_s[tid] = a.rs.lse2[ro0 + tid];
+    an2_s[tid] = a.rs.an2[ro0 + tid];
   }
   const int jsl = (lane < kRows) ? a.rs.jstar[ro0 + lane] : -1;
   const float csl = (lane < kRows) ? a.rs.cstar[ro0 + lane] : 0.f;
   const float invG = 1.f / (float)a.G;
   uint32_t flags = 0;
+  __syncthreads();
 
-  bf16x8 kN[NC], vN[NC];
-  if (wid < next) {
-    const int64_t t0 = e0 + (int64_t)wid * kTile;
-    load_kv_tile<NC, FULLD>(kg, vg, t0 + r, t0 + r < e1, t0 + kTile > e1, hh, d, kN, vN);
-  }
-  for (int t = wid; t < next; t += kWaves) {
+  auto issue = [&](int t, bf16x8 (&kk)[NC], bf16x8 (&vv)[NC]) {
+    const int64_t t0 = e0 + (int64_t)t * kTile;
+    load_kv_tile<NC, FULLD>(kg, vg, t0 + r, t0 + r < e1, t0 + kTile > e1, hh, d, kk, vv);
+  };
+  auto tile = [&](int t, bf16x8 (&kB)[NC], bf16x8 (&vB)[NC], bf16x8 (&kn)[NC], bf16x8 (&vn)[NC]) {
     const int64_t j0 = e0 + (int64_t)t * kTile;
     const int64_t tok = j0 + r;
     const bool tok_ok = tok < e1;
-    bf16x8 kB[NC], vB[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) { kB[c] = kN[c]; vB[c] = vN[c]; }
-    if (t + kWaves < next) {
-      const int64_t t0 = j0 + (int64_t)kWaves * kTile;
-      load_kv_tile<NC, FULLD>(kg, vg, t0 + r, t0 + r < e1, t0 + kTile > e1, hh, d, kN, vN);
-    }
+    if (t + kWaves < next) issue(t + kWaves, kn, vn);
     f32x16 sacc, av;
 #pragma unroll
     for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; av[v] = 0.f; }
 #pragma unroll
-    for (int c = 0; c < NC; ++c) sacc = mfma32(qA[c], kB[c], sacc);
+    for (int c = 0; c < NC; ++c) sacc = mfma32(lds8<DP>(qs, r, 2 * c + hh), kB[c], sacc);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      av = mfma32(hA[c], vB[c], av);
-      av = mfma32(lA[c], vB[c], av);
+      av = mfma32(lds8<DP>(hs, r, 2 * c + hh), vB[c], av);
+      av = mfma32(lds8<DP>(ls, r, 2 * c + hh), vB[c], av);
     }
-    float vn = 0.f;
+    float vn2 = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bf16x2 x2 = {vB[c][2 * e], vB[c][2 * e + 1]};
-        vn = __builtin_amdgcn_fdot2_f32_bf16(x2, x2, vn, false);
+        vn2 = __builtin_amdgcn_fdot2_f32_bf16(x2, x2, vn2, false);
       }
     }
-    vn += __shfl_xor(vn, 32);
+    vn2 += __shfl_xor(vn2, 32);
     float cc[16];
     float ovf = 0.f;   // becomes NaN if an expansion term overflowed fp32
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float p = ex2(sacc[v] * a.scale_log2 - lse[v]);
-      const float odds = p * __builtin_amdgcn_rcpf(1.f - p);
-      const float d0 = an2[v] - 2.f * av[v] + vn;
-      ovf = fmaf(d0, 0.f, ovf);
-      const float dist = fmaxf(d0, 0.f);
-      cc[v] = odds * odds * dist;
+    for (int q4 = 0; q4 < 4; ++q4) {
+      // this lane's rows 8*q4 + 4*hh + 0..3
+      const float4 l4 = *reinterpret_cast<const float4*>(lse_s + 8 * q4 + 4 * hh);
+      const float4 n4 = *reinterpret_cast<const float4*>(an2_s + 8 * q4 + 4 * hh);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float nv[4] = {n4.x, n4.y, n4.z, n4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int v = 4 * q4 + i;
+        const float p = ex2(sacc[v] * a.scale_log2 - lv[i]);
+        const float odds = p * __builtin_amdgcn_rcpf(1.f - p);
+        const float d0 = nv[i] - 2.f * av[v] + vn2;
+        ovf = fmaf(d0, 0.f, ovf);
+        cc[v] = odds * odds * fmaxf(d0, 0.f);
+      }
     }
     if (tok_ok && !(ovf == 0.f)) flags |= LATCH_RANGE;
     const bool interior = (j0 + kTile <= e1) && (j0 + kTile - 1 <= all_see);
     if (!interior) {
       const int itok = (int)tok;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) cc[v] = (tok_ok && itok <= lim[v]) ? cc[v] : 0.f;
+      for (int v = 0; v < 16; ++v) {
+        const int rv = 8 * (v >> 2) + 4 * hh + (v & 3);
+        const int lim = rv < a.M ? (int)(n - a.w + (rv % a.w)) : -1;
+        cc[v] = (tok_ok && itok <= lim) ? cc[v] : 0.f;
+      }
     }
     // the arg-max token of a row takes the value computed by the merge instead
     const bool hit = (jsl >= j0) && (jsl < j0 + kTile);
@@ -642,9 +718,9 @@ __global__ __launch_bounds__(kThreads) void pass2_kernel(ScoreArgs a) {
       bal &= bal - 1;
       const int js = __shfl(jsl, rr);
       const float cs = __shfl(csl, rr);
-      const int L = (int)(js - j0) + 32 * ((rr >> 2) & 1);
+      const int Ln = (int)(js - j0) + 32 * ((rr >> 2) & 1);
       const int vr = 4 * (rr >> 3) + (rr & 3);
-      if (lane == L && tok_ok) {
+      if (lane == Ln && tok_ok) {
 #pragma unroll
         for (int v = 0; v < 16; ++v)
           if (v == vr) cc[v] = cs;
@@ -659,6 +735,13 @@ __global__ __launch_bounds__(kThreads) void pass2_kernel(ScoreArgs a) {
     // fp32 overflow of a score or of its terms
     if (tok_ok && !(raw <= FLT_MAX)) flags |= LATCH_RANGE;
     if (hh == 0 && tok_ok) rawbuf[tok - e0] = raw;
+  };
+
+  bf16x8 kX[NC], vX[NC], kY[NC], vY[NC];
+  if (wid < next) issue(wid, kX, vX);
+  for (int t = wid; t < next; t += 2 * kWaves) {
+    tile(t, kX, vX, kY, vY);
+    if (t + kWaves < next) tile(t + kWaves, kY, vY, kX, vX);
   }
   __syncthreads();
   for (int64_t j = c0 + tid; j < c1; j += kThreads) {
@@ -717,18 +800,25 @@ void carve_scratch(void* base, int Hkv, int splits, int DP, Partials* p, RowStat
 
 template <int DP, bool FULLD>
 static hipError_t launch_score_dp(void* ctx, const ScoreArgs& a, hipStream_t s) {
-  const size_t lds1 = (size_t)kWaves * kTile * (DP + 8) * 2;
   const size_t red = (size_t)kRows * DP * 4;
-  const size_t lds = lds1 > red ? lds1 : red;
+  const size_t lds1 = pass1_lds_bytes<DP>() > red ? pass1_lds_bytes<DP>() : red;
+  const size_t lds2 = pass2_lds_bytes<DP>();
   static bool attr_done = false;
-  if (!attr_done && lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)pass1_kernel<DP, FULLD>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+  if (!attr_done) {
+    if (lds1 > 65536) {
+      hipError_t e = hipFuncSetAttribute((const void*)pass1_kernel<DP, FULLD>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
+      if (e != hipSuccess) return e;
+    }
+    if (lds2 > 65536) {
+      hipError_t e = hipFuncSetAttribute((const void*)pass2_kernel<DP, FULLD>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
+      if (e != hipSuccess) return e;
+    }
     attr_done = true;
   }
   prof_begin(ctx, "pass1", s);
-  hipLaunchKernelGGL((pass1_kernel<DP, FULLD>), dim3(a.Hkv * a.splits), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((pass1_kernel<DP, FULLD>), dim3(a.Hkv * a.splits), dim3(kThreads), lds1, s, a);
   prof_end(ctx, "pass1", s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -737,7 +827,8 @@ static hipError_t launch_score_dp(void* ctx, const ScoreArgs& a, hipStream_t s) 
   prof_end(ctx, "merge", s);
   const int nchunks = (int)((a.n + kChunk2 - 1) / kChunk2);
   prof_begin(ctx, "pass2", s);
-  hipLaunchKernelGGL((pass2_kernel<DP, FULLD>), dim3((unsigned)a.Hkv * nchunks), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((pass2_kernel<DP, FULLD>), dim3((unsigned)a.Hkv * nchunks), dim3(kThreads), lds2,
+                     s, a);
   prof_end(ctx, "pass2", s);
   return hipGetLastError();
 }
