@@ -156,6 +156,7 @@ int dropkv_score(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
   a.n = n; a.w = w; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.G = G; a.M = G * w; a.pool = pool;
   a.DP = (d + 31) / 32 * 32;
   a.splits = plan_splits(n, Hkv, &a.split_len);
+  a.chunks2 = plan_chunks2(n, Hkv, &a.chunk2_len);
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
   a.latch = c->latch;
   const size_t need = score_scratch_bytes(Hkv, a.splits, a.DP);

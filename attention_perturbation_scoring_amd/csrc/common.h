@@ -21,8 +21,28 @@ constexpr int kRows = 32;        // window-query rows per KV head handled by one
 constexpr int kTile = 32;        // tokens per MFMA tile
 constexpr int kWaves = 4;        // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kChunk2 = 2048;    // tokens per pass-2 workgroup (before the pooling halo)
-constexpr int kTargetWG1 = 512;  // pass-1 workgroups aimed for over all heads (2 per CU)
+// Launch shape of the two K/V passes (d <= 128): waves per SIMD the register
+// budget is cut for, and whether a wave starts its next tile's loads before
+// finishing the current tile (tuning knobs; the defaults are the measured best).
+#ifndef DROPKV_P1_WAVES
+#define DROPKV_P1_WAVES 2
+#endif
+#ifndef DROPKV_P2_WAVES
+#define DROPKV_P2_WAVES 3
+#endif
+#ifndef DROPKV_P1_OVERLAP
+#define DROPKV_P1_OVERLAP 0
+#endif
+#ifndef DROPKV_P2_OVERLAP
+#define DROPKV_P2_OVERLAP 0
+#endif
+constexpr int kP1Waves = DROPKV_P1_WAVES;
+constexpr int kP2Waves = DROPKV_P2_WAVES;
+constexpr bool kP1Overlap = DROPKV_P1_OVERLAP != 0;
+constexpr bool kP2Overlap = DROPKV_P2_OVERLAP != 0;
+constexpr int kChunk2 = 2048;                // most tokens per pass-2 workgroup (before the pooling halo)
+constexpr int kTargetWG1 = 256 * kP1Waves;   // pass-1 workgroups aimed for over all heads
+constexpr int kTargetWG2 = 256 * kP2Waves;   // pass-2 workgroups aimed for over all heads
 
 // S_excl below this (argmax probability above ~0.94) routes the arg-max term
 // through the exact exclusion kernel instead of the fp32 output a.
@@ -59,6 +79,8 @@ struct ScoreArgs {
   int w, Hq, Hkv, d, G, M, pool, DP;
   int splits;
   int64_t split_len;
+  int chunks2;          // pass-2 workgroups per head
+  int64_t chunk2_len;   // tokens per pass-2 workgroup (multiple of the tile, <= kChunk2)
   float scale_log2;   // log2(e) / sqrt(d)
   Partials part;
   RowState rs;
@@ -101,5 +123,6 @@ hipError_t launch_compact(void* ctx, const u16* k, const u16* v, int Hkv, int64_
 size_t score_scratch_bytes(int Hkv, int splits, int DP);
 void carve_scratch(void* base, int Hkv, int splits, int DP, Partials* p, RowState* rs);
 int plan_splits(int64_t n, int Hkv, int64_t* split_len);
+int plan_chunks2(int64_t n, int Hkv, int64_t* chunk_len);
 
 }  // namespace dropkv

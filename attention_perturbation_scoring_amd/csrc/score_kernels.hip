@@ -17,7 +17,7 @@
 //            Rows whose arg-max holds probability above ~0.94 recompute the
 //            output over the other tokens exactly and take the arg-max term as
 //            p*^2 ||abar - v_j*||^2, which stays accurate as p* -> 1.
-//   pass2  : per (KV head, 2048-token chunk + pooling halo) stream K and V again:
+//   pass2  : per (KV head, chunk of up to 2048 tokens + pooling halo) stream K and V again:
 //            logits Q K^T and A V^T (a as hi + lo) on MFMA, then per element
 //            p = 2^(l - lse), odds = p/(1-p), ||a - v||^2 = ||a||^2 - 2 a.v + ||v||^2,
 //            contribution odds^2 ||a - v||^2, summed over the M rows, divided by
@@ -47,12 +47,7 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
 }
-// Direct global->LDS loads complete on the vector-memory counter, and the
-// compiler does not order later LDS reads after them: wait for all of them.
-__device__ __forceinline__ void wait_lds_dma() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __builtin_amdgcn_wave_barrier();
-}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
@@ -147,7 +142,7 @@ __device__ __forceinline__ void load_kv_tile(const u16* kg, const u16* vg, int64
 
 template <int DP>
 constexpr size_t pass1_lds_bytes() {
-  return (size_t)kRows * RowLayout<DP>::ROWB * (1 + kWaves);
+  return (size_t)kRows * RowLayout<DP>::ROWB * (1 + 2 * kWaves);
 }
 
 // K tile into registers (operand layout as load_kv_tile).
@@ -166,30 +161,59 @@ __device__ __forceinline__ void load_k_tile(const u16* kg, int64_t tok, bool tok
   }
 }
 
-// V tile of tokens [t0, t0+32) straight into an LDS slot (direct global->LDS
-// loads, no registers), in RowLayout order: instruction i fills bytes
-// [1024 i, 1024 i + 1024) of the slot, lane l the 16 bytes at 1024 i + 16 l.
-// Padding chunks (column >= d) and tokens past `end` read some in-range row of
-// the tile instead; they are multiplied by p = 0 or never used.
+// One direct global->LDS load of 16 bytes per lane: lane l's bytes land at LDS
+// address `lds` + 16 l.  Issued from inline assembly so that the compiler does
+// not order every later LDS access after it; the caller waits explicitly
+// (vector-memory counter) before reading the destination.
+__device__ __forceinline__ void dma16(const void* gaddr, unsigned char* lds_generic) {
+  const unsigned lds = __builtin_amdgcn_readfirstlane(
+      (unsigned)(size_t)((__attribute__((address_space(3))) unsigned char*)lds_generic));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds)
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmem_below() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// LDS layout of a V tile: row-major rows of CHP 16-byte chunks; on rows with
+// bit 2 set the chunk index is XOR-ed with 4 (a 64-byte shift), so the two
+// lane halves of a transposed read -- rows tau and tau + 4 -- hit disjoint
+// banks, while every lane's address stays a fixed base plus a per-row constant.
+template <int DP>
+struct VLayout {
+  static constexpr int CHP = RowLayout<DP>::CHP;
+  static constexpr int ROWB = RowLayout<DP>::ROWB;
+  static constexpr int SW = CHP >= 8 ? 4 : 0;
+  __device__ __forceinline__ static int off(int row, int chunk) {
+    return row * ROWB + ((chunk ^ (((row >> 2) & 1) * SW)) << 4);
+  }
+};
+
+// V tile of tokens [t0, t0+32) straight into an LDS slot (no registers), in
+// VLayout order: instruction i fills bytes [1024 i, 1024 i + 1024) of the slot,
+// lane l the 16 bytes at 1024 i + 16 l.  Padding chunks (column >= d) and
+// tokens past `end` read some in-range row of the tile instead; they are
+// multiplied by p = 0 or never used.  Issues RowLayout<DP>::CHP / 2 loads.
 template <int DP>
 __device__ __forceinline__ void dma_v_tile(const u16* vg, int64_t t0, int64_t end, int d,
                                            unsigned char* slot, int lane) {
-  using L = RowLayout<DP>;
+  using L = VLayout<DP>;
 #pragma unroll
   for (int i = 0; i < L::CHP / 2; ++i) {
     const int P = 64 * i + lane;
     const int row = P / L::CHP, pc = P % L::CHP;
-    int c = pc ^ (row & L::MASK);
+    int c = pc ^ (((row >> 2) & 1) * L::SW);
     int64_t tok = t0 + row;
     if (tok >= end) tok = t0;
     if (c * 8 >= d) c = 0;
-    __builtin_amdgcn_global_load_lds((const void*)(vg + tok * d + c * 8),
-                                     (__attribute__((address_space(3))) void*)(slot + 1024 * i), 16, 0, 0);
+    dma16(vg + tok * d + c * 8, slot + 1024 * i);
   }
 }
 
 template <int DP, bool FULLD>
-__global__ __launch_bounds__(kThreads, (DP <= 128 ? 2 : 1)) void pass1_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kThreads, (DP <= 128 ? kP1Waves : 1)) void pass1_kernel(ScoreArgs a) {
   using L = RowLayout<DP>;
   constexpr int NC = DP / 16;
   constexpr int DB = DP / 32;
@@ -210,7 +234,8 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? 2 : 1)) void pass1_kernel(Sc
   const int64_t causal = row_ok ? a.n - a.w + (r % a.w) : -1;
   const int64_t all_see = a.n - a.w;   // every window query sees keys 0..n-w
   unsigned char* qs = smem_raw;                                  // Q rows of the group
-  unsigned char* vs = smem_raw + (size_t)kRows * L::ROWB * (1 + wid);   // this wave's V tile
+  unsigned char* vslot0 = smem_raw + (size_t)kRows * L::ROWB * (1 + 2 * wid);   // this wave's V tiles
+  unsigned char* vslot1 = vslot0 + (size_t)kRows * L::ROWB;
 
   stage_rows<DP>(qs, a.q + (size_t)g * a.M * d, a.M, d, d);
   __syncthreads();
@@ -224,18 +249,42 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? 2 : 1)) void pass1_kernel(Sc
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
 
-  // Each wave walks its tiles one at a time; the memory latency of one wave is
-  // covered by the other waves of the CU (two workgroups per CU).
+  // Each wave walks its tiles in order.  The next tile's K goes into the same
+  // registers as soon as the logits have consumed them, and its V into the
+  // other LDS slot, so those loads fly during this tile's softmax and PV; the
+  // second workgroup on the CU covers the rest of the latency.
+  constexpr int kLoadsPerTile = NC + L::CHP / 2;
+  bf16x8 kk[NC];
+  if (kP1Overlap && wid < ntiles) {
+    const int64_t f0 = jbeg + (int64_t)wid * kTile;
+    load_k_tile<NC, FULLD>(kg, f0 + r, f0 + r < jend, f0 + kTile > jend, hh, d, kk);
+    dma_v_tile<DP>(vg, f0, jend, d, vslot0, lane);
+  }
+  int slot = 0;
   for (int t = wid; t < ntiles; t += kWaves) {
     const int64_t j0 = jbeg + (int64_t)t * kTile;
-    bf16x8 kk[NC];
-    load_k_tile<NC, FULLD>(kg, j0 + r, j0 + r < jend, j0 + kTile > jend, hh, d, kk);
-    dma_v_tile<DP>(vg, j0, jend, d, vs, lane);
-    f32x16 st;
+    unsigned char* vs = slot ? vslot1 : vslot0;
+    if (!kP1Overlap) {
+      load_k_tile<NC, FULLD>(kg, j0 + r, j0 + r < jend, j0 + kTile > jend, hh, d, kk);
+      dma_v_tile<DP>(vg, j0, jend, d, vslot0, lane);
+    }
+    // two independent accumulation chains keep the matrix core busy
+    f32x16 st, st1;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) st[v] = 0.f;
+    for (int v = 0; v < 16; ++v) { st[v] = 0.f; st1[v] = 0.f; }
 #pragma unroll
-    for (int c = 0; c < NC; ++c) st = mfma32(kk[c], lds8<DP>(qs, r, 2 * c + hh), st);
+    for (int c = 0; c < NC; c += 2) {
+      st = mfma32(kk[c], lds8<DP>(qs, r, 2 * c + hh), st);
+      if (c + 1 < NC) st1 = mfma32(kk[c + 1], lds8<DP>(qs, r, 2 * c + 2 + hh), st1);
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) st[v] += st1[v];
+    const bool more = t + kWaves < ntiles;
+    if (kP1Overlap && more) {
+      const int64_t n0 = j0 + (int64_t)kWaves * kTile;
+      load_k_tile<NC, FULLD>(kg, n0 + r, n0 + r < jend, n0 + kTile > jend, hh, d, kk);
+      dma_v_tile<DP>(vg, n0, jend, d, slot ? vslot0 : vslot1, lane);
+    }
 
     // logits in log2 units; masks only on tiles that reach past the split end
     // or into the window (rows >= M have zero queries and are never read)
@@ -322,23 +371,32 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? 2 : 1)) void pass1_kernel(Sc
         ph[kc][e] = hi;
         pl[kc][e] = (__bf16)(x - (float)hi);
       }
-    wait_lds_dma();
+    // this tile's V has landed once at most the loads issued above are pending
+    if (kP1Overlap && more) wait_vmem_below<kLoadsPerTile>();
+    else wait_vmem_below<0>();
     wave_sync_lds();
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+    for (int kc = 0; kc < 2; ++kc) {
+      bf16x8 va[DB];
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        bf16x8 va;
-        const int dch = 4 * b + (r >> 3);
+      for (int b = 0; b < DB; ++b) {
+        // rows 16 kc + 8 (e/4) + 4 hh + e%4: bit 2 of every such row is hh, so
+        // the lane's address is one base plus a compile-time row offset
+        const unsigned char* vb = vs + VLayout<DP>::off(4 * hh, 4 * b + (r >> 3)) + (r & 7) * 2;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int tl = 16 * kc + 8 * (e >> 2) + 4 * hh + (e & 3);
-          va[e] = *reinterpret_cast<const __bf16*>(vs + L::off(tl, dch) + (r & 7) * 2);
+          const int tl = 16 * kc + 8 * (e >> 2) + (e & 3);
+          va[b][e] = *reinterpret_cast<const __bf16*>(vb + tl * L::ROWB);
         }
-        acc[b] = mfma32(va, ph[kc], acc[b]);
-        acc[b] = mfma32(va, pl[kc], acc[b]);
       }
+      // the DB accumulators are independent: issue them back to back
+#pragma unroll
+      for (int b = 0; b < DB; ++b) acc[b] = mfma32(va[b], ph[kc], acc[b]);
+#pragma unroll
+      for (int b = 0; b < DB; ++b) acc[b] = mfma32(va[b], pl[kc], acc[b]);
+    }
     wave_sync_lds();
+    if (kP1Overlap) slot ^= 1;
   }
   if (!(chk == 0.f)) bad = 1;
 
@@ -612,7 +670,7 @@ constexpr size_t pass2_lds_bytes() {
 }
 
 template <int DP, bool FULLD>
-__global__ __launch_bounds__(kThreads, (DP <= 128 ? 2 : 1)) void pass2_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_kernel(ScoreArgs a) {
   using L = RowLayout<DP>;
   constexpr int NC = DP / 16;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -625,9 +683,8 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? 2 : 1)) void pass2_kernel(Sc
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
   const int64_t n = a.n;
-  const int nchunks = (int)((n + kChunk2 - 1) / kChunk2);
-  const int g = blockIdx.x / nchunks, ch = blockIdx.x % nchunks;
-  const int64_t c0 = (int64_t)ch * kChunk2, c1 = min(n, c0 + kChunk2);
+  const int g = blockIdx.x / a.chunks2, ch = blockIdx.x % a.chunks2;
+  const int64_t c0 = (int64_t)ch * a.chunk2_len, c1 = min(n, c0 + a.chunk2_len);
   const int rad = (a.pool - 1) / 2;
   const int64_t e0 = max((int64_t)0, c0 - rad), e1 = min(n, c1 + rad);
   const int next = (int)((e1 - e0 + kTile - 1) / kTile);
@@ -655,21 +712,31 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? 2 : 1)) void pass2_kernel(Sc
     const int64_t t0 = e0 + (int64_t)t * kTile;
     load_kv_tile<NC, FULLD>(kg, vg, t0 + r, t0 + r < e1, t0 + kTile > e1, hh, d, kk, vv);
   };
-  auto tile = [&](int t, bf16x8 (&kB)[NC], bf16x8 (&vB)[NC], bf16x8 (&kn)[NC], bf16x8 (&vn)[NC]) {
+  // Each wave walks its tiles in order; the next tile's K and V are loaded into
+  // the same registers as soon as the matrix products have consumed them, so
+  // they fly during this tile's vector work.  Three workgroups per CU cover the
+  // rest of the latency.
+  bf16x8 kB[NC], vB[NC];
+  if (kP2Overlap && wid < next) issue(wid, kB, vB);
+  for (int t = wid; t < next; t += kWaves) {
     const int64_t j0 = e0 + (int64_t)t * kTile;
     const int64_t tok = j0 + r;
     const bool tok_ok = tok < e1;
-    if (t + kWaves < next) issue(t + kWaves, kn, vn);
-    f32x16 sacc, av;
+    if (!kP2Overlap) issue(t, kB, vB);
+    // four independent accumulation chains (logits split in two, a.v split
+    // into its hi and lo parts) keep the matrix core busy
+    f32x16 sacc, sacc1, av, av1;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; av[v] = 0.f; }
-#pragma unroll
-    for (int c = 0; c < NC; ++c) sacc = mfma32(lds8<DP>(qs, r, 2 * c + hh), kB[c], sacc);
+    for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; sacc1[v] = 0.f; av[v] = 0.f; av1[v] = 0.f; }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
+      if (c & 1) sacc1 = mfma32(lds8<DP>(qs, r, 2 * c + hh), kB[c], sacc1);
+      else sacc = mfma32(lds8<DP>(qs, r, 2 * c + hh), kB[c], sacc);
       av = mfma32(lds8<DP>(hs, r, 2 * c + hh), vB[c], av);
-      av = mfma32(lds8<DP>(ls, r, 2 * c + hh), vB[c], av);
+      av1 = mfma32(lds8<DP>(ls, r, 2 * c + hh), vB[c], av1);
     }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) { sacc[v] += sacc1[v]; av[v] += av1[v]; }
     float vn2 = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -680,6 +747,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? 2 : 1)) void pass2_kernel(Sc
       }
     }
     vn2 += __shfl_xor(vn2, 32);
+    if (kP2Overlap && t + kWaves < next) issue(t + kWaves, kB, vB);
     float cc[16];
     float ovf = 0.f;   // becomes NaN if an expansion term overflowed fp32
 #pragma unroll
@@ -735,13 +803,6 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? 2 : 1)) void pass2_kernel(Sc
     // fp32 overflow of a score or of its terms
     if (tok_ok && !(raw <= FLT_MAX)) flags |= LATCH_RANGE;
     if (hh == 0 && tok_ok) rawbuf[tok - e0] = raw;
-  };
-
-  bf16x8 kX[NC], vX[NC], kY[NC], vY[NC];
-  if (wid < next) issue(wid, kX, vX);
-  for (int t = wid; t < next; t += 2 * kWaves) {
-    tile(t, kX, vX, kY, vY);
-    if (t + kWaves < next) tile(t + kWaves, kY, vY, kX, vX);
   }
   __syncthreads();
   for (int64_t j = c0 + tid; j < c1; j += kThreads) {
@@ -764,6 +825,18 @@ int plan_splits(int64_t n, int Hkv, int64_t* split_len) {
   int64_t len = (n + want - 1) / want;
   len = (len + kTile - 1) / kTile * kTile;
   *split_len = len;
+  return (int)((n + len - 1) / len);
+}
+
+int plan_chunks2(int64_t n, int Hkv, int64_t* chunk_len) {
+  // about kTargetWG2 workgroups over the chip, whole tiles, at most kChunk2 tokens
+  int64_t want = (kTargetWG2 + Hkv - 1) / Hkv;
+  if (want < 1) want = 1;
+  int64_t len = (n + want - 1) / want;
+  len = (len + kTile - 1) / kTile * kTile;
+  if (len < 256) len = 256;
+  if (len > kChunk2) len = kChunk2;
+  *chunk_len = len;
   return (int)((n + len - 1) / len);
 }
 
@@ -825,9 +898,8 @@ static hipError_t launch_score_dp(void* ctx, const ScoreArgs& a, hipStream_t s) 
   prof_begin(ctx, "merge", s);
   hipLaunchKernelGGL(merge_kernel<DP>, dim3(a.Hkv * kRows), dim3(kThreads), 0, s, a);
   prof_end(ctx, "merge", s);
-  const int nchunks = (int)((a.n + kChunk2 - 1) / kChunk2);
   prof_begin(ctx, "pass2", s);
-  hipLaunchKernelGGL((pass2_kernel<DP, FULLD>), dim3((unsigned)a.Hkv * nchunks), dim3(kThreads), lds2,
+  hipLaunchKernelGGL((pass2_kernel<DP, FULLD>), dim3((unsigned)a.Hkv * a.chunks2), dim3(kThreads), lds2,
                      s, a);
   prof_end(ctx, "pass2", s);
   return hipGetLastError();
