@@ -242,6 +242,11 @@ int dropkv_sync(dropkv_ctx* c, void* stream) {
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return to_status(e);
   }
+  if (bits & LATCH_TIMEOUT) {
+    // a selection gave up inside its barriers: its scratch counters are stale
+    c->sel_hkv = 0;
+    return DROPKV_EDEVICE;
+  }
   if (bits & LATCH_NONFINITE) return DROPKV_ENONFINITE;
   if (bits & LATCH_SINGULAR) return DROPKV_ESINGULAR;
   if (bits & LATCH_RANGE) return DROPKV_ERANGE;

@@ -15,6 +15,7 @@ enum : uint32_t {
   LATCH_NONFINITE = 1u,
   LATCH_SINGULAR = 2u,
   LATCH_RANGE = 4u,
+  LATCH_TIMEOUT = 8u,   // a workgroup barrier of the single-launch selection gave up waiting
 };
 
 constexpr int kRows = 32;        // window-query rows per KV head handled by one MFMA tile (G*w <= 32)
@@ -92,6 +93,10 @@ struct ScoreArgs {
 struct SelScratch {
   uint32_t* hist1;         // [Hkv][4096]
   uint32_t* cand_cnt;      // [Hkv]
+  uint32_t* fh;            // [Hkv][4096 + 1024 + 1024] histograms of the single-launch path
+  uint32_t* bar;           // [Hkv] arrival counters of the single-launch path
+  uint32_t* done;          // [Hkv] finished-workgroup counters of the single-launch path
+  uint64_t* fcand;         // [Hkv][8192] (key, member) candidates of the single-launch path
   uint32_t* cand_key;      // [Hkv][8192]
   int32_t* cand_idx;       // [Hkv][8192]
   uint32_t* b1;            // [Hkv]

@@ -16,8 +16,17 @@
 
 namespace dropkv {
 
-// Selection runs as four wide kernels over blocks of kSelBlock consecutive
-// tokens of one head (all integer arithmetic, so the result is exact):
+// Selection is exact integer arithmetic on order-preserving keys.  When a
+// team of ceil(n / 32768) workgroups per head fits on the device at once, one
+// kernel does everything with each workgroup's keys held in registers: a 12-bit
+// histogram round over the team (device-scope adds, then a per-head barrier)
+// finds the bin holding the k-th smallest key; the team then exchanges that
+// bin's keys and each member's count of keys above it, after which every
+// member finds T, its own output offset and its evicted ties without further
+// waiting, and emits its survivors.  (If the bin holds more than 8192 keys, two
+// more histogram rounds and an exchange of per-member counts replace the
+// candidate exchange.)  Otherwise selection runs as four wide kernels over
+// blocks of kSelBlock tokens:
 //   s1  12-bit histogram of the keys' top bits (per-block LDS, then global adds)
 //   s2  find the bin b1 holding the k-th smallest key; count keys above b1 per
 //       block and collect the keys of bin b1 (with their indices) as candidates
@@ -41,34 +50,36 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inclusive scan over the 64 lanes of a wave with DPP moves: row shifts scan
+// each row of 16 lanes, then two row broadcasts carry rows into the next ones.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
 // Exclusive block scan of one uint per thread (NW waves); returns the total too.
+// `sh` holds at least NW words; the block may reuse it once this returns.
 template <int NW>
 __device__ __forceinline__ uint32_t block_exscan(uint32_t x, uint32_t* total, uint32_t* sh) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  uint32_t incl = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  const uint32_t incl = wave_incl_scan(x);
   if (lane == 63) sh[wid] = incl;
   __syncthreads();
-  if (wid == 0) {
-    const uint32_t t = (lane < NW) ? sh[lane] : 0u;
-    uint32_t ti = t;
+  uint32_t before = 0u, tot = 0u;
 #pragma unroll
-    for (int o = 1; o < NW; o <<= 1) {
-      const uint32_t y = __shfl_up(ti, o);
-      if (lane >= o) ti += y;
-    }
-    if (lane < NW) sh[NW + lane] = ti - t;
-    if (lane == NW - 1) sh[2 * NW] = ti;
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t t = sh[w];
+    tot += t;
+    before += w < wid ? t : 0u;
   }
+  *total = tot;
   __syncthreads();
-  const uint32_t res = sh[NW + wid] + incl - x;
-  *total = sh[2 * NW];
-  __syncthreads();
-  return res;
+  return before + incl - x;
 }
 
 struct SelArgs {
@@ -326,6 +337,358 @@ __global__ __launch_bounds__(kSelThreads) void select_s4(SelArgs a) {
   if (b == 0 && tid == 0) a.sc.cand_cnt[g] = 0u;
 }
 
+// ------------------------------------------------ single-launch selection --
+// A team of ceil(n / kFusedBlock) workgroups per head, kFusedThreads threads
+// each holding kFusedPer consecutive keys in registers.  Few, large workgroups
+// keep the device-scope histogram adds and reads shallow (at most a team's
+// worth of adds land on one bin).
+// Cooperative launch (guaranteed co-residency) costs more per call than an
+// ordinary one; the ordinary launch relies on the team fitting an idle device
+// and on the barriers' bounded wait otherwise.
+#ifndef DROPKV_SEL_COOP
+#define DROPKV_SEL_COOP 0
+#endif
+
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedPer = 32;
+constexpr int kFusedBlock = kFusedThreads * kFusedPer;   // 32768 tokens per workgroup
+constexpr int kFusedBins = kBins1 + 2 * 1024;            // per-head histograms of the three rounds
+constexpr int kFusedCand = 8192;                         // threshold-bin keys a team exchanges
+constexpr uint32_t kSpinLimit = 1u << 20;                // about a second of polling before giving up
+
+__device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Arrive at the head's barrier and wait for `target` arrivals in total (the
+// counter only grows during one call).  Values exchanged through device-scope
+// atomics need no cache maintenance: the writer waits for their completion
+// before it arrives.  With PLAIN, the workgroup also published ordinary stores:
+// every wave waits until its stores reach L2, then one release fence writes L2
+// back before the arrival, and one acquire fence follows the wait.
+// Returns false, for every thread of the workgroup, if the wait gave up.
+template <bool PLAIN = false>
+__device__ bool team_barrier(uint32_t* bar, uint32_t target, int* s_ok) {
+  if (PLAIN) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (PLAIN) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const uint32_t o = __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::"v"(o) : "memory");
+    uint32_t spins = 0u;
+    int ok = 1;
+    while (load_agent(bar) < target) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > kSpinLimit) { ok = 0; break; }
+    }
+    if (PLAIN) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *s_ok = ok;
+  }
+  __syncthreads();
+  return *s_ok != 0;
+}
+
+// Like find_bin, over a histogram the team built with device-scope adds.
+template <int NW, int NB>
+__device__ void find_bin_agent(const uint32_t* hist, uint32_t krem, uint32_t* s_bin,
+                               uint32_t* s_below, uint32_t* s_count, uint32_t* sh) {
+  constexpr int PER = NB / (NW * 64);
+  const int t = threadIdx.x;
+  uint32_t hv[PER];
+  uint32_t loc = 0u;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    hv[i] = load_agent(hist + t * PER + i);
+    loc += hv[i];
+  }
+  uint32_t tot;
+  const uint32_t excl = block_exscan<NW>(loc, &tot, sh);
+  if (excl < krem && excl + loc >= krem) {
+    uint32_t c = excl;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (c < krem && c + hv[i] >= krem) {
+        *s_bin = (uint32_t)(t * PER + i);
+        *s_below = c;
+        *s_count = hv[i];
+      }
+      c += hv[i];
+    }
+  }
+  __syncthreads();
+}
+
+// One radix round: add this workgroup's keys matching (prefix, mask) to the
+// head's histogram of digit (key >> shift) & (NB - 1), wait for the rest of the
+// team, then narrow the prefix to the bin holding the krem-th smallest key.
+// In the first round every key matches (mask = 0).
+template <int NB, bool FIRST>
+__device__ bool radix_round(const uint32_t (&key)[kFusedPer], int shift, uint32_t* h,
+                            uint32_t* gh, uint32_t* bar, uint32_t target, uint32_t& prefix,
+                            uint32_t& mask, uint32_t& krem, uint32_t* sh, uint32_t* s_bin,
+                            uint32_t* s_below, uint32_t* s_count, int* s_ok) {
+  constexpr int NW = kFusedThreads / 64;
+  constexpr int PER = NB / kFusedThreads;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) h[i * kFusedThreads + tid] = 0u;
+  __syncthreads();
+  if (FIRST) {
+    // consecutive tokens often share a bin (pooling makes plateaus): one add per run
+    uint32_t run = 0u;
+#pragma unroll
+    for (int i = 0; i < kFusedPer; ++i) {
+      const uint32_t bin = (key[i] >> shift) & (NB - 1);
+      ++run;
+      const bool last = i == kFusedPer - 1 || ((key[i + (i < kFusedPer - 1)] >> shift) & (NB - 1)) != bin;
+      if (last) atomicAdd(&h[bin], run);
+      run = last ? 0u : run;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kFusedPer; ++i)
+      if ((key[i] & mask) == prefix) atomicAdd(&h[(key[i] >> shift) & (NB - 1)], 1u);
+  }
+  __syncthreads();
+  // issue every device-scope add, then wait once for all of them
+  uint32_t hv[PER], old[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) hv[i] = h[i * kFusedThreads + tid];
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    old[i] = hv[i] ? __hip_atomic_fetch_add(&gh[i * kFusedThreads + tid], hv[i], __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT)
+                   : 0u;
+  uint32_t sink = 0u;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) sink |= old[i];
+  asm volatile("s_waitcnt vmcnt(0)" ::"v"(sink) : "memory");
+  if (!team_barrier(bar, target, s_ok)) return false;
+  find_bin_agent<NW, NB>(gh, krem, s_bin, s_below, s_count, sh);
+  prefix |= *s_bin << shift;
+  mask |= (uint32_t)(NB - 1) << shift;
+  krem -= *s_below;
+  __syncthreads();
+  return true;
+}
+
+__device__ __forceinline__ uint64_t load_agent64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Slots past the end of the head hold key 0, below every key a float maps to
+// (-inf maps to 0x007fffff): they rank first, the rank sought moves up by their
+// number, and they are never kept.
+__global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
+  constexpr int NW = kFusedThreads / 64;
+  __shared__ uint32_t h[kBins1];
+  __shared__ uint32_t ck[kFusedCand];            // candidate keys of the threshold bin
+  __shared__ uint16_t cw[kFusedCand];            // ... and the team member each came from
+  __shared__ uint32_t gtc[kFusedThreads];        // per team member: keys above T
+  __shared__ uint32_t tiec[kFusedThreads];       // per team member: keys equal to T
+  __shared__ uint32_t sh[NW];
+  __shared__ uint32_t s_bin, s_below, s_count, s_base;
+  __shared__ int s_ok;
+  if (latched(a.latch)) return;
+  const int g = blockIdx.x / a.nblk, b = blockIdx.x % a.nblk;
+  const int tid = threadIdx.x;
+  const uint32_t nblk = (uint32_t)a.nblk;
+  uint32_t* bar = a.sc.bar + g;
+  uint32_t* fh = a.sc.fh + (size_t)g * kFusedBins;
+  uint32_t* blk_gt = a.sc.blk_above + (size_t)g * nblk;
+  uint32_t* blk_tie = a.sc.blk_ties + (size_t)g * nblk;
+
+  // this thread's kFusedPer consecutive tokens, as order keys
+  const float* sg = a.scores + (size_t)g * a.n;
+  const int64_t base = (int64_t)b * kFusedBlock + (int64_t)tid * kFusedPer;
+  const int nv = (int)max((int64_t)0, min((int64_t)kFusedPer, a.n - base));
+  uint32_t key[kFusedPer];
+  if (nv == kFusedPer && (((size_t)g * a.n + base) & 3) == 0) {   // 16-byte aligned run
+#pragma unroll
+    for (int q = 0; q < kFusedPer / 4; ++q) {
+      const float4 x = *reinterpret_cast<const float4*>(sg + base + 4 * q);
+      key[4 * q + 0] = order_key(x.x);
+      key[4 * q + 1] = order_key(x.y);
+      key[4 * q + 2] = order_key(x.z);
+      key[4 * q + 3] = order_key(x.w);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kFusedPer; ++i) key[i] = i < nv ? order_key(sg[base + i]) : 0u;
+  }
+  const uint32_t pad = nblk * (uint32_t)kFusedBlock - (uint32_t)a.n;
+
+  // round 1: the 12-bit bin b1 holding the k-th smallest key, and its size
+  uint32_t prefix = 0u, mask = 0u, krem = (uint32_t)(a.n - a.budget) + pad;
+  if (!radix_round<kBins1, true>(key, 20, h, fh, bar, nblk, prefix, mask, krem, sh, &s_bin,
+                                 &s_below, &s_count, &s_ok)) {
+    if (tid == 0) atomicOr((uint32_t*)a.latch, LATCH_TIMEOUT);
+    return;
+  }
+  const uint32_t c1 = s_count;   // the same in every member: read from one histogram
+  const uint32_t b1 = prefix >> 20;
+  uint32_t T, need;
+  if (c1 <= (uint32_t)kFusedCand) {
+    // Exchange the bin's keys (tagged with the member) and each member's count
+    // of keys above the bin; then every member finishes alone.
+    uint32_t mine = 0u, gt1 = 0u;
+#pragma unroll
+    for (int i = 0; i < kFusedPer; ++i) {
+      const uint32_t bin = key[i] >> 20;
+      mine += bin == b1 ? 1u : 0u;
+      gt1 += bin > b1 ? 1u : 0u;
+    }
+    uint32_t tot;   // both counts are below 2^16 per member: scan them packed
+    const uint32_t off = block_exscan<NW>(mine | (gt1 << 16), &tot, sh) & 0xffffu;
+    if (tid == 0) {
+      const uint32_t o = __hip_atomic_exchange(blk_gt + b, tot >> 16, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t mt = tot & 0xffffu;
+      s_base = mt ? __hip_atomic_fetch_add(a.sc.cand_cnt + g, mt, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)
+                  : 0u;
+      asm volatile("s_waitcnt vmcnt(0)" ::"v"(o) : "memory");
+    }
+    __syncthreads();
+    uint64_t* cand = a.sc.fcand + (size_t)g * kFusedCand;
+    uint32_t pos = s_base + off;
+    // ordinary stores (one device-scope atomic per key would serialise at the
+    // memory side), published by the fences of the barrier
+#pragma unroll
+    for (int i = 0; i < kFusedPer; ++i)
+      if ((key[i] >> 20) == b1) {
+        if (pos < (uint32_t)kFusedCand) cand[pos] = (uint64_t)key[i] | ((uint64_t)b << 32);
+        ++pos;
+      }
+    if (!team_barrier<true>(bar, 2 * nblk, &s_ok)) {
+      if (tid == 0) atomicOr((uint32_t*)a.latch, LATCH_TIMEOUT);
+      return;
+    }
+    for (uint32_t i = tid; i < c1; i += kFusedThreads) {
+      const uint64_t v = load_agent64(cand + i);
+      ck[i] = (uint32_t)v;
+      cw[i] = (uint16_t)(v >> 32);
+    }
+    for (uint32_t i = tid; i < nblk; i += kFusedThreads) {
+      gtc[i] = load_agent(blk_gt + i);
+      tiec[i] = 0u;
+    }
+    __syncthreads();
+    // the exact k-th smallest key: two 10-bit digits below the bin, in LDS
+    for (int shift = 10; shift >= 0; shift -= 10) {
+      h[tid] = 0u;
+      __syncthreads();
+      for (uint32_t i = tid; i < c1; i += kFusedThreads) {
+        const uint32_t k = ck[i];
+        if ((k & mask) == prefix) atomicAdd(&h[(k >> shift) & 1023u], 1u);
+      }
+      __syncthreads();
+      find_bin<NW>(h, 1024, krem, &s_bin, &s_below, sh);
+      prefix |= s_bin << shift;
+      mask |= 1023u << shift;
+      krem -= s_below;
+      __syncthreads();
+    }
+    T = prefix;
+    need = krem;
+    for (uint32_t i = tid; i < c1; i += kFusedThreads) {
+      const uint32_t k = ck[i];
+      if (k > T) atomicAdd(&gtc[cw[i]], 1u);
+      else if (k == T) atomicAdd(&tiec[cw[i]], 1u);
+    }
+    __syncthreads();
+  } else {
+    // Too many keys share the bin: two more histogram rounds over the team,
+    // then an exchange of each member's counts above and equal to T.
+    bool ok = radix_round<1024, false>(key, 10, h, fh + kBins1, bar, 2 * nblk, prefix, mask, krem,
+                                       sh, &s_bin, &s_below, &s_count, &s_ok);
+    ok = ok && radix_round<1024, false>(key, 0, h, fh + kBins1 + 1024, bar, 3 * nblk, prefix,
+                                        mask, krem, sh, &s_bin, &s_below, &s_count, &s_ok);
+    if (!ok) {
+      if (tid == 0) atomicOr((uint32_t*)a.latch, LATCH_TIMEOUT);
+      return;
+    }
+    T = prefix;
+    need = krem;
+    uint32_t gt = 0u, nt = 0u;
+#pragma unroll
+    for (int i = 0; i < kFusedPer; ++i) {
+      gt += key[i] > T ? 1u : 0u;
+      nt += key[i] == T ? 1u : 0u;
+    }
+    uint32_t tot;
+    (void)block_exscan<NW>(gt | (nt << 16), &tot, sh);
+    if (tid == 0) {
+      const uint32_t o1 = __hip_atomic_exchange(blk_gt + b, tot & 0xffffu, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t o2 = __hip_atomic_exchange(blk_tie + b, tot >> 16, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+      asm volatile("s_waitcnt vmcnt(0)" ::"v"(o1), "v"(o2) : "memory");
+    }
+    if (!team_barrier(bar, 4 * nblk, &s_ok)) {
+      if (tid == 0) atomicOr((uint32_t*)a.latch, LATCH_TIMEOUT);
+      return;
+    }
+    for (uint32_t i = tid; i < nblk; i += kFusedThreads) {
+      gtc[i] = load_agent(blk_gt + i);
+      tiec[i] = load_agent(blk_tie + i);
+    }
+    __syncthreads();
+  }
+  // T is the k-th smallest key; `need` (>= 1) of the keys equal to T are evicted.
+  // Evicted ties are the oldest, so the members before b evict min(need, their
+  // ties) of them and b evicts what remains of `need`, up to its own ties.
+  uint32_t gt_before = 0u, ties_before = 0u;
+  for (int bb = 0; bb < b; ++bb) {
+    gt_before += gtc[bb];
+    ties_before += tiec[bb];
+  }
+  const uint32_t ev_before = min(need, ties_before);
+  const uint32_t ev = min(tiec[b], need - ev_before);
+  const uint32_t keep_before = gt_before + ties_before - ev_before;
+
+  // The whole team is past its last barrier, so nobody reads the histograms or
+  // the candidate count again: clear this member's share of the histograms;
+  // the last member to get here resets the counters.
+  for (int i = b * kFusedThreads + tid; i < kFusedBins; i += (int)nblk * kFusedThreads) fh[i] = 0u;
+  if (tid == 0) {
+    if (atomicAdd(a.sc.done + g, 1u) == nblk - 1u) {
+      __hip_atomic_store(bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.sc.cand_cnt + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.sc.done + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+  // ordered emission (thread order is index order within the member): the
+  // threads before this one hold gt_pre keys above T and tie_pre ties, of which
+  // the first `ev` of the member are evicted
+  uint32_t gt = 0u, nt = 0u;
+#pragma unroll
+  for (int i = 0; i < kFusedPer; ++i) {
+    gt += key[i] > T ? 1u : 0u;
+    nt += key[i] == T ? 1u : 0u;
+  }
+  uint32_t tot;
+  const uint32_t pre = block_exscan<NW>(gt | (nt << 16), &tot, sh);
+  const uint32_t gt_pre = pre & 0xffffu, tie_pre = pre >> 16;
+  uint32_t rank = tie_pre, keepbits = 0u;
+#pragma unroll
+  for (int i = 0; i < kFusedPer; ++i) {
+    const bool tie = key[i] == T;
+    const bool keepit = key[i] > T || (tie && rank >= ev);
+    rank += tie ? 1u : 0u;
+    keepbits |= keepit ? 1u << i : 0u;
+  }
+  uint32_t pos = keep_before + gt_pre + (tie_pre > ev ? tie_pre - ev : 0u);
+  int32_t* kg = a.keep + (size_t)g * a.budget;
+  while (keepbits) {   // one store per kept token, in index order
+    const int i = __builtin_ctz(keepbits);
+    keepbits &= keepbits - 1u;
+    if (pos < (uint32_t)a.budget) kg[pos] = (int32_t)(base + i);
+    ++pos;
+  }
+}
+
 __global__ __launch_bounds__(256) void select_all_kernel(int32_t* keep, int64_t n, int64_t total,
                                                          const uint32_t* latch) {
   if (latched(latch)) return;
@@ -335,7 +698,8 @@ __global__ __launch_bounds__(256) void select_all_kernel(int32_t* keep, int64_t 
 
 size_t select_scratch_bytes(int Hkv, int64_t n) {
   const int64_t nblk = (n + kSelBlock - 1) / kSelBlock;
-  const size_t per_head = (size_t)kBins1 * 4 + (size_t)kCandCap * 8 + 5 * 4 * 4 + (size_t)nblk * 5 * 4;
+  const size_t per_head = (size_t)kBins1 * 4 + (size_t)kFusedBins * 4 + (size_t)kCandCap * 8 +
+                          (size_t)kFusedCand * 8 + 8 * 4 + (size_t)nblk * 5 * 4;
   return (size_t)Hkv * per_head + 64 * 256;
 }
 
@@ -347,6 +711,10 @@ void carve_select(void* base, int Hkv, int64_t n, SelScratch* sc) {
   auto take = [&](size_t bytes) { char* x = c; c += al256(bytes); return x; };
   sc->hist1 = (uint32_t*)take((size_t)Hkv * kBins1 * 4);
   sc->cand_cnt = (uint32_t*)take((size_t)Hkv * 4);
+  sc->fh = (uint32_t*)take((size_t)Hkv * kFusedBins * 4);
+  sc->bar = (uint32_t*)take((size_t)Hkv * 4);
+  sc->done = (uint32_t*)take((size_t)Hkv * 4);
+  sc->fcand = (uint64_t*)take((size_t)Hkv * kFusedCand * 8);
   sc->cand_key = (uint32_t*)take((size_t)Hkv * kCandCap * 4);
   sc->cand_idx = (int32_t*)take((size_t)Hkv * kCandCap * 4);
   sc->b1 = (uint32_t*)take((size_t)Hkv * 4);
@@ -359,9 +727,11 @@ void carve_select(void* base, int Hkv, int64_t n, SelScratch* sc) {
   sc->blk_evt = (uint32_t*)take((size_t)Hkv * nblk * 4);
 }
 
-// Bytes of select scratch that must start zeroed (hist1 and cand_cnt lead the carve).
+// Bytes of select scratch that must start zeroed (hist1, cand_cnt, fh, bar and
+// done lead the carve).
 size_t select_zero_prefix_bytes(int Hkv) {
-  return al256((size_t)Hkv * kBins1 * 4) + al256((size_t)Hkv * 4);
+  return al256((size_t)Hkv * kBins1 * 4) + al256((size_t)Hkv * 4) +
+         al256((size_t)Hkv * kFusedBins * 4) + 2 * al256((size_t)Hkv * 4);
 }
 
 __global__ __launch_bounds__(256) void compact_kernel(const u16* __restrict__ k,
@@ -394,6 +764,28 @@ __global__ __launch_bounds__(256) void compact_kernel(const u16* __restrict__ k,
   if (bad) atomicOr(latch, LATCH_RANGE);
 }
 
+// Workgroups of select_fused that can be resident at once on the current device
+// (0 if the device cannot launch cooperatively).
+static int64_t fused_capacity() {
+  static int64_t cap[64];
+  static bool known[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!known[dev]) {
+    int coop = 0, cus = 0, per_cu = 0;
+    int64_t c = 0;
+    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess &&
+        coop &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, select_fused, kFusedThreads, 0) ==
+            hipSuccess)
+      c = (int64_t)cus * per_cu;
+    cap[dev] = c;
+    known[dev] = true;
+  }
+  return cap[dev];
+}
+
 hipError_t launch_select(void* ctx, const float* scores, int Hkv, int64_t n, int64_t budget,
                          int32_t* keep, uint32_t* latch, const SelScratch& sc, hipStream_t s) {
   if (budget == n) {
@@ -411,8 +803,25 @@ hipError_t launch_select(void* ctx, const float* scores, int Hkv, int64_t n, int
   a.nblk = (int)((n + kSelBlock - 1) / kSelBlock);
   a.latch = latch;
   a.sc = sc;
-  const unsigned grid = (unsigned)((int64_t)Hkv * a.nblk);
   prof_begin(ctx, "select", s);
+  const int64_t team = (n + kFusedBlock - 1) / kFusedBlock;
+  if (team <= kFusedThreads && (int64_t)Hkv * team <= fused_capacity()) {
+    SelArgs f = a;
+    f.nblk = (int)team;
+    void* args[] = {&f};
+    const dim3 fgrid((unsigned)((int64_t)Hkv * team)), fblock(kFusedThreads);
+    const hipError_t e =
+        DROPKV_SEL_COOP
+            ? hipLaunchCooperativeKernel(reinterpret_cast<const void*>(select_fused), fgrid, fblock,
+                                         args, 0, s)
+            : hipLaunchKernel(reinterpret_cast<const void*>(select_fused), fgrid, fblock, args, 0, s);
+    if (e == hipSuccess) {
+      prof_end(ctx, "select", s);
+      return hipSuccess;
+    }
+    (void)hipGetLastError();   // did not fit after all: take the multi-launch path
+  }
+  const unsigned grid = (unsigned)((int64_t)Hkv * a.nblk);
   hipLaunchKernelGGL(select_s1, dim3(grid), dim3(kSelThreads), 0, s, a);
   hipLaunchKernelGGL(select_s2, dim3(grid), dim3(kSelThreads), 0, s, a);
   hipLaunchKernelGGL(select_s3, dim3(Hkv), dim3(kS3Threads), 0, s, a);

@@ -240,12 +240,17 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str):
     f_scale = COPY_BYTES / (copy_fetch * 1024.0) if copy_fetch else None
     w_scale = COPY_BYTES / (copy_write * 1024.0) if copy_write else None
     kernels = {}
-    for short, key in (("pass1", "pass1_kernel"), ("merge", "merge_kernel"),
-                       ("pass2", "pass2_kernel"),
-                       ("select", "select_kernel"), ("compact", "compact_kernel")):
-        fk, wk = pick(fetch, key), pick(write, key)
-        if fk is None or wk is None or f_scale is None or w_scale is None:
+    families = (("pass1", ("pass1_kernel",)), ("merge", ("merge_kernel",)),
+                ("pass2", ("pass2_kernel",)),
+                ("select", ("select_s1", "select_s2", "select_s3", "select_s4")),
+                ("compact", ("compact_kernel",)))
+    for short, keys in families:
+        # a family of several kernels launched once each per call: sum per-launch means
+        fks = [pick(fetch, k) for k in keys]
+        wks = [pick(write, k) for k in keys]
+        if None in fks or None in wks or f_scale is None or w_scale is None:
             continue
+        fk, wk = sum(fks), sum(wks)
         kernels[short] = {"fetch_kib": fk, "write_kib": wk,
                           "bytes_per_launch": fk * 1024.0 * f_scale + wk * 1024.0 * w_scale}
     out = {"workload": workload, "kernel_source_hash": kernel_source_hash(),

@@ -96,6 +96,9 @@ int dropkv_score(dropkv_ctx *ctx, const uint16_t *q_win, const uint16_t *k_cache
  *   budget < 0 or budget > n.  (dropkv_score's protected window survives any
  *   budget >= w.)
  * If the context has a latched device error, nothing is written.
+ * When Hkv * ceil(n / 32768) workgroups of 1024 threads fit on the device at
+ * once, this is one launch whose workgroups wait for each other (bounded: see
+ * dropkv_sync); otherwise four launches.  Both give the same result.
  */
 int dropkv_select(dropkv_ctx *ctx, const float *scores, int32_t Hkv, int64_t n, int64_t budget,
                   int32_t *keep, void *stream);
@@ -112,7 +115,10 @@ int dropkv_compact(dropkv_ctx *ctx, const uint16_t *k, const uint16_t *v, int32_
                    uint16_t *v_out, void *stream);
 
 /* Wait for `stream`, then return and clear the latched device condition
- * (ENONFINITE before ESINGULAR before ERANGE), or DROPKV_OK. */
+ * (EDEVICE before ENONFINITE before ESINGULAR before ERANGE), or DROPKV_OK.
+ * EDEVICE here means a selection's workgroups stopped waiting for each other
+ * (about a second without progress, e.g. a device shared with other work); its
+ * keep list is unspecified and the next dropkv_select resets its scratch. */
 int dropkv_sync(dropkv_ctx *ctx, void *stream);
 
 /* Static string naming a status code. */

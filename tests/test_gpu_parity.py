@@ -145,6 +145,23 @@ def test_select_heavy_ties_and_signs(ctx, kind):
                                       err_msg=f"{kind} budget={budget}")
 
 
+def test_select_multi_launch_path(ctx):
+    """More blocks of 4096 tokens than the device holds at once (4096 > 256 CUs x
+    at most 10): selection runs as four launches instead of one, same result."""
+    Hkv, n = 2048, 8192
+    rng = np.random.default_rng(21)
+    s = rng.integers(0, 300, size=(Hkv, n)).astype(np.float32)
+    s[:, : n // 2] += rng.random((Hkv, n // 2)).astype(np.float32)
+    s[:, -8:] = np.inf
+    sd = torch.from_numpy(s).cuda()
+    for budget in (8, 1000, n - 1):
+        keep = torch.full((Hkv, budget), -9, dtype=torch.int32, device="cuda")
+        ctx.select(sd, Hkv, n, budget, keep)
+        assert ctx.sync() == dropkv.OK
+        np.testing.assert_array_equal(keep.cpu().numpy(), orc.select(s.astype(np.float64), budget),
+                                      err_msg=f"budget={budget}")
+
+
 def test_singular_rejected_and_select_withheld(ctx):
     n, d = 40, 8
     q = np.zeros((1, 1, d), np.float32); q[0, 0, 0] = 1.0
