@@ -10,6 +10,63 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// ------------------------------------------------ wave-level DPP helpers --
+// Inclusive scan / reduction over the 64 lanes of a wave with DPP moves: row
+// shifts combine within each row of 16 lanes, then two row broadcasts carry
+// row totals forward (lane 15 into row 1 and row 3, lane 31 into rows 2 and 3).
+// Lanes whose source is out of range take `ident`, the operation's identity.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_incl_u32(uint32_t x, uint32_t ident, Op op) {
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)x, 0x111, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)x, 0x112, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)x, 0x114, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)x, 0x118, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)x, 0x142, 0xa, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)x, 0x143, 0xc, 0xf, false));
+  return x;
+}
+
+// Inclusive prefix sum of a uint over the wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  return wave_incl_u32(x, 0u, [](uint32_t p, uint32_t q) { return p + q; });
+}
+
+// Sum of a float over the wave, in every lane (fixed combination order).
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  const uint32_t r = wave_incl_u32(__float_as_uint(x), 0u, [](uint32_t p, uint32_t q) {
+    return __float_as_uint(__uint_as_float(p) + __uint_as_float(q));
+  });
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)r, 63));
+}
+
+// Bitwise OR of a uint over the wave, in every lane.
+__device__ __forceinline__ uint32_t wave_or_dpp(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane(
+      (int)wave_incl_u32(x, 0u, [](uint32_t p, uint32_t q) { return p | q; }), 63);
+}
+
+template <int CTRL, int RMASK>
+__device__ __forceinline__ uint64_t max_u64_dpp_step(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, RMASK, 0xf, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, RMASK, 0xf, false);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return v > o ? v : o;
+}
+
+// Maximum of a uint64 over the wave, in every lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+  x = max_u64_dpp_step<0x111, 0xf>(x);
+  x = max_u64_dpp_step<0x112, 0xf>(x);
+  x = max_u64_dpp_step<0x114, 0xf>(x);
+  x = max_u64_dpp_step<0x118, 0xf>(x);
+  x = max_u64_dpp_step<0x142, 0xa>(x);
+  x = max_u64_dpp_step<0x143, 0xc>(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // Device error latch bits (OR-ed by kernels, decoded by dropkv_sync).
 enum : uint32_t {
   LATCH_NONFINITE = 1u,

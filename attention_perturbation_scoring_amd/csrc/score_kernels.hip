@@ -458,9 +458,11 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP1Waves : 1)) void pass1_ke
 }
 
 // ----------------------------------------------------------------- merge --
-// One workgroup per (KV head, row).  Split statistics are combined with a
-// fixed-order reduction (bitwise reproducible); a is summed by column with the
-// splits partitioned over NG thread groups.  Rows whose arg-max holds
+// One workgroup per (KV head, row).  Every split's statistics and the first
+// partial sums of a are fetched in one round trip; the maximum and its split
+// come from one packed reduction; every reduction has a fixed order (bitwise
+// reproducible); a is summed by float4 column group with the splits
+// partitioned over SG thread groups.  Rows whose arg-max holds
 // probability above ~0.94 then get their arg-max term from the exact
 // exclusion sum, computed by the same workgroup.
 constexpr int kMaxSplits = 1024;
@@ -553,15 +555,33 @@ __device__ float exclusion_term(const ScoreArgs& a, int g, int r, int jst, float
   return pstar * pstar * dist;
 }
 
+// Order-preserving uint32 image of a float for max-reductions; NaN and -0 map
+// like -inf and +0 (fmaxf ignores NaN).
+__device__ __forceinline__ uint32_t max_key(float f) {
+  if (!(f == f)) f = -INFINITY;
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_max_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 template <int DP>
 __global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
-  constexpr int NG = kThreads / DP;   // thread groups over the splits when summing a
-  __shared__ float sm_f[kMaxSplits];
+  constexpr int CG = DP / 4;              // float4 column groups of a row of a
+  constexpr int SG = kThreads / CG;       // split groups summing a
+  constexpr int PF = 8;                   // a loads per thread issued before the weights exist
+  __shared__ float sm_m2[kMaxSplits], sm_S[kMaxSplits], sm_Sx[kMaxSplits], sm_f[kMaxSplits];
+  __shared__ int sm_j[kMaxSplits];
+  __shared__ float4 red4[SG * CG];
+  __shared__ uint64_t rk[kWaves];
+  __shared__ float rf[3][kWaves];
+  __shared__ uint32_t ro_[2][kWaves];
   __shared__ float red[16 * (DP + 1)];
   __shared__ float rsx[16];
   __shared__ float tmp[kWaves];
-  __shared__ int tmpi[kWaves];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g = blockIdx.x / kRows, r = blockIdx.x % kRows;
   const size_t ro = (size_t)g * kRows + r;
   if (r >= a.M) {  // padded rows: zero operands so pass 2's MFMA rows stay inert
@@ -577,67 +597,114 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
   }
   const int S = a.splits;
   const size_t base = (size_t)g * S * kRows;
-  float M = -INFINITY;
-  for (int s = tid; s < S; s += kThreads) M = fmaxf(M, a.part.m2[base + (size_t)s * kRows + r]);
-  M = block_max256(M, tmp);
-  int sstar = INT_MAX;
-  for (int s = tid; s < S; s += kThreads)
-    if (M > -INFINITY && a.part.m2[base + (size_t)s * kRows + r] == M) sstar = min(sstar, s);
-  sstar = block_min256(sstar, tmpi);
-  float Sf = 0.f, Sxo = 0.f;
-  int bad = 0;
+
+  // Issue the first PF partial-a loads of this thread (they need no weights yet)
+  // together with every split's statistics: one memory round trip.
+  const int cg = tid % CG, sg = tid / CG;
+  const bool sum_lane = sg < SG;
+  const float* pa = a.part.a + (base + r) * DP + cg * 4;
+  float4 av[PF];
+#pragma unroll
+  for (int k = 0; k < PF; ++k) {
+    const int s = sg + SG * k;
+    av[k] = (sum_lane && s < S) ? *reinterpret_cast<const float4*>(pa + (size_t)s * kRows * DP)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  uint64_t best = 0u;   // (max key of m2, ~split): the largest m2, lowest split on ties
+  uint32_t badl = 0u;
   for (int s = tid; s < S; s += kThreads) {
     const size_t o = base + (size_t)s * kRows + r;
     const float ms = a.part.m2[o];
+    sm_m2[s] = ms;
+    sm_S[s] = a.part.S[o];
+    sm_Sx[s] = a.part.Sx[o];
+    sm_j[s] = a.part.jstar[o];
+    badl |= a.part.bad[o] ? 1u : 0u;
+    const uint64_t k = ((uint64_t)max_key(ms) << 32) | (uint32_t)~(uint32_t)s;
+    best = best > k ? best : k;
+  }
+  best = wave_max_u64(best);
+  if (lane == 0) rk[wid] = best;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) best = best > rk[w] ? best : rk[w];
+  const float M = from_max_key((uint32_t)(best >> 32));
+  const bool have = M > -INFINITY;
+  const int sstar = have ? (int)~(uint32_t)best : -1;
+  int jst = have ? sm_j[sstar] : -1;
+  uint32_t bad = 0u;
+  if (jst < 0 || jst >= a.n) { jst = -1; bad = 1u; }
+  // the arg-max token's value row, needed at the end
+  const float vstar = (tid < a.d && jst >= 0) ? bf2f(a.v[((size_t)g * a.n + jst) * a.d + tid]) : 0.f;
+
+  // split weights f_s = 2^(m2_s - M) and the normaliser with and without the
+  // arg-max split (fixed-order sums)
+  float Sf = 0.f, Sxo = 0.f;
+  for (int s = tid; s < S; s += kThreads) {
+    const float ms = sm_m2[s];
     const float f = (ms > -INFINITY) ? ex2(ms - M) : 0.f;
     sm_f[s] = f;
-    Sf += a.part.S[o] * f;
-    if (s != sstar) Sxo += a.part.S[o] * f;
-    bad |= a.part.bad[o];
+    Sf += sm_S[s] * f;
+    if (s != sstar) Sxo += sm_S[s] * f;
   }
-  Sf = block_sum256(Sf, tmp);
-  Sxo = block_sum256(Sxo, tmp);
-  bad = (int)block_max256(bad ? 1.f : 0.f, tmp);
-  const bool have = (sstar != INT_MAX);
-  const float Sx = have ? a.part.Sx[base + (size_t)sstar * kRows + r] + Sxo : 0.f;
-  int jst = have ? a.part.jstar[base + (size_t)sstar * kRows + r] : -1;
-  if (jst < 0 || jst >= a.n) { jst = -1; bad = 1; }
-
-  // a = sum_s f_s a_s / S : column dd, splits s = grp, grp + NG, ...
-  const int dd = tid % DP, grp = tid / DP;
-  float t = 0.f;
-  if (grp < NG) {
-    const float* pa = a.part.a + (base + r) * DP + dd;
-#pragma unroll 16
-    for (int s = grp; s < S; s += NG) t += pa[(size_t)s * kRows * DP] * sm_f[s];
-  }
+  Sf = wave_sum_dpp(Sf);
+  Sxo = wave_sum_dpp(Sxo);
+  badl = wave_or_dpp(badl);
+  if (lane == 0) { rf[0][wid] = Sf; rf[1][wid] = Sxo; ro_[0][wid] = badl; }
   __syncthreads();
-  if (grp < NG) red[grp * (DP + 1) + dd] = t;
+  Sf = 0.f; Sxo = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) { Sf += rf[0][w]; Sxo += rf[1][w]; bad |= ro_[0][w]; }
+  const float Sx = have ? sm_Sx[sstar] + Sxo : 0.f;
+
+  // a = sum_s f_s a_s / S: each thread sums its column group over its splits
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (sum_lane) {
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+      const int s = sg + SG * k;
+      const float f = s < S ? sm_f[s] : 0.f;
+      acc.x += av[k].x * f; acc.y += av[k].y * f; acc.z += av[k].z * f; acc.w += av[k].w * f;
+    }
+    for (int s = sg + SG * PF; s < S; s += SG) {
+      const float4 x = *reinterpret_cast<const float4*>(pa + (size_t)s * kRows * DP);
+      const float f = sm_f[s];
+      acc.x += x.x * f; acc.y += x.y * f; acc.z += x.z * f; acc.w += x.w * f;
+    }
+    red4[sg * CG + cg] = acc;
+  }
   __syncthreads();
   const float invS = 1.f / Sf;
   float an2 = 0.f, dist = 0.f;
-  int nonfin = 0;
+  uint32_t nonfin = 0u;
   if (tid < DP) {
+    const float* rr = reinterpret_cast<const float*>(red4);
     float tt = 0.f;
 #pragma unroll
-    for (int k = 0; k < NG; ++k) tt += red[k * (DP + 1) + tid];
+    for (int k = 0; k < SG; ++k) tt += rr[k * DP + tid];
     // columns >= d hold products with padding rows of V: they are zero by definition
-    const float av = tid < a.d ? tt * invS : 0.f;
-    if (!(fabsf(av) <= FLT_MAX)) nonfin = 1;
-    an2 = av * av;
-    const __bf16 hi = (__bf16)av;
-    const __bf16 lo = (__bf16)(av - (float)hi);
+    const float avv = tid < a.d ? tt * invS : 0.f;
+    if (!(fabsf(avv) <= FLT_MAX)) nonfin = 1u;
+    an2 = avv * avv;
+    const __bf16 hi = (__bf16)avv;
+    const __bf16 lo = (__bf16)(avv - (float)hi);
     a.rs.a_hi[ro * DP + tid] = __builtin_bit_cast(u16, hi);
     a.rs.a_lo[ro * DP + tid] = __builtin_bit_cast(u16, lo);
     if (tid < a.d && jst >= 0) {
-      const float df = av - bf2f(a.v[((size_t)g * a.n + jst) * a.d + tid]);
+      const float df = avv - vstar;
       dist = df * df;
     }
   }
-  an2 = block_sum256(an2, tmp);
-  dist = block_sum256(dist, tmp);
-  nonfin = (int)block_max256(nonfin ? 1.f : 0.f, tmp);
-  nonfin |= bad | (!(Sf <= FLT_MAX) ? 1 : 0) | (!(M > -INFINITY) ? 1 : 0);
+  an2 = wave_sum_dpp(an2);
+  dist = wave_sum_dpp(dist);
+  nonfin = wave_or_dpp(nonfin);
+  if (lane == 0) { rf[2][wid] = an2; tmp[wid] = dist; ro_[1][wid] = nonfin; }
+  __syncthreads();
+  an2 = 0.f; dist = 0.f; nonfin = 0u;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) { an2 += rf[2][w]; dist += tmp[w]; nonfin |= ro_[1][w]; }
+  __syncthreads();   // tmp is reused by the exclusion sum
+  nonfin |= bad | (!(Sf <= FLT_MAX) ? 1u : 0u) | (!have ? 1u : 0u);
   const bool singular = !nonfin && !(Sx > 0x1p-53f);
   const bool fix = !nonfin && !singular && Sx < kFixupThreshold;
   float cstar = (nonfin || singular) ? 0.f : dist / (Sx * Sx);
