@@ -94,12 +94,21 @@ constexpr int kThreads = 64 * kWaves;
 #ifndef DROPKV_P2_OVERLAP
 #define DROPKV_P2_OVERLAP 0
 #endif
+#ifndef DROPKV_P1_WG_WAVES
+#define DROPKV_P1_WG_WAVES 4
+#endif
 constexpr int kP1Waves = DROPKV_P1_WAVES;
 constexpr int kP2Waves = DROPKV_P2_WAVES;
 constexpr bool kP1Overlap = DROPKV_P1_OVERLAP != 0;
 constexpr bool kP2Overlap = DROPKV_P2_OVERLAP != 0;
 constexpr int kChunk2 = 2048;                // most tokens per pass-2 workgroup (before the pooling halo)
-constexpr int kTargetWG1 = 256 * kP1Waves;   // pass-1 workgroups aimed for over all heads
+// Pass 1 runs kP1WgWaves waves per workgroup: with 4 * kP1Waves of them, one
+// workgroup fills a CU, so no second workgroup on the CU trails the first.
+// (Head dimensions above 128 need more than 256 VGPRs, one wave per SIMD:
+// their workgroups keep four waves.)
+constexpr int kP1WgWaves = DROPKV_P1_WG_WAVES;
+constexpr int p1_waves(int DP) { return DP <= 128 ? kP1WgWaves : 4; }
+constexpr int kTargetWG1 = 256 * 4 * kP1Waves / kP1WgWaves;   // pass-1 workgroups aimed for
 constexpr int kTargetWG2 = 256 * kP2Waves;   // pass-2 workgroups aimed for over all heads
 
 // S_excl below this (argmax probability above ~0.94) routes the arg-max term

@@ -103,10 +103,10 @@ __device__ __forceinline__ bf16x8 lds8(const unsigned char* base, int row, int c
 
 // Stage rows [0, 32) of a row-major bf16 matrix (rows >= nrows and columns >= d
 // are zero) into LDS with the swizzled layout.  Whole workgroup.
-template <int DP>
+template <int DP, int NT = kThreads>
 __device__ __forceinline__ void stage_rows(unsigned char* dst, const u16* src, int nrows, int ld, int d) {
   using L = RowLayout<DP>;
-  for (int i = threadIdx.x; i < kRows * L::CH; i += kThreads) {
+  for (int i = threadIdx.x; i < kRows * L::CH; i += NT) {
     const int row = i / L::CH, ch = i % L::CH;
     u32x4 x = {0u, 0u, 0u, 0u};
     if (row < nrows && ch * 8 < d) x = *reinterpret_cast<const u32x4*>(src + (size_t)row * ld + ch * 8);
@@ -142,7 +142,8 @@ __device__ __forceinline__ void load_kv_tile(const u16* kg, const u16* vg, int64
 
 template <int DP>
 constexpr size_t pass1_lds_bytes() {
-  return (size_t)kRows * RowLayout<DP>::ROWB * (1 + 2 * kWaves);
+  // Q rows, then one V slot per wave (two when the next tile is prefetched)
+  return (size_t)kRows * RowLayout<DP>::ROWB * (1 + (kP1Overlap ? 2 : 1) * p1_waves(DP));
 }
 
 // K tile into registers (operand layout as load_kv_tile).
@@ -213,13 +214,15 @@ __device__ __forceinline__ void dma_v_tile(const u16* vg, int64_t t0, int64_t en
 }
 
 template <int DP, bool FULLD>
-__global__ __launch_bounds__(kThreads, (DP <= 128 ? kP1Waves : 1)) void pass1_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void pass1_kernel(
+    ScoreArgs a) {
   using L = RowLayout<DP>;
   constexpr int NC = DP / 16;
   constexpr int DB = DP / 32;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  __shared__ float sm_m[kWaves][kRows], sm_S[kWaves][kRows], sm_Sx[kWaves][kRows];
-  __shared__ int sm_j[kWaves][kRows], sm_bad[kWaves][kRows];
+  constexpr int NWV = p1_waves(DP), NT = 64 * NWV;
+  __shared__ float sm_m[NWV][kRows], sm_S[NWV][kRows], sm_Sx[NWV][kRows];
+  __shared__ int sm_j[NWV][kRows], sm_bad[NWV][kRows];
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
@@ -234,10 +237,11 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP1Waves : 1)) void pass1_ke
   const int64_t causal = row_ok ? a.n - a.w + (r % a.w) : -1;
   const int64_t all_see = a.n - a.w;   // every window query sees keys 0..n-w
   unsigned char* qs = smem_raw;                                  // Q rows of the group
-  unsigned char* vslot0 = smem_raw + (size_t)kRows * L::ROWB * (1 + 2 * wid);   // this wave's V tiles
+  unsigned char* vslot0 =   // this wave's V tile(s)
+      smem_raw + (size_t)kRows * L::ROWB * (1 + (kP1Overlap ? 2 : 1) * wid);
   unsigned char* vslot1 = vslot0 + (size_t)kRows * L::ROWB;
 
-  stage_rows<DP>(qs, a.q + (size_t)g * a.M * d, a.M, d, d);
+  stage_rows<DP, NT>(qs, a.q + (size_t)g * a.M * d, a.M, d, d);
   __syncthreads();
 
   float m = -INFINITY, S = 0.f, Sx = 0.f, chk = 0.f;
@@ -261,7 +265,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP1Waves : 1)) void pass1_ke
     dma_v_tile<DP>(vg, f0, jend, d, vslot0, lane);
   }
   int slot = 0;
-  for (int t = wid; t < ntiles; t += kWaves) {
+  for (int t = wid; t < ntiles; t += NWV) {
     const int64_t j0 = jbeg + (int64_t)t * kTile;
     unsigned char* vs = slot ? vslot1 : vslot0;
     if (!kP1Overlap) {
@@ -279,9 +283,9 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP1Waves : 1)) void pass1_ke
     }
 #pragma unroll
     for (int v = 0; v < 16; ++v) st[v] += st1[v];
-    const bool more = t + kWaves < ntiles;
+    const bool more = t + NWV < ntiles;
     if (kP1Overlap && more) {
-      const int64_t n0 = j0 + (int64_t)kWaves * kTile;
+      const int64_t n0 = j0 + (int64_t)NWV * kTile;
       load_k_tile<NC, FULLD>(kg, n0 + r, n0 + r < jend, n0 + kTile > jend, hh, d, kk);
       dma_v_tile<DP>(vg, n0, jend, d, slot ? vslot0 : vslot1, lane);
     }
@@ -400,7 +404,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP1Waves : 1)) void pass1_ke
   }
   if (!(chk == 0.f)) bad = 1;
 
-  // ---- combine the four waves' states for each row (fixed order) ----
+  // ---- combine the waves' states for each row (fixed order) ----
   bad |= __shfl_xor(bad, 32);
   if (hh == 0) {
     sm_m[wid][r] = m;
@@ -412,10 +416,10 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP1Waves : 1)) void pass1_ke
   __syncthreads();
   float Mf = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) Mf = fmaxf(Mf, sm_m[w][r]);
+  for (int w = 0; w < NWV; ++w) Mf = fmaxf(Mf, sm_m[w][r]);
   int wstar = -1, jbest = INT_MAX, badf = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < NWV; ++w) {
     if (Mf > -INFINITY && sm_m[w][r] == Mf && sm_j[w][r] < jbest) {
       jbest = sm_j[w][r];
       wstar = w;
@@ -424,7 +428,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP1Waves : 1)) void pass1_ke
   }
   float Sf = 0.f, Sxf = 0.f;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < NWV; ++w) {
     const float f = (sm_m[w][r] > -INFINITY) ? ex2(sm_m[w][r] - Mf) : 0.f;
     Sf += sm_S[w][r] * f;
     Sxf += (w == wstar) ? sm_Sx[w][r] * f : sm_S[w][r] * f;
@@ -432,7 +436,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP1Waves : 1)) void pass1_ke
   const float myf = (m > -INFINITY) ? ex2(m - Mf) : 0.f;
   __syncthreads();  // every wave is done with its V tile; reuse LDS as a float buffer
   float* red = reinterpret_cast<float*>(smem_raw);
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < NWV; ++w) {
     if (wid == w) {
 #pragma unroll
       for (int b = 0; b < DB; ++b)
@@ -454,7 +458,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP1Waves : 1)) void pass1_ke
     a.part.jstar[pb + r] = jbest;
     a.part.bad[pb + r] = badf;
   }
-  for (int i = tid; i < a.M * DP; i += kThreads) a.part.a[pb * DP + i] = red[i];
+  for (int i = tid; i < a.M * DP; i += NT) a.part.a[pb * DP + i] = red[i];
 }
 
 // ----------------------------------------------------------------- merge --
@@ -958,7 +962,7 @@ static hipError_t launch_score_dp(void* ctx, const ScoreArgs& a, hipStream_t s) 
     attr_done = true;
   }
   prof_begin(ctx, "pass1", s);
-  hipLaunchKernelGGL((pass1_kernel<DP, FULLD>), dim3(a.Hkv * a.splits), dim3(kThreads), lds1, s, a);
+  hipLaunchKernelGGL((pass1_kernel<DP, FULLD>), dim3(a.Hkv * a.splits), dim3(64 * p1_waves(DP)), lds1, s, a);
   prof_end(ctx, "pass1", s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -106,7 +106,12 @@ def run(args):
     def dev(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda")
 
-    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    # Consecutive steps score different copies of the layer (different
+    # addresses), as a multi-layer run scores a different layer each time: a
+    # step never finds the previous step's reads still in the last-level cache.
+    q0, k0, v0 = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    copies = [(q0, k0, v0)] + [(q0.clone(), k0.clone(), v0.clone())
+                               for _ in range(args.rotate - 1)]
     Hq, Hkv, d, n, w, pool, budget = cfg.Hq, cfg.Hkv, cfg.d, cfg.n, cfg.w, cfg.pool, cfg.budget
     scores = torch.empty((Hkv, n), dtype=torch.float32, device="cuda")
     keep = torch.empty((Hkv, budget), dtype=torch.int32, device="cuda")
@@ -115,7 +120,11 @@ def run(args):
     stream = torch.cuda.current_stream()
     ctx = dropkv.Context(0)
 
+    counter = [0]
+
     def step():
+        q, k, v = copies[counter[0] % len(copies)]
+        counter[0] += 1
         ctx.score(q, k, v, n, w, Hq, Hkv, d, pool, scores, stream)
         ctx.select(scores, Hkv, n, budget, keep, stream)
         ctx.compact(k, v, Hkv, n, d, keep, budget, k_out, v_out, stream)
@@ -189,7 +198,8 @@ def run(args):
         "data": "synthetic",
         "config": {"workload": cfg.name, "Hq": Hq, "Hkv": Hkv, "d": d, "n": n, "w": w,
                    "pool": pool, "budget": budget, "batch": 1, "layers": 1,
-                   "input_dtype": "bf16", "step": "score+select+compact"},
+                   "input_dtype": "bf16", "step": "score+select+compact",
+                   "layer_copies": args.rotate},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "kernel_us": {k_: round(v_["avg_us"], 2) for k_, v_ in kern.items()},
@@ -290,6 +300,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate", type=int, default=2,
+                    help="copies of the layer that consecutive steps cycle through")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--summarize-kt", nargs=2, metavar=("STATS_CSV", "COMMAND"))
