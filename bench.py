@@ -250,10 +250,11 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str):
     f_scale = COPY_BYTES / (copy_fetch * 1024.0) if copy_fetch else None
     w_scale = COPY_BYTES / (copy_write * 1024.0) if copy_write else None
     kernels = {}
+    # selection is one kernel when the head teams fit on the device, else four
+    sel = ("select_fused",) if pick(fetch, "select_fused") is not None else (
+        "select_s1", "select_s2", "select_s3", "select_s4")
     families = (("pass1", ("pass1_kernel",)), ("merge", ("merge_kernel",)),
-                ("pass2", ("pass2_kernel",)),
-                ("select", ("select_s1", "select_s2", "select_s3", "select_s4")),
-                ("compact", ("compact_kernel",)))
+                ("pass2", ("pass2_kernel",)), ("select", sel), ("compact", ("compact_kernel",)))
     for short, keys in families:
         # a family of several kernels launched once each per call: sum per-launch means
         fks = [pick(fetch, k) for k in keys]
