@@ -19,6 +19,8 @@
  *     probability that rounds to 1 is rejected rather than epsilon-patched.
  *   - Section 2.2: eviction removes the tokens from the resident cache
  *     (compaction keeps the surviving rows).
+ *   - "paper tables", Table 14 (SnapKV row) and "paper digest", App. B: the
+ *     attention-only score the pages compare against (oracle_attention_*).
  *
  * Readings taken where the pages leave a step open (all listed in the design doc):
  *   - q-head h uses KV head g = h / G, G = Hq / Hkv (contiguous groups).
@@ -273,6 +275,76 @@ int oracle_compact(const uint16_t *in, int hkv, int64_t n, int d, const int32_t 
                    sizeof(uint16_t) * (size_t)d);
         }
     return ORC_OK;
+}
+
+/*
+ * Attention-only scores (the pages' negative control; "paper tables", Table 14,
+ * SnapKV row: MaxPool1d over the window-summed attention weights, kept large;
+ * "paper digest", App. B: the same observation window and pooling kernel as
+ * DropKV, the scores differing only by the value-residual factor).  Reading:
+ * heads of a group are averaged as for DropKV, and the same protection and
+ * eviction of the smallest follow.
+ *   raw[g][j] = (1/G) * sum_{h in group g} sum_t p_j^(h,t),  p = 0 for unseen keys.
+ * Only K is read.
+ */
+int oracle_attention_raw(const uint16_t *q, const uint16_t *k, int64_t n, int w, int hq, int hkv,
+                         int d, int nthreads, double *raw) {
+    int rc = check_shapes(n, w, hq, hkv, d);
+    if (rc) return rc;
+    const int G = hq / hkv;
+    for (int64_t i = 0; i < (int64_t)hq * w * d; ++i)
+        if (!bf16_is_finite(q[i])) return ORC_ENONFINITE;
+    for (int64_t i = 0; i < (int64_t)hkv * n * d; ++i)
+        if (!bf16_is_finite(k[i])) return ORC_ENONFINITE;
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+    int status = ORC_OK;
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int g = 0; g < hkv; ++g) {
+        double *l = malloc(sizeof(double) * (size_t)n);
+        double *rg = raw + (size_t)g * n;
+        if (!l) {
+#pragma omp critical
+            { status = ORC_ENOMEM; }
+            continue;
+        }
+        for (int64_t j = 0; j < n; ++j) rg[j] = 0.0;
+        for (int h = g * G; h < (g + 1) * G; ++h) {
+            for (int t = 0; t < w; ++t) {
+                const int64_t Pt = n - w + t; /* query t's last visible key */
+                const uint16_t *qr = q + ((size_t)h * w + t) * d;
+                double m = -INFINITY;
+                for (int64_t j = 0; j <= Pt; ++j) {
+                    double s = 0.0;
+                    for (int i = 0; i < d; ++i)
+                        s += bf16_to_double(qr[i]) * bf16_to_double(k[((size_t)g * n + j) * d + i]);
+                    l[j] = inv_sqrt_d * s;
+                    if (l[j] > m) m = l[j];
+                }
+                double S = 0.0;
+                for (int64_t j = 0; j <= Pt; ++j) {
+                    l[j] = exp(l[j] - m);
+                    S += l[j];
+                }
+                for (int64_t j = 0; j <= Pt; ++j) rg[j] += l[j] / S;
+            }
+        }
+        for (int64_t j = 0; j < n; ++j) rg[j] = rg[j] / (double)G;
+        free(l);
+    }
+    return status;
+}
+
+/* Attention-only scoring: raw attention sums, pooling, protection. */
+int oracle_attention_score(const uint16_t *q, const uint16_t *k, int64_t n, int w, int hq, int hkv,
+                           int d, int pool, int nthreads, double *scores) {
+    if (pool < 1 || pool % 2 == 0) return ORC_EINVAL;
+    double *raw = malloc(sizeof(double) * (size_t)hkv * n);
+    if (!raw) return ORC_ENOMEM;
+    int rc = oracle_attention_raw(q, k, n, w, hq, hkv, d, nthreads, raw);
+    if (rc == ORC_OK) rc = oracle_pool_protect(raw, n, hkv, w, pool, scores);
+    free(raw);
+    return rc;
 }
 
 /*

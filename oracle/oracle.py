@@ -54,6 +54,8 @@ def load(path: str):
     L.oracle_select.argtypes = [P, i32, i64, i64, P]
     L.oracle_compact.argtypes = [P, i32, i64, i32, P, i64, P]
     L.oracle_window_attention.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P]
+    L.oracle_attention_raw.argtypes = [P, P, i64, i32, i32, i32, i32, i32, P]
+    L.oracle_attention_score.argtypes = [P, P, i64, i32, i32, i32, i32, i32, i32, P]
     for f in (L.oracle_raw_scores, L.oracle_pool_protect, L.oracle_score, L.oracle_select,
               L.oracle_compact, L.oracle_window_attention):
         f.restype = ctypes.c_int
@@ -118,6 +120,26 @@ def score(q, k, v, pool, nthreads=None):
     out = np.zeros((Hkv, n), dtype=np.float64)
     _check(lib().oracle_score(_ptr(q), _ptr(k), _ptr(v), n, w, Hq, Hkv, d, pool,
                               nthreads or default_threads(), _ptr(out)))
+    return out
+
+
+def attention_raw(q, k, nthreads=None):
+    """Attention-only raw scores: head-averaged, window-summed p_j. float64 [Hkv][n]."""
+    q, k = _u16(q), _u16(k)
+    Hq, w, d, Hkv, n = _dims(q, k)
+    out = np.zeros((Hkv, n), dtype=np.float64)
+    _check(lib().oracle_attention_raw(_ptr(q), _ptr(k), n, w, Hq, Hkv, d,
+                                      nthreads or default_threads(), _ptr(out)))
+    return out
+
+
+def attention_score(q, k, pool, nthreads=None):
+    """Attention-only final scores (pooled, window = +inf): float64 [Hkv][n]."""
+    q, k = _u16(q), _u16(k)
+    Hq, w, d, Hkv, n = _dims(q, k)
+    out = np.zeros((Hkv, n), dtype=np.float64)
+    _check(lib().oracle_attention_score(_ptr(q), _ptr(k), n, w, Hq, Hkv, d, pool,
+                                        nthreads or default_threads(), _ptr(out)))
     return out
 
 

@@ -103,3 +103,28 @@ def sort_select(scores, budget):
         order = sorted(range(n), key=lambda j: (float(scores[g, j]), j))
         out[g] = np.sort(np.array(order[n - budget:], dtype=np.int32))
     return out
+
+
+def attention_raw(q, k):
+    """Attention-only raw scores by plain Python loops: softmax of q.k/sqrt(d) over
+    the keys each window query sees, summed over the window, averaged over the
+    heads of a group."""
+    import math
+    qf = bf16_to_f32(q).astype(np.float64)
+    kf = bf16_to_f32(k).astype(np.float64)
+    Hq, w, d = qf.shape
+    Hkv, n, _ = kf.shape
+    G = Hq // Hkv
+    out = [[0.0] * n for _ in range(Hkv)]
+    for h in range(Hq):
+        g = h // G
+        for t in range(w):
+            P = n - w + t
+            logits = [sum(qf[h, t, i] * kf[g, j, i] for i in range(d)) / math.sqrt(d)
+                      for j in range(P + 1)]
+            m = max(logits)
+            e = [math.exp(x - m) for x in logits]
+            tot = sum(e)
+            for j in range(P + 1):
+                out[g][j] += e[j] / tot / G
+    return np.array(out)

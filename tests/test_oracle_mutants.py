@@ -26,6 +26,11 @@ MUTANTS = {
     "pool_radius": ("const int64_t r = (pool - 1) / 2;", "const int64_t r = (pool + 1) / 2;"),
     "protect_one_short": ("y[j] = (j >= n - w) ? INFINITY : mx;", "y[j] = (j > n - w) ? INFINITY : mx;"),
     "ties_newest_first": ("return (a->j > b->j) - (a->j < b->j);", "return (a->j < b->j) - (a->j > b->j);"),
+    # attention-only scores
+    "attn_no_head_mean": ("rg[j] = rg[j] / (double)G;", "rg[j] = rg[j];"),
+    "attn_causal_off_by_one": ("const int64_t Pt = n - w + t;", "const int64_t Pt = n - w + t - 1;"),
+    "attn_no_sqrt_d": ("l[j] = inv_sqrt_d * s;", "l[j] = s;"),
+    "attn_unnormalised": ("rg[j] += l[j] / S;", "rg[j] += l[j];"),
 }
 
 
@@ -54,6 +59,9 @@ def _pins_pass(L):
             return False
         s = rng.integers(0, 4, size=(2, 30)).astype(np.float64)
         if not np.array_equal(orc.select(s, 11), brute.sort_select(s, 11)):
+            return False
+        qa = wl.bf16_bits(rng.standard_normal((4, 3, 8), dtype=np.float32) * 2)
+        if not np.allclose(orc.attention_raw(qa, k), brute.attention_raw(qa, k), rtol=1e-12, atol=0):
             return False
         return True
     except orc.OracleError:
