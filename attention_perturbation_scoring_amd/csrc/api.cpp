@@ -134,12 +134,15 @@ int dropkv_plan_splits(int64_t n, int32_t Hkv, int32_t* splits) {
   return DROPKV_OK;
 }
 
-int dropkv_score(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
-                 const uint16_t* v_cache, int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int32_t d,
-                 int32_t pool, float* scores, void* stream) {
+namespace {
+
+// Shared by both scoring entry points: checks, launch geometry, scratch.
+int score_common(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
+                 const uint16_t* v_cache, bool attention_only, int64_t n, int32_t w, int32_t Hq,
+                 int32_t Hkv, int32_t d, int32_t pool, float* scores, void* stream) {
   if (!c) return DROPKV_EINVAL;
-  if (!aligned16(q_win) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(scores))
-    return DROPKV_EINVAL;
+  if (!aligned16(q_win) || !aligned16(k_cache) || !aligned16(scores)) return DROPKV_EINVAL;
+  if (!attention_only && !aligned16(v_cache)) return DROPKV_EINVAL;
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return DROPKV_EINVAL;
   if (n < 1 || n >= (int64_t(1) << 31)) return DROPKV_EINVAL;
   if (w < 1 || w > n) return DROPKV_EINVAL;
@@ -155,7 +158,7 @@ int dropkv_score(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
   a.q = q_win; a.k = k_cache; a.v = v_cache; a.scores = scores;
   a.n = n; a.w = w; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.G = G; a.M = G * w; a.pool = pool;
   a.DP = (d + 31) / 32 * 32;
-  a.splits = plan_splits(n, Hkv, &a.split_len);
+  a.splits = plan_splits(n, Hkv, &a.split_len, attention_only ? kTargetWGAttn : kTargetWG1);
   a.chunks2 = plan_chunks2(n, Hkv, &a.chunk2_len);
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
   a.latch = c->latch;
@@ -173,7 +176,21 @@ int dropkv_score(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
     c->scratch_bytes = need;
   }
   carve_scratch(c->scratch, Hkv, a.splits, a.DP, &a.part, &a.rs);
-  return to_status(launch_score(c, a, s));
+  return to_status(attention_only ? launch_score_attention(c, a, s) : launch_score(c, a, s));
+}
+
+}  // namespace
+
+int dropkv_score(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
+                 const uint16_t* v_cache, int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int32_t d,
+                 int32_t pool, float* scores, void* stream) {
+  return score_common(c, q_win, k_cache, v_cache, false, n, w, Hq, Hkv, d, pool, scores, stream);
+}
+
+int dropkv_score_attention(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
+                           int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int32_t d, int32_t pool,
+                           float* scores, void* stream) {
+  return score_common(c, q_win, k_cache, nullptr, true, n, w, Hq, Hkv, d, pool, scores, stream);
 }
 
 int dropkv_select(dropkv_ctx* c, const float* scores, int32_t Hkv, int64_t n, int64_t budget,

@@ -193,7 +193,9 @@ hipError_t launch_compact(void* ctx, const u16* k, const u16* v, int Hkv, int64_
 // Bytes of scratch the scoring pass needs for these sizes.
 size_t score_scratch_bytes(int Hkv, int splits, int DP);
 void carve_scratch(void* base, int Hkv, int splits, int DP, Partials* p, RowState* rs);
-int plan_splits(int64_t n, int Hkv, int64_t* split_len);
+int plan_splits(int64_t n, int Hkv, int64_t* split_len, int target = kTargetWG1);
+hipError_t launch_score_attention(void* ctx, const ScoreArgs& a, hipStream_t s);
+constexpr int kTargetWGAttn = 1024;   // attention-only pass A: four small workgroups per CU
 int plan_chunks2(int64_t n, int Hkv, int64_t* chunk_len);
 
 }  // namespace dropkv

@@ -885,10 +885,246 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
   if (flags) atomicOr(a.latch, flags);
 }
 
+// -------------------------------------------------------- attention-only --
+// Attention-only scores, the pages' SnapKV comparison ("paper tables",
+// Table 14: MaxPool over the window-summed attention weights; "paper digest",
+// App. B: same observation window and pooling as DropKV).  Pass A is pass 1
+// without V: per (head, split) the running maximum and normaliser of every row.
+// Pass B turns the split states into each row's log-sum-exp (fixed order),
+// recomputes the logits, adds p over the rows of each token, divides by G and
+// pools / protects like pass 2.  Only K is read, twice.
+template <int DP, bool FULLD>
+__global__ __launch_bounds__(kThreads, (DP <= 128 ? 4 : 2)) void attn_pass1_kernel(ScoreArgs a) {
+  constexpr int NC = DP / 16;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __shared__ float sm_m[kWaves][kRows], sm_S[kWaves][kRows];
+  __shared__ int sm_bad[kWaves][kRows];
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int r = lane & 31, hh = lane >> 5;
+  const int g = blockIdx.x / a.splits, s = blockIdx.x % a.splits;
+  const int64_t jbeg = (int64_t)s * a.split_len;
+  const int64_t jend = min(a.n, jbeg + a.split_len);
+  const int ntiles = (int)((jend - jbeg + kTile - 1) / kTile);
+  const int d = a.d;
+  const u16* kg = a.k + (size_t)g * a.n * d;
+  const bool row_ok = r < a.M;
+  const int64_t causal = row_ok ? a.n - a.w + (r % a.w) : -1;
+  const int64_t all_see = a.n - a.w;
+  unsigned char* qs = smem_raw;
+  stage_rows<DP>(qs, a.q + (size_t)g * a.M * d, a.M, d, d);
+  __syncthreads();
+
+  // S^T = K Q^T as in pass 1: lane l owns row l%32 and 16 of the tile's tokens
+  float m = -INFINITY, S = 0.f, chk = 0.f;
+  bf16x8 kk[NC];
+  for (int t = wid; t < ntiles; t += kWaves) {
+    const int64_t j0 = jbeg + (int64_t)t * kTile;
+    load_k_tile<NC, FULLD>(kg, j0 + r, j0 + r < jend, j0 + kTile > jend, hh, d, kk);
+    f32x16 st, st1;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) { st[v] = 0.f; st1[v] = 0.f; }
+#pragma unroll
+    for (int c = 0; c < NC; c += 2) {
+      st = mfma32(kk[c], lds8<DP>(qs, r, 2 * c + hh), st);
+      if (c + 1 < NC) st1 = mfma32(kk[c + 1], lds8<DP>(qs, r, 2 * c + 2 + hh), st1);
+    }
+    const bool interior = (j0 + kTile <= jend) && (j0 + kTile - 1 <= all_see);
+    float s2[16];
+    float lm = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float x = st[v] + st1[v];
+      const int64_t tv = j0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+      const bool valid = interior || (row_ok && tv < jend && tv <= causal);
+      if (valid) chk = fmaf(x, 0.f, chk);   // becomes NaN on any inf / NaN logit
+      s2[v] = valid ? x * a.scale_log2 : -INFINITY;
+      lm = fmaxf(lm, s2[v]);
+    }
+    lm = fmaxf(lm, __shfl_xor(lm, 32));
+    const float mn = fmaxf(m, lm);
+    if (mn > -INFINITY) {
+      const float alpha = ex2(m - mn);   // 0 while nothing was seen (S = 0 then)
+      float ts = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) ts += ex2(s2[v] - mn);
+      ts += __shfl_xor(ts, 32);
+      S = S * alpha + ts;
+      m = mn;
+    }
+  }
+  int bad = (chk == 0.f) ? 0 : 1;
+  bad |= __shfl_xor(bad, 32);
+  if (hh == 0) {
+    sm_m[wid][r] = m;
+    sm_S[wid][r] = S;
+    sm_bad[wid][r] = bad;
+  }
+  __syncthreads();
+  if (tid < kRows) {   // combine the waves' states of row tid (fixed order)
+    float Mf = -INFINITY;
+    int badf = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) { Mf = fmaxf(Mf, sm_m[w][tid]); badf |= sm_bad[w][tid]; }
+    float Sf = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      Sf += (sm_m[w][tid] > -INFINITY) ? sm_S[w][tid] * ex2(sm_m[w][tid] - Mf) : 0.f;
+    const size_t pb = ((size_t)g * a.splits + s) * kRows + tid;
+    a.part.m2[pb] = Mf;
+    a.part.S[pb] = Sf;
+    a.part.bad[pb] = badf;
+  }
+}
+
+template <int DP>
+constexpr size_t attn_pass2_lds_bytes() {
+  return (size_t)kRows * RowLayout<DP>::ROWB + (size_t)(kChunk2 + 2 * kMaxRadius + kTile) * 4;
+}
+
+template <int DP, bool FULLD>
+__global__ __launch_bounds__(kThreads, (DP <= 128 ? 4 : 2)) void attn_pass2_kernel(ScoreArgs a) {
+  constexpr int NC = DP / 16;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __shared__ float lse_s[kRows];
+  unsigned char* qs = smem_raw;
+  float* rawbuf = reinterpret_cast<float*>(qs + kRows * RowLayout<DP>::ROWB);
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int r = lane & 31, hh = lane >> 5;
+  const int64_t n = a.n;
+  const int g = blockIdx.x / a.chunks2, ch = blockIdx.x % a.chunks2;
+  const int64_t c0 = (int64_t)ch * a.chunk2_len, c1 = min(n, c0 + a.chunk2_len);
+  const int rad = (a.pool - 1) / 2;
+  const int64_t e0 = max((int64_t)0, c0 - rad), e1 = min(n, c1 + rad);
+  const int next = (int)((e1 - e0 + kTile - 1) / kTile);
+  const int d = a.d;
+  const u16* kg = a.k + (size_t)g * n * d;
+  const int64_t all_see = n - a.w;
+
+  stage_rows<DP>(qs, a.q + (size_t)g * a.M * d, a.M, d, d);
+  {   // each row's log2-sum-exp from the split states: 8 threads per row take
+      // every 8th split (online max/sum), then a fixed shuffle tree combines them
+    const int row = tid >> 3, part = tid & 7;
+    const size_t base = (size_t)g * a.splits * kRows + row;
+    float M = -INFINITY, Ssum = 0.f;
+    int bad = 0;
+#pragma unroll 4
+    for (int sp = part; sp < a.splits; sp += 8) {
+      const float ms = a.part.m2[base + (size_t)sp * kRows];
+      const float ss = a.part.S[base + (size_t)sp * kRows];
+      bad |= a.part.bad[base + (size_t)sp * kRows];
+      if (ms > M) {
+        Ssum = Ssum * ex2(M - ms) + ss;
+        M = ms;
+      } else if (ms > -INFINITY) {
+        Ssum += ss * ex2(ms - M);
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      const float Mo = __shfl_xor(M, o), So = __shfl_xor(Ssum, o);
+      bad |= __shfl_xor(bad, o);
+      const float Mn = fmaxf(M, Mo);
+      const float x = (M > -INFINITY) ? Ssum * ex2(M - Mn) : 0.f;
+      const float y = (Mo > -INFINITY) ? So * ex2(Mo - Mn) : 0.f;
+      // the lower lane of the pair adds first, so both lanes hold the same sum
+      Ssum = ((tid & o) == 0) ? x + y : y + x;
+      M = Mn;
+    }
+    if (part == 0) {
+      // rows >= M have no query: lse = +inf makes every p of theirs 0
+      lse_s[row] = (row < a.M && M > -INFINITY) ? M + log2f(Ssum) : INFINITY;
+      if (row < a.M && (bad || !(M > -INFINITY) || !(Ssum <= FLT_MAX)) && ch == 0)
+        atomicOr(a.latch, LATCH_NONFINITE);
+    }
+  }
+  __syncthreads();
+  const float invG = 1.f / (float)a.G;
+
+  // S = Q K^T as in pass 2: lane l owns token l%32 and 16 rows
+  bf16x8 kB[NC];
+  for (int t = wid; t < next; t += kWaves) {
+    const int64_t j0 = e0 + (int64_t)t * kTile;
+    const int64_t tok = j0 + r;
+    const bool tok_ok = tok < e1;
+    load_k_tile<NC, FULLD>(kg, tok, tok_ok, j0 + kTile > e1, hh, d, kB);
+    f32x16 sacc, sacc1;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; sacc1[v] = 0.f; }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (c & 1) sacc1 = mfma32(lds8<DP>(qs, r, 2 * c + hh), kB[c], sacc1);
+      else sacc = mfma32(lds8<DP>(qs, r, 2 * c + hh), kB[c], sacc);
+    }
+    const bool interior = (j0 + kTile <= e1) && (j0 + kTile - 1 <= all_see);
+    float sum = 0.f;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 l4 = *reinterpret_cast<const float4*>(lse_s + 8 * q4 + 4 * hh);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int v = 4 * q4 + i;
+        float p = ex2((sacc[v] + sacc1[v]) * a.scale_log2 - lv[i]);
+        if (!interior) {
+          const int rv = 8 * q4 + 4 * hh + i;
+          const int64_t lim = rv < a.M ? n - a.w + (rv % a.w) : -1;
+          p = (tok_ok && tok <= lim) ? p : 0.f;
+        }
+        sum += p;
+      }
+    }
+    sum += __shfl_xor(sum, 32);
+    if (hh == 0 && tok_ok) rawbuf[tok - e0] = sum * invG;
+  }
+  __syncthreads();
+  for (int64_t j = c0 + tid; j < c1; j += kThreads) {
+    const int64_t lo = max((int64_t)0, j - rad), hi = min(n - 1, j + rad);
+    float mx = rawbuf[lo - e0];
+    for (int64_t i = lo + 1; i <= hi; ++i) mx = fmaxf(mx, rawbuf[i - e0]);
+    a.scores[(size_t)g * n + j] = (j >= n - a.w) ? INFINITY : mx + 0.f;
+  }
+}
+
+template <int DP, bool FULLD>
+static hipError_t launch_attn_dp(void* ctx, const ScoreArgs& a, hipStream_t s) {
+  const size_t lds1 = (size_t)kRows * RowLayout<DP>::ROWB;
+  const size_t lds2 = attn_pass2_lds_bytes<DP>();
+  prof_begin(ctx, "attn_pass1", s);
+  hipLaunchKernelGGL((attn_pass1_kernel<DP, FULLD>), dim3(a.Hkv * a.splits), dim3(kThreads), lds1,
+                     s, a);
+  prof_end(ctx, "attn_pass1", s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  prof_begin(ctx, "attn_pass2", s);
+  hipLaunchKernelGGL((attn_pass2_kernel<DP, FULLD>), dim3((unsigned)a.Hkv * a.chunks2),
+                     dim3(kThreads), lds2, s, a);
+  prof_end(ctx, "attn_pass2", s);
+  return hipGetLastError();
+}
+
+template <int DP>
+static hipError_t launch_attn_d(void* ctx, const ScoreArgs& a, hipStream_t s) {
+  return a.d == DP ? launch_attn_dp<DP, true>(ctx, a, s) : launch_attn_dp<DP, false>(ctx, a, s);
+}
+
+hipError_t launch_score_attention(void* ctx, const ScoreArgs& a, hipStream_t s) {
+  switch (a.DP) {
+    case 32: return launch_attn_d<32>(ctx, a, s);
+    case 64: return launch_attn_d<64>(ctx, a, s);
+    case 96: return launch_attn_d<96>(ctx, a, s);
+    case 128: return launch_attn_d<128>(ctx, a, s);
+    case 160: return launch_attn_d<160>(ctx, a, s);
+    case 192: return launch_attn_d<192>(ctx, a, s);
+    case 224: return launch_attn_d<224>(ctx, a, s);
+    case 256: return launch_attn_d<256>(ctx, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 // ------------------------------------------------------------- host side --
-int plan_splits(int64_t n, int Hkv, int64_t* split_len) {
-  // about kTargetWG1 workgroups over the chip, at least 256 tokens each.
-  int64_t want = (kTargetWG1 + Hkv - 1) / Hkv;
+int plan_splits(int64_t n, int Hkv, int64_t* split_len, int target) {
+  // about `target` workgroups over the chip, at least 256 tokens each.
+  int64_t want = (target + Hkv - 1) / Hkv;
   const int64_t max_by_len = (n + 255) / 256;
   if (want > max_by_len) want = max_by_len;
   if (want > kMaxSplits) want = kMaxSplits;

@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdropkv.so")
 
 OK, EINVAL, ESINGULAR, ENONFINITE, ERANGE, EDEVICE, ENOMEM = range(7)
-KERNELS = ("pass1", "merge", "pass2", "select", "compact")
+KERNELS = ("pass1", "merge", "pass2", "select", "compact", "attn_pass1", "attn_pass2")
 
 
 class DropKVError(RuntimeError):
@@ -42,6 +42,7 @@ def lib():
             "dropkv_create": [ctypes.POINTER(P), ctypes.c_int],
             "dropkv_destroy": [P],
             "dropkv_score": [P, P, P, P, i64, i32, i32, i32, i32, i32, P, P],
+            "dropkv_score_attention": [P, P, P, i64, i32, i32, i32, i32, i32, P, P],
             "dropkv_select": [P, P, i32, i64, i64, P, P],
             "dropkv_compact": [P, P, P, i32, i64, i32, P, i64, P, P, P],
             "dropkv_sync": [P, P],
@@ -132,6 +133,11 @@ class Context:
         _check(lib().dropkv_score(self._h, _ptr(q_win), _ptr(k_cache), _ptr(v_cache), n, w, Hq,
                                   Hkv, d, pool, _ptr(scores), _stream(stream)), "dropkv_score")
 
+    def score_attention(self, q_win, k_cache, n, w, Hq, Hkv, d, pool, scores, stream=None):
+        _check(lib().dropkv_score_attention(self._h, _ptr(q_win), _ptr(k_cache), n, w, Hq, Hkv, d,
+                                            pool, _ptr(scores), _stream(stream)),
+               "dropkv_score_attention")
+
     def select(self, scores, Hkv, n, budget, keep, stream=None):
         _check(lib().dropkv_select(self._h, _ptr(scores), Hkv, n, budget, _ptr(keep),
                                    _stream(stream)), "dropkv_select")
@@ -164,6 +170,10 @@ class Context:
 # Module-level aliases with the C names.
 def dropkv_score(ctx: Context, *args, **kw):
     return ctx.score(*args, **kw)
+
+
+def dropkv_score_attention(ctx: Context, *args, **kw):
+    return ctx.score_attention(*args, **kw)
 
 
 def dropkv_select(ctx: Context, *args, **kw):

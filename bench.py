@@ -165,6 +165,46 @@ def run(args):
     ctx.profile(False)
     ctx.check(stream)
 
+    # ---- the attention-only (SnapKV-style) score mode, timed the same way ----
+    def attn_step():
+        q, k, v = copies[counter[0] % len(copies)]
+        counter[0] += 1
+        ctx.score_attention(q, k, n, w, Hq, Hkv, d, pool, scores, stream)
+        ctx.select(scores, Hkv, n, budget, keep, stream)
+        ctx.compact(k, v, Hkv, n, d, keep, budget, k_out, v_out, stream)
+
+    for _ in range(args.warmup):
+        attn_step()
+    ctx.check(stream)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        attn_step()
+    torch.cuda.synchronize()
+    attn_ms = (time.perf_counter() - t2) * 1e3 / args.steps
+    ctx.profile(True)
+    ctx.profile_reset()
+    for _ in range(args.steps):
+        attn_step()
+    torch.cuda.synchronize()
+    attn_kern = {}
+    for name in ("attn_pass1", "attn_pass2", "select", "compact"):
+        tot, cnt = ctx.profile_read(name)
+        if cnt:
+            attn_kern[name] = round(1e3 * tot / cnt, 2)
+    ctx.profile(False)
+    ctx.check(stream)
+    attn_ss = sum(attn_kern.get(x, 0.0) for x in ("attn_pass1", "attn_pass2", "select"))
+    attention_mode = {
+        "what": "attention-only (SnapKV-style) scores + the same select + compact",
+        "ms_per_step": attn_ms,
+        "tokens_per_s": n / (attn_ms * 1e-3),
+        "kernel_us": attn_kern,
+        "score_select_us": attn_ss,
+        # K read twice + score write/read: 4d + 8 bytes per (token, KV head)
+        "score_select_algorithmic_GBs": Hkv * n * (4.0 * d + 8.0) / (attn_ss * 1e-6) / 1e9,
+    }
+
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 2, dtype=torch.int16, device="cuda")
         dst = torch.empty_like(src)
@@ -208,6 +248,7 @@ def run(args):
         "score_select_frac_of_peak": path_gbs / HBM_PEAK_GBS,
         "token_heads_per_s": Hkv * n / (ms_per_step * 1e-3),
         "profiled_ms_per_step": prof_wall * 1e3 / args.steps,
+        "attention_mode": attention_mode,
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:

@@ -15,6 +15,8 @@
  *     set to +inf, the smallest scores are evicted, and a probability that
  *     rounds to 1 is rejected instead of being epsilon-patched.
  *   - Section 2.2: eviction shrinks the resident cache (compaction).
+ *   - "paper tables", Table 14 and "paper digest", App. B: the attention-only
+ *     (SnapKV-style) score the pages compare against (dropkv_score_attention).
  *
  * Conventions shared by every call:
  *   - bf16 tensors are passed as uint16_t bit patterns in device memory.
@@ -87,6 +89,25 @@ int dropkv_score(dropkv_ctx *ctx, const uint16_t *q_win, const uint16_t *k_cache
                  int32_t pool, float *scores, void *stream);
 
 /*
+ * Attention-only scores: the comparison rule the pages evaluate DropKV against
+ * ("paper tables", Table 14, SnapKV row: MaxPool1d over the window-summed
+ * attention weights; "paper digest", App. B: the same observation window and
+ * pooling kernel, without DropKV's value-residual factor).  For each KV head g
+ * and position j:
+ *       raw_g[j]    = (1/G) * sum_{h in group g} sum_{t < w} p_j^(h,t)
+ *                     (p = softmax(K q / sqrt(d)) over the keys query t sees),
+ *       scores[g][j] = max over [j - r, j + r] and [0, n) of raw_g[i], then +inf
+ *                     for j >= n - w  -- the same pooling and protection as
+ *                     dropkv_score, so dropkv_select applies unchanged.
+ * Only K is read (no value cache).  Arguments and layouts as dropkv_score.
+ * EINVAL as for dropkv_score.  Latched: ENONFINITE if an input element is not
+ * finite.  (A probability near 1 is not an error here.)
+ */
+int dropkv_score_attention(dropkv_ctx *ctx, const uint16_t *q_win, const uint16_t *k_cache,
+                           int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int32_t d, int32_t pool,
+                           float *scores, void *stream);
+
+/*
  * Keep `budget` tokens per KV head: evict the k = n - budget smallest scores by
  * the total order (score, index) ascending -- among equal scores the older token
  * goes first -- and write the survivors' indices in ascending order.
@@ -128,7 +149,7 @@ const char *dropkv_strerror(int code);
  * Per-kernel timing for measurement.  While enabled, every kernel the library
  * launches is bracketed by HIP events on the caller's stream; dropkv_profile_read
  * returns, for the kernel family `name` ("pass1", "merge", "pass2",
- * "select", "compact"), the summed milliseconds and launch count since the last
+ * "select", "compact", "attn_pass1", "attn_pass2"), the summed milliseconds and launch count since the last
  * reset (it synchronises on the recorded events).  Disabled by default.
  */
 int dropkv_profile_enable(dropkv_ctx *ctx, int on);
