@@ -278,6 +278,42 @@ int oracle_compact(const uint16_t *in, int hkv, int64_t n, int d, const int32_t 
 }
 
 /*
+ * Log-sum-exp of every window query's logits over the keys it sees (natural
+ * log): lse[h][t] = log sum_{j <= n-w+t} exp(q.k_j / sqrt(d)).  With the output a
+ * of oracle_window_attention, this is what pass 1 can hand back to the caller
+ * (the pages' result object returns the query output alongside the scores).
+ */
+int oracle_window_lse(const uint16_t *q, const uint16_t *k, int64_t n, int w, int hq, int hkv,
+                      int d, double *lse) {
+    int rc = check_shapes(n, w, hq, hkv, d);
+    if (rc) return rc;
+    const int G = hq / hkv;
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+    double *lg = malloc(sizeof(double) * (size_t)n);
+    if (!lg) return ORC_ENOMEM;
+    for (int h = 0; h < hq; ++h) {
+        const int g = h / G;
+        for (int t = 0; t < w; ++t) {
+            const int64_t last = n - w + t;
+            const uint16_t *qr = q + ((size_t)h * w + t) * d;
+            double mx = -INFINITY;
+            for (int64_t j = 0; j <= last; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < d; ++i)
+                    acc += bf16_to_double(qr[i]) * bf16_to_double(k[((size_t)g * n + j) * d + i]);
+                lg[j] = acc * inv_sqrt_d;
+                if (lg[j] > mx) mx = lg[j];
+            }
+            double sum = 0.0;
+            for (int64_t j = 0; j <= last; ++j) sum += exp(lg[j] - mx);
+            lse[(size_t)h * w + t] = mx + log(sum);
+        }
+    }
+    free(lg);
+    return ORC_OK;
+}
+
+/*
  * Attention-only scores (the pages' negative control; "paper tables", Table 14,
  * SnapKV row: MaxPool1d over the window-summed attention weights, kept large;
  * "paper digest", App. B: the same observation window and pooling kernel as

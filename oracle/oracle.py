@@ -55,6 +55,7 @@ def load(path: str):
     L.oracle_compact.argtypes = [P, i32, i64, i32, P, i64, P]
     L.oracle_window_attention.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P]
     L.oracle_attention_raw.argtypes = [P, P, i64, i32, i32, i32, i32, i32, P]
+    L.oracle_window_lse.argtypes = [P, P, i64, i32, i32, i32, i32, P]
     L.oracle_attention_score.argtypes = [P, P, i64, i32, i32, i32, i32, i32, i32, P]
     for f in (L.oracle_raw_scores, L.oracle_pool_protect, L.oracle_score, L.oracle_select,
               L.oracle_compact, L.oracle_window_attention):
@@ -172,6 +173,15 @@ def window_attention(q, k, v):
     _check(lib().oracle_window_attention(_ptr(q), _ptr(k), _ptr(v), n, w, Hq, Hkv, d,
                                          _ptr(p), _ptr(a), _ptr(sx)))
     return p, a, sx
+
+
+def window_lse(q, k):
+    """Natural-log log-sum-exp of each window query's visible logits: float64 [Hq][w]."""
+    q, k = _u16(q), _u16(k)
+    Hq, w, d, Hkv, n = _dims(q, k)
+    out = np.zeros((Hq, w))
+    _check(lib().oracle_window_lse(_ptr(q), _ptr(k), n, w, Hq, Hkv, d, _ptr(out)))
+    return out
 
 
 def max_probability(q, k, v) -> float:

@@ -74,3 +74,24 @@ def test_nonfinite_rejected():
     with pytest.raises(orc.OracleError) as e:
         orc.attention_raw(q, k)
     assert e.value.code == 3
+
+
+def test_window_lse_against_logsumexp_and_closed_form():
+    """Window LSE: torch's float64 logsumexp over the tail-causal logits, and
+    log(n-w+t+1) exactly for a zero query."""
+    import torch
+    rng = np.random.default_rng(4)
+    Hq, Hkv, w, d, n = 4, 2, 3, 16, 25
+    q, k = _rand(rng, Hq, Hkv, w, d, n, scale=2.0)
+    got = orc.window_lse(q, k)
+    qf = torch.from_numpy(wl.bf16_to_f32(q).astype(np.float64))
+    kf = torch.from_numpy(wl.bf16_to_f32(k).astype(np.float64))
+    G = Hq // Hkv
+    for h in range(Hq):
+        for t in range(w):
+            P = n - w + t
+            logits = kf[h // G, : P + 1] @ qf[h, t] / np.sqrt(d)
+            assert abs(got[h, t] - float(torch.logsumexp(logits, 0))) <= 1e-12 * max(1.0, abs(got[h, t]))
+    z = orc.window_lse(np.zeros_like(q), k)
+    for t in range(w):
+        np.testing.assert_allclose(z[:, t], np.log(n - w + t + 1), rtol=1e-15)
