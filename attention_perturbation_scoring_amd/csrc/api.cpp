@@ -139,9 +139,11 @@ namespace {
 // Shared by both scoring entry points: checks, launch geometry, scratch.
 int score_common(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
                  const uint16_t* v_cache, bool attention_only, int64_t n, int32_t w, int32_t Hq,
-                 int32_t Hkv, int32_t d, int32_t pool, float* scores, void* stream) {
+                 int32_t Hkv, int32_t d, int32_t pool, float* scores, float* out_a,
+                 float* out_lse, void* stream) {
   if (!c) return DROPKV_EINVAL;
   if (!aligned16(q_win) || !aligned16(k_cache) || !aligned16(scores)) return DROPKV_EINVAL;
+  if ((out_a && !aligned16(out_a)) || (out_lse && !aligned16(out_lse))) return DROPKV_EINVAL;
   if (!attention_only && !aligned16(v_cache)) return DROPKV_EINVAL;
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return DROPKV_EINVAL;
   if (n < 1 || n >= (int64_t(1) << 31)) return DROPKV_EINVAL;
@@ -162,6 +164,8 @@ int score_common(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
   a.chunks2 = plan_chunks2(n, Hkv, &a.chunk2_len);
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
   a.latch = c->latch;
+  a.out_a = out_a;
+  a.out_lse = out_lse;
   const size_t need = score_scratch_bytes(Hkv, a.splits, a.DP);
   if (need > c->scratch_bytes) {
     if (c->scratch) {
@@ -184,13 +188,23 @@ int score_common(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
 int dropkv_score(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
                  const uint16_t* v_cache, int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int32_t d,
                  int32_t pool, float* scores, void* stream) {
-  return score_common(c, q_win, k_cache, v_cache, false, n, w, Hq, Hkv, d, pool, scores, stream);
+  return score_common(c, q_win, k_cache, v_cache, false, n, w, Hq, Hkv, d, pool, scores, nullptr,
+                      nullptr, stream);
+}
+
+int dropkv_score_ex(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
+                    const uint16_t* v_cache, int64_t n, int32_t w, int32_t Hq, int32_t Hkv,
+                    int32_t d, int32_t pool, float* scores, float* out_a, float* out_lse,
+                    void* stream) {
+  return score_common(c, q_win, k_cache, v_cache, false, n, w, Hq, Hkv, d, pool, scores, out_a,
+                      out_lse, stream);
 }
 
 int dropkv_score_attention(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
                            int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int32_t d, int32_t pool,
                            float* scores, void* stream) {
-  return score_common(c, q_win, k_cache, nullptr, true, n, w, Hq, Hkv, d, pool, scores, stream);
+  return score_common(c, q_win, k_cache, nullptr, true, n, w, Hq, Hkv, d, pool, scores, nullptr,
+                      nullptr, stream);
 }
 
 int dropkv_select(dropkv_ctx* c, const float* scores, int32_t Hkv, int64_t n, int64_t budget,

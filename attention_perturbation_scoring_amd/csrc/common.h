@@ -152,6 +152,8 @@ struct ScoreArgs {
   Partials part;
   RowState rs;
   uint32_t* latch;
+  float* out_a;     // optional [Hq][w][d] fp32: each window query's attention output
+  float* out_lse;   // optional [Hq][w]: natural-log log-sum-exp of its visible logits
 };
 
 // Scratch of the selection kernels (owned by the context; hist1 and cand_cnt

@@ -694,6 +694,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
     const __bf16 lo = (__bf16)(avv - (float)hi);
     a.rs.a_hi[ro * DP + tid] = __builtin_bit_cast(u16, hi);
     a.rs.a_lo[ro * DP + tid] = __builtin_bit_cast(u16, lo);
+    // row r of head g is window query (g * G + r / w, r % w): [Hq][w][d] order
+    if (a.out_a && tid < a.d) a.out_a[((size_t)g * a.M + r) * a.d + tid] = avv;
     if (tid < a.d && jst >= 0) {
       const float df = avv - vstar;
       dist = df * df;
@@ -717,6 +719,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
     a.rs.m2[ro] = M;
     a.rs.S[ro] = Sf;
     a.rs.lse2[ro] = M + log2f(Sf);
+    if (a.out_lse) a.out_lse[(size_t)g * a.M + r] = (M + log2f(Sf)) * 0.6931471805599453f;
     a.rs.an2[ro] = an2;
     a.rs.jstar[ro] = jst;
     a.rs.fix[ro] = fix ? 1 : 0;

@@ -43,6 +43,7 @@ def lib():
             "dropkv_destroy": [P],
             "dropkv_score": [P, P, P, P, i64, i32, i32, i32, i32, i32, P, P],
             "dropkv_score_attention": [P, P, P, i64, i32, i32, i32, i32, i32, P, P],
+            "dropkv_score_ex": [P, P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P],
             "dropkv_select": [P, P, i32, i64, i64, P, P],
             "dropkv_compact": [P, P, P, i32, i64, i32, P, i64, P, P, P],
             "dropkv_sync": [P, P],
@@ -133,6 +134,12 @@ class Context:
         _check(lib().dropkv_score(self._h, _ptr(q_win), _ptr(k_cache), _ptr(v_cache), n, w, Hq,
                                   Hkv, d, pool, _ptr(scores), _stream(stream)), "dropkv_score")
 
+    def score_ex(self, q_win, k_cache, v_cache, n, w, Hq, Hkv, d, pool, scores, out_a=None,
+                 out_lse=None, stream=None):
+        _check(lib().dropkv_score_ex(self._h, _ptr(q_win), _ptr(k_cache), _ptr(v_cache), n, w, Hq,
+                                     Hkv, d, pool, _ptr(scores), _ptr(out_a), _ptr(out_lse),
+                                     _stream(stream)), "dropkv_score_ex")
+
     def score_attention(self, q_win, k_cache, n, w, Hq, Hkv, d, pool, scores, stream=None):
         _check(lib().dropkv_score_attention(self._h, _ptr(q_win), _ptr(k_cache), n, w, Hq, Hkv, d,
                                             pool, _ptr(scores), _stream(stream)),
@@ -170,6 +177,10 @@ class Context:
 # Module-level aliases with the C names.
 def dropkv_score(ctx: Context, *args, **kw):
     return ctx.score(*args, **kw)
+
+
+def dropkv_score_ex(ctx: Context, *args, **kw):
+    return ctx.score_ex(*args, **kw)
 
 
 def dropkv_score_attention(ctx: Context, *args, **kw):

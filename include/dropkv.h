@@ -89,6 +89,22 @@ int dropkv_score(dropkv_ctx *ctx, const uint16_t *q_win, const uint16_t *k_cache
                  int32_t pool, float *scores, void *stream);
 
 /*
+ * dropkv_score, also handing back what the first pass computes anyway for the
+ * window queries (the pages' result object returns the query output with the
+ * scores; the notes, "Code mapping and limits"):
+ *   out_a   [Hq][w][d] fp32 (may be NULL): a = sum_j p_j v_j of window query
+ *           (h, t), p = softmax over the keys j <= n-w+t of q.k_j / sqrt(d);
+ *   out_lse [Hq][w] fp32 (may be NULL): log sum_j exp(q.k_j / sqrt(d)) over the
+ *           same keys (natural log).
+ * Both are caller-owned device memory, 16-byte aligned.  Everything else is as
+ * for dropkv_score; on a latched error their contents are unspecified.
+ */
+int dropkv_score_ex(dropkv_ctx *ctx, const uint16_t *q_win, const uint16_t *k_cache,
+                    const uint16_t *v_cache, int64_t n, int32_t w, int32_t Hq, int32_t Hkv,
+                    int32_t d, int32_t pool, float *scores, float *out_a, float *out_lse,
+                    void *stream);
+
+/*
  * Attention-only scores: the comparison rule the pages evaluate DropKV against
  * ("paper tables", Table 14, SnapKV row: MaxPool1d over the window-summed
  * attention weights; "paper digest", App. B: the same observation window and
