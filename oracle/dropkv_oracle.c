@@ -264,6 +264,27 @@ int oracle_select(const double *scores, int hkv, int64_t n, int64_t budget, int3
     return ORC_OK;
 }
 
+/*
+ * Layer-wide selection (cross-head budgets; "paper digest" §5.3 pairs DropKV
+ * scores with an adaptive head-budget allocation whose rule the pages do not
+ * give -- reading: one selection over the whole layer).  Evict the
+ * hkv*n - budget smallest scores over all heads by (score, head, index)
+ * ascending; keep[] lists the survivors as flat indices g*n + j in ascending
+ * order and counts[g] how many of them belong to head g.
+ */
+int oracle_select_layer(const double *scores, int hkv, int64_t n, int64_t budget, int32_t *keep,
+                        int32_t *counts) {
+    const int64_t total = (int64_t)hkv * n;
+    if (hkv < 1 || n < 1 || total >= ((int64_t)1 << 31) || budget < 0 || budget > total)
+        return ORC_EINVAL;
+    /* the flat [hkv][n] array is one sequence whose index order is (head, index) */
+    int rc = oracle_select(scores, 1, total, budget, keep);
+    if (rc != ORC_OK) return rc;
+    for (int g = 0; g < hkv; ++g) counts[g] = 0;
+    for (int64_t r = 0; r < budget; ++r) counts[keep[r] / n] += 1;
+    return ORC_OK;
+}
+
 /* Compaction: out[g][r][:] = in[g][keep[g][r]][:] as exact bit copies. */
 int oracle_compact(const uint16_t *in, int hkv, int64_t n, int d, const int32_t *keep,
                    int64_t budget, uint16_t *out) {

@@ -56,6 +56,7 @@ def load(path: str):
     L.oracle_window_attention.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P]
     L.oracle_attention_raw.argtypes = [P, P, i64, i32, i32, i32, i32, i32, P]
     L.oracle_window_lse.argtypes = [P, P, i64, i32, i32, i32, i32, P]
+    L.oracle_select_layer.argtypes = [P, i32, i64, i64, P, P]
     L.oracle_attention_score.argtypes = [P, P, i64, i32, i32, i32, i32, i32, i32, P]
     for f in (L.oracle_raw_scores, L.oracle_pool_protect, L.oracle_score, L.oracle_select,
               L.oracle_compact, L.oracle_window_attention):
@@ -151,6 +152,17 @@ def select(scores, budget):
     keep = np.zeros((Hkv, budget), dtype=np.int32)
     _check(lib().oracle_select(_ptr(s), Hkv, n, budget, _ptr(keep)))
     return keep
+
+
+def select_layer(scores, budget):
+    """Layer-wide selection: (flat kept indices g*n + j ascending int32 [budget],
+    per-head counts int32 [Hkv])."""
+    s = np.ascontiguousarray(scores, dtype=np.float64)
+    Hkv, n = s.shape
+    keep = np.zeros(max(budget, 1), dtype=np.int32)
+    counts = np.zeros(Hkv, dtype=np.int32)
+    _check(lib().oracle_select_layer(_ptr(s), Hkv, n, budget, _ptr(keep), _ptr(counts)))
+    return keep[:budget], counts
 
 
 def compact(x, keep):
