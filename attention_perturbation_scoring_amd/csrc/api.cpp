@@ -24,9 +24,13 @@ struct dropkv_ctx {
   int device = 0;
   void* scratch = nullptr;
   size_t scratch_bytes = 0;
-  void* sel_scratch = nullptr;     // selection scratch (see carve_select)
-  size_t sel_bytes = 0;
-  int sel_hkv = 0;                 // head count the zeroed prefix was laid out for
+  // selection scratch (see carve_select): [0] per-head selection, [1] the
+  // layer-wide one, kept apart so that alternating calls do not re-zero them
+  struct SelBuf {
+    void* p = nullptr;
+    size_t bytes = 0;
+    int hkv = 0;                   // head count the zeroed prefix was laid out for
+  } sel[2];
   uint32_t* latch = nullptr;       // device word
   uint32_t* latch_host = nullptr;  // pinned read-back
   bool prof = false;
@@ -120,7 +124,8 @@ int dropkv_destroy(dropkv_ctx* c) {
   for (auto& r : c->recs) { (void)hipEventDestroy(r.start); (void)hipEventDestroy(r.stop); }
   for (auto e : c->free_events) (void)hipEventDestroy(e);
   if (c->scratch) (void)hipFree(c->scratch);
-  if (c->sel_scratch) (void)hipFree(c->sel_scratch);
+  for (auto& b : c->sel)
+    if (b.p) (void)hipFree(b.p);
   if (c->latch) (void)hipFree(c->latch);
   if (c->latch_host) (void)hipHostFree(c->latch_host);
   delete c;
@@ -207,6 +212,39 @@ int dropkv_score_attention(dropkv_ctx* c, const uint16_t* q_win, const uint16_t*
                       nullptr, stream);
 }
 
+namespace {
+
+// Selection scratch for Hkv heads of n tokens in buffer `b`: (re)allocated on
+// growth; its zeroed prefix is (re)laid out when the head count changes, and
+// every selection leaves it zeroed again.
+int sel_prepare(dropkv_ctx* c, dropkv_ctx::SelBuf& b, int Hkv, int64_t n, hipStream_t s,
+                SelScratch* sc) {
+  const size_t need = select_scratch_bytes(Hkv, n);
+  if (need > b.bytes || Hkv != b.hkv) {
+    if (b.p) {
+      (void)hipStreamSynchronize(s);
+      (void)hipDeviceSynchronize();
+      if (need > b.bytes) {
+        (void)hipFree(b.p);
+        b.p = nullptr;
+        b.bytes = 0;
+      }
+    }
+    if (!b.p) {
+      hipError_t e = hipMalloc(&b.p, need);
+      if (e != hipSuccess) { b.p = nullptr; return DROPKV_ENOMEM; }
+      b.bytes = need;
+    }
+    hipError_t e = hipMemset(b.p, 0, select_zero_prefix_bytes(Hkv));
+    if (e != hipSuccess) return to_status(e);
+    b.hkv = Hkv;
+  }
+  carve_select(b.p, Hkv, n, sc);
+  return DROPKV_OK;
+}
+
+}  // namespace
+
 int dropkv_select(dropkv_ctx* c, const float* scores, int32_t Hkv, int64_t n, int64_t budget,
                   int32_t* keep, void* stream) {
   if (!c || !aligned16(scores)) return DROPKV_EINVAL;
@@ -216,31 +254,31 @@ int dropkv_select(dropkv_ctx* c, const float* scores, int32_t Hkv, int64_t n, in
   DeviceGuard guard(c->device);
   if (!guard.ok) return DROPKV_EDEVICE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t need = select_scratch_bytes(Hkv, n);
-  if (need > c->sel_bytes || Hkv != c->sel_hkv) {
-    // (re)allocate; the histogram and candidate counters start zeroed and every
-    // selection leaves them zeroed again
-    if (c->sel_scratch) {
-      (void)hipStreamSynchronize(s);
-      (void)hipDeviceSynchronize();
-      if (need > c->sel_bytes) {
-        (void)hipFree(c->sel_scratch);
-        c->sel_scratch = nullptr;
-        c->sel_bytes = 0;
-      }
-    }
-    if (!c->sel_scratch) {
-      hipError_t e = hipMalloc(&c->sel_scratch, need);
-      if (e != hipSuccess) { c->sel_scratch = nullptr; return DROPKV_ENOMEM; }
-      c->sel_bytes = need;
-    }
-    hipError_t e = hipMemset(c->sel_scratch, 0, select_zero_prefix_bytes(Hkv));
-    if (e != hipSuccess) return to_status(e);
-    c->sel_hkv = Hkv;
-  }
   SelScratch sc{};
-  carve_select(c->sel_scratch, Hkv, n, &sc);
+  const int rc = sel_prepare(c, c->sel[0], Hkv, n, s, &sc);
+  if (rc != DROPKV_OK) return rc;
   return to_status(launch_select(c, scores, Hkv, n, budget, keep, c->latch, sc, s));
+}
+
+int dropkv_select_layer(dropkv_ctx* c, const float* scores, int32_t Hkv, int64_t n,
+                        int64_t budget, int32_t* keep, int32_t* counts, void* stream) {
+  if (!c || !aligned16(scores) || !aligned16(counts)) return DROPKV_EINVAL;
+  if (Hkv < 1 || n < 1) return DROPKV_EINVAL;
+  const int64_t total = (int64_t)Hkv * n;
+  if (total >= (int64_t(1) << 31) || budget < 0 || budget > total) return DROPKV_EINVAL;
+  if (budget > 0 && !aligned16(keep)) return DROPKV_EINVAL;
+  DeviceGuard guard(c->device);
+  if (!guard.ok) return DROPKV_EDEVICE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (budget > 0) {
+    // the [Hkv][n] scores are one sequence in (head, index) order
+    SelScratch sc{};
+    const int rc = sel_prepare(c, c->sel[1], 1, total, s, &sc);
+    if (rc != DROPKV_OK) return rc;
+    const hipError_t e = launch_select(c, scores, 1, total, budget, keep, c->latch, sc, s);
+    if (e != hipSuccess) return to_status(e);
+  }
+  return to_status(launch_layer_counts(c, keep, budget, n, Hkv, counts, c->latch, s));
 }
 
 int dropkv_compact(dropkv_ctx* c, const uint16_t* k, const uint16_t* v, int32_t Hkv, int64_t n,
@@ -275,7 +313,7 @@ int dropkv_sync(dropkv_ctx* c, void* stream) {
   }
   if (bits & LATCH_TIMEOUT) {
     // a selection gave up inside its barriers: its scratch counters are stale
-    c->sel_hkv = 0;
+    c->sel[0].hkv = c->sel[1].hkv = 0;
     return DROPKV_EDEVICE;
   }
   if (bits & LATCH_NONFINITE) return DROPKV_ENONFINITE;

@@ -188,6 +188,8 @@ void prof_end(void* ctx, const char* name, hipStream_t s);
 hipError_t launch_score(void* ctx, const ScoreArgs& a, hipStream_t s);
 hipError_t launch_select(void* ctx, const float* scores, int Hkv, int64_t n, int64_t budget,
                          int32_t* keep, uint32_t* latch, const SelScratch& sc, hipStream_t s);
+hipError_t launch_layer_counts(void* ctx, const int32_t* keep, int64_t budget, int64_t n, int Hkv,
+                               int32_t* counts, uint32_t* latch, hipStream_t s);
 hipError_t launch_compact(void* ctx, const u16* k, const u16* v, int Hkv, int64_t n, int d,
                           const int32_t* keep, int64_t budget, u16* k_out, u16* v_out,
                           uint32_t* latch, hipStream_t s);

@@ -818,6 +818,35 @@ hipError_t launch_select(void* ctx, const float* scores, int Hkv, int64_t n, int
   return hipGetLastError();
 }
 
+// Per-head counts of a layer-wide keep list (flat indices g*n + j, ascending):
+// head g owns the entries in [g*n, (g+1)*n), found by binary search.
+__global__ __launch_bounds__(256) void layer_counts_kernel(const int32_t* keep, int64_t budget,
+                                                           int64_t n, int Hkv, int32_t* counts,
+                                                           const uint32_t* latch) {
+  if (latched(latch)) return;
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= Hkv) return;
+  auto lower = [&](int64_t x) {
+    int64_t lo = 0, hi = budget;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) / 2;
+      if (keep[mid] < x) lo = mid + 1;
+      else hi = mid;
+    }
+    return lo;
+  };
+  counts[g] = (int32_t)(lower((int64_t)(g + 1) * n) - lower((int64_t)g * n));
+}
+
+hipError_t launch_layer_counts(void* ctx, const int32_t* keep, int64_t budget, int64_t n, int Hkv,
+                               int32_t* counts, uint32_t* latch, hipStream_t s) {
+  prof_begin(ctx, "select", s);
+  hipLaunchKernelGGL(layer_counts_kernel, dim3((unsigned)((Hkv + 255) / 256)), dim3(256), 0, s,
+                     keep, budget, n, Hkv, counts, (const uint32_t*)latch);
+  prof_end(ctx, "select", s);
+  return hipGetLastError();
+}
+
 hipError_t launch_compact(void* ctx, const u16* k, const u16* v, int Hkv, int64_t n, int d,
                           const int32_t* keep, int64_t budget, u16* k_out, u16* v_out,
                           uint32_t* latch, hipStream_t s) {

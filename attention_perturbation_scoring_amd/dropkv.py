@@ -45,6 +45,7 @@ def lib():
             "dropkv_score_attention": [P, P, P, i64, i32, i32, i32, i32, i32, P, P],
             "dropkv_score_ex": [P, P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P],
             "dropkv_select": [P, P, i32, i64, i64, P, P],
+            "dropkv_select_layer": [P, P, i32, i64, i64, P, P, P],
             "dropkv_compact": [P, P, P, i32, i64, i32, P, i64, P, P, P],
             "dropkv_sync": [P, P],
             "dropkv_profile_enable": [P, ctypes.c_int],
@@ -149,6 +150,10 @@ class Context:
         _check(lib().dropkv_select(self._h, _ptr(scores), Hkv, n, budget, _ptr(keep),
                                    _stream(stream)), "dropkv_select")
 
+    def select_layer(self, scores, Hkv, n, budget, keep, counts, stream=None):
+        _check(lib().dropkv_select_layer(self._h, _ptr(scores), Hkv, n, budget, _ptr(keep),
+                                         _ptr(counts), _stream(stream)), "dropkv_select_layer")
+
     def compact(self, k, v, Hkv, n, d, keep, budget, k_out, v_out, stream=None):
         _check(lib().dropkv_compact(self._h, _ptr(k), _ptr(v), Hkv, n, d, _ptr(keep), budget,
                                     _ptr(k_out), _ptr(v_out), _stream(stream)), "dropkv_compact")
@@ -189,6 +194,10 @@ def dropkv_score_attention(ctx: Context, *args, **kw):
 
 def dropkv_select(ctx: Context, *args, **kw):
     return ctx.select(*args, **kw)
+
+
+def dropkv_select_layer(ctx: Context, *args, **kw):
+    return ctx.select_layer(*args, **kw)
 
 
 def dropkv_compact(ctx: Context, *args, **kw):

@@ -205,6 +205,21 @@ def run(args):
         "score_select_algorithmic_GBs": Hkv * n * (4.0 * d + 8.0) / (attn_ss * 1e-6) / 1e9,
     }
 
+    # ---- layer-wide selection (cross-head budgets) over the same scores ----
+    keep_l = torch.empty((Hkv * budget,), dtype=torch.int32, device="cuda")
+    counts_l = torch.empty((Hkv,), dtype=torch.int32, device="cuda")
+    for _ in range(args.warmup):
+        ctx.select_layer(scores, Hkv, n, Hkv * budget, keep_l, counts_l, stream)
+    ctx.profile(True)
+    ctx.profile_reset()
+    for _ in range(args.steps):
+        ctx.select_layer(scores, Hkv, n, Hkv * budget, keep_l, counts_l, stream)
+    torch.cuda.synchronize()
+    tot, cnt = ctx.profile_read("select")   # selection + per-head counts
+    ctx.profile(False)
+    ctx.check(stream)
+    layer_select_us = 1e3 * tot / max(cnt // 2, 1)
+
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 2, dtype=torch.int16, device="cuda")
         dst = torch.empty_like(src)
@@ -249,6 +264,7 @@ def run(args):
         "token_heads_per_s": Hkv * n / (ms_per_step * 1e-3),
         "profiled_ms_per_step": prof_wall * 1e3 / args.steps,
         "attention_mode": attention_mode,
+        "layer_select_us": layer_select_us,
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:

@@ -141,6 +141,26 @@ int dropkv_select(dropkv_ctx *ctx, const float *scores, int32_t Hkv, int64_t n, 
                   int32_t *keep, void *stream);
 
 /*
+ * Layer-wide selection for cross-head budgets ("paper digest" §5.3 pairs DropKV
+ * scores with an adaptive per-head budget; the pages do not give the
+ * allocation rule, and this call takes the plainest one: a single selection over
+ * the whole layer).  Evict the Hkv*n - budget smallest of all the layer's scores
+ * by (score, head, index) ascending.
+ *   scores [Hkv][n] fp32 (in), budget = total tokens kept over all heads;
+ *   keep   [budget] int32 (out): survivors as flat indices g*n + j, ascending
+ *          (so head-major, each head's indices ascending);
+ *   counts [Hkv] int32 (out): survivors per head (they sum to budget).
+ * The +inf window of every head survives whenever budget >= Hkv*w.  The packed
+ * cache follows from dropkv_compact with Hkv = 1 and n = Hkv*n (the keep
+ * entries address rows of the [Hkv][n][d] cache directly).
+ * EINVAL if: a pointer is NULL or misaligned (keep may be NULL when budget is
+ * 0); Hkv < 1; n < 1; Hkv*n >= 2^31; budget < 0 or budget > Hkv*n.
+ * Latched errors and device waits as for dropkv_select.
+ */
+int dropkv_select_layer(dropkv_ctx *ctx, const float *scores, int32_t Hkv, int64_t n,
+                        int64_t budget, int32_t *keep, int32_t *counts, void *stream);
+
+/*
  * Gather the kept rows into a packed cache (exact bit copies):
  *   k_out[g][r][:] = k[g][keep[g][r]][:],  v_out likewise;  [Hkv][budget][d] bf16.
  * Inputs and outputs must not overlap.
