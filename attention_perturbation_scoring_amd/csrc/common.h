@@ -108,7 +108,11 @@ constexpr int kChunk2 = 2048;                // most tokens per pass-2 workgroup
 // their workgroups keep four waves.)
 constexpr int kP1WgWaves = DROPKV_P1_WG_WAVES;
 constexpr int p1_waves(int DP) { return DP <= 128 ? kP1WgWaves : 4; }
-constexpr int kTargetWG1 = 256 * 4 * kP1Waves / kP1WgWaves;   // pass-1 workgroups aimed for
+#ifndef DROPKV_P1_SPLIT_MULT
+#define DROPKV_P1_SPLIT_MULT 1
+#endif
+constexpr int kTargetWG1 =   // pass-1 workgroups aimed for
+    DROPKV_P1_SPLIT_MULT * 256 * 4 * kP1Waves / kP1WgWaves;
 constexpr int kTargetWG2 = 256 * kP2Waves;   // pass-2 workgroups aimed for over all heads
 
 // S_excl below this (argmax probability above ~0.94) routes the arg-max term

@@ -28,8 +28,9 @@ namespace dropkv {
 // candidate exchange.)  Otherwise selection runs as four wide kernels over
 // blocks of kSelBlock tokens:
 //   s1  12-bit histogram of the keys' top bits (per-block LDS, then global adds)
-//   s2  find the bin b1 holding the k-th smallest key; count keys above b1 per
-//       block and collect the keys of bin b1 (with their indices) as candidates
+//   find1  per head, the bin b1 holding the k-th smallest key
+//   s2  count keys above b1 per block and collect the keys of bin b1 (with
+//       their indices) as candidates
 //   s3  per head: the exact k-th smallest key T from the candidates (two more
 //       10-bit digits), how many keys equal to T are evicted, and each block's
 //       output offset and number of evicted ties
@@ -145,21 +146,31 @@ __device__ void find_bin(const uint32_t* hist, int nbins, uint32_t krem, uint32_
   __syncthreads();
 }
 
+// Once per head: the 12-bit bin holding the k-th smallest key, and the rank
+// left within it (so that s2's blocks read two words, not the histogram).
+__global__ __launch_bounds__(kSelThreads) void select_find1(SelArgs a) {
+  __shared__ uint32_t sh[2 * (kSelThreads / 64) + 1];
+  __shared__ uint32_t s_bin, s_below;
+  if (latched(a.latch)) return;
+  const int g = blockIdx.x;
+  const uint32_t kev = (uint32_t)(a.n - a.budget);
+  find_bin<kSelThreads / 64>(a.sc.hist1 + (size_t)g * kBins1, kBins1, kev, &s_bin, &s_below, sh);
+  if (threadIdx.x == 0) {
+    a.sc.b1[g] = s_bin;
+    a.sc.krem1[g] = kev - s_below;
+  }
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_s2(SelArgs a) {
   __shared__ uint32_t sh[2 * (kSelThreads / 64) + 1];
-  __shared__ uint32_t s_bin, s_below, s_cnt, s_base;
+  __shared__ uint32_t s_cnt, s_base;
   __shared__ uint32_t lk[kSelBlock];
   __shared__ int32_t li[kSelBlock];
   if (latched(a.latch)) return;
   const int g = blockIdx.x / a.nblk, b = blockIdx.x % a.nblk;
   const int tid = threadIdx.x;
-  const uint32_t kev = (uint32_t)(a.n - a.budget);
-  find_bin<kSelThreads / 64>(a.sc.hist1 + (size_t)g * kBins1, kBins1, kev, &s_bin, &s_below, sh);
-  const uint32_t b1 = s_bin;
-  if (tid == 0) {
-    s_cnt = 0u;
-    if (b == 0) { a.sc.b1[g] = b1; a.sc.krem1[g] = kev - s_below; }
-  }
+  const uint32_t b1 = a.sc.b1[g];
+  if (tid == 0) s_cnt = 0u;
   __syncthreads();
   const float* sg = a.scores + (size_t)g * a.n;
   const int64_t base = (int64_t)b * kSelBlock;
@@ -292,12 +303,22 @@ __global__ __launch_bounds__(kSelThreads) void select_s4(SelArgs a) {
     const int64_t base = (int64_t)b * kSelBlock + (int64_t)tid * kSelPer;
     uint32_t keys[kSelPer];
     uint32_t nt = 0u;
+    if (base + kSelPer <= a.n && (((size_t)g * a.n + base) & 3) == 0) {   // 16-byte aligned run
 #pragma unroll
-    for (int i = 0; i < kSelPer; ++i) {
-      const int64_t j = base + i;
-      keys[i] = (j < a.n) ? order_key(sg[j]) : 0u;
-      if (j < a.n && keys[i] == T) ++nt;
+      for (int q = 0; q < kSelPer / 4; ++q) {
+        const float4 x = *reinterpret_cast<const float4*>(sg + base + 4 * q);
+        keys[4 * q + 0] = order_key(x.x);
+        keys[4 * q + 1] = order_key(x.y);
+        keys[4 * q + 2] = order_key(x.z);
+        keys[4 * q + 3] = order_key(x.w);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kSelPer; ++i) keys[i] = (base + i < a.n) ? order_key(sg[base + i]) : 0u;
     }
+#pragma unroll
+    for (int i = 0; i < kSelPer; ++i)
+      if (base + i < a.n && keys[i] == T) ++nt;
     uint32_t ttot;
     uint32_t rank = block_exscan<kSelThreads / 64>(nt, &ttot, sh);
     uint32_t kc = 0u, keepbits = 0u;
@@ -811,6 +832,7 @@ hipError_t launch_select(void* ctx, const float* scores, int Hkv, int64_t n, int
   }
   const unsigned grid = (unsigned)((int64_t)Hkv * a.nblk);
   hipLaunchKernelGGL(select_s1, dim3(grid), dim3(kSelThreads), 0, s, a);
+  hipLaunchKernelGGL(select_find1, dim3(Hkv), dim3(kSelThreads), 0, s, a);
   hipLaunchKernelGGL(select_s2, dim3(grid), dim3(kSelThreads), 0, s, a);
   hipLaunchKernelGGL(select_s3, dim3(Hkv), dim3(kS3Threads), 0, s, a);
   hipLaunchKernelGGL(select_s4, dim3(grid), dim3(kSelThreads), 0, s, a);
