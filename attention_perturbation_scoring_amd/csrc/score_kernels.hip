@@ -434,22 +434,20 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
     Sxf += (w == wstar) ? sm_Sx[w][r] * f : sm_S[w][r] * f;
   }
   const float myf = (m > -INFINITY) ? ex2(m - Mf) : 0.f;
-  __syncthreads();  // every wave is done with its V tile; reuse LDS as a float buffer
-  float* red = reinterpret_cast<float*>(smem_raw);
-  for (int w = 0; w < NWV; ++w) {
-    if (wid == w) {
+  __syncthreads();  // every wave is done with its V tile; reuse LDS as float slabs
+  // each wave stores its scaled accumulators in a slab of its own (row stride
+  // DP + 1 floats, so the 32 rows a store touches fall in distinct banks); one
+  // barrier; then the slabs are summed in wave order straight into the partials
+  constexpr int SP = DP + 1;
+  float* slab = reinterpret_cast<float*>(smem_raw) + (size_t)wid * kRows * SP;
 #pragma unroll
-      for (int b = 0; b < DB; ++b)
+  for (int b = 0; b < DB; ++b)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int dd = 32 * b + 8 * (v >> 2) + 4 * hh + (v & 3);
-          const float x = acc[b][v] * myf;
-          float* dst = red + r * DP + dd;
-          *dst = (w == 0) ? x : *dst + x;
-        }
+    for (int v = 0; v < 16; ++v) {
+      const int dd = 32 * b + 8 * (v >> 2) + 4 * hh + (v & 3);
+      slab[r * SP + dd] = acc[b][v] * myf;
     }
-    __syncthreads();
-  }
+  __syncthreads();
   const size_t pb = ((size_t)g * a.splits + s) * kRows;
   if (tid < kRows) {
     a.part.m2[pb + r] = Mf;
@@ -458,7 +456,14 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
     a.part.jstar[pb + r] = jbest;
     a.part.bad[pb + r] = badf;
   }
-  for (int i = tid; i < a.M * DP; i += NT) a.part.a[pb * DP + i] = red[i];
+  const float* slabs = reinterpret_cast<const float*>(smem_raw);
+  for (int i = tid; i < a.M * DP; i += NT) {
+    const int rr = i / DP, dd = i - rr * DP;
+    float x = slabs[rr * SP + dd];
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) x += slabs[(size_t)w * kRows * SP + rr * SP + dd];
+    a.part.a[pb * DP + i] = x;
+  }
 }
 
 // ----------------------------------------------------------------- merge --
@@ -1183,7 +1188,7 @@ void carve_scratch(void* base, int Hkv, int splits, int DP, Partials* p, RowStat
 
 template <int DP, bool FULLD>
 static hipError_t launch_score_dp(void* ctx, const ScoreArgs& a, hipStream_t s) {
-  const size_t red = (size_t)kRows * DP * 4;
+  const size_t red = (size_t)p1_waves(DP) * kRows * (DP + 1) * 4;   // the combine's slabs
   const size_t lds1 = pass1_lds_bytes<DP>() > red ? pass1_lds_bytes<DP>() : red;
   const size_t lds2 = pass2_lds_bytes<DP>();
   static bool attr_done = false;
