@@ -178,19 +178,28 @@ __device__ __forceinline__ void wait_vmem_below() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// LDS layout of a V tile: row-major rows of CHP 16-byte chunks; on rows with
-// bit 2 set the chunk index is XOR-ed with 4 (a 64-byte shift), so the two
-// lane halves of a transposed read -- rows tau and tau + 4 -- hit disjoint
-// banks, while every lane's address stays a fixed base plus a per-row constant.
+// LDS layout of a V tile: row-major rows of CHP 16-byte chunks, the chunk
+// index XOR-ed with 4 * (row % 4) (kept inside the row): the four rows one
+// transposed read gathers from land in distinct 64-byte bank ranges.
 template <int DP>
 struct VLayout {
   static constexpr int CHP = RowLayout<DP>::CHP;
   static constexpr int ROWB = RowLayout<DP>::ROWB;
-  static constexpr int SW = CHP >= 8 ? 4 : 0;
+  __device__ __forceinline__ static int sw(int row) { return ((row & 3) << 2) & (CHP - 1); }
   __device__ __forceinline__ static int off(int row, int chunk) {
-    return row * ROWB + ((chunk ^ (((row >> 2) & 1) * SW)) << 4);
+    return row * ROWB + ((chunk ^ sw(row)) << 4);
   }
 };
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 (checked on gfx950): within each group of 16 lanes, lane i
+// receives, as element e (e < 4), the 16-bit element i % 4 of the 8 bytes that
+// lane 4e + i / 4 of its group addresses.
+__device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) unsigned char*)p));
+}
 
 // V tile of tokens [t0, t0+32) straight into an LDS slot (no registers), in
 // VLayout order: instruction i fills bytes [1024 i, 1024 i + 1024) of the slot,
@@ -205,7 +214,7 @@ __device__ __forceinline__ void dma_v_tile(const u16* vg, int64_t t0, int64_t en
   for (int i = 0; i < L::CHP / 2; ++i) {
     const int P = 64 * i + lane;
     const int row = P / L::CHP, pc = P % L::CHP;
-    int c = pc ^ (((row >> 2) & 1) * L::SW);
+    int c = pc ^ L::sw(row);
     int64_t tok = t0 + row;
     if (tok >= end) tok = t0;
     if (c * 8 >= d) c = 0;
@@ -381,17 +390,23 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
     wave_sync_lds();
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
+      // V^T operand of lane (r, hh): column 32 b + r, tokens 16 kc + 8 (e/4) +
+      // 4 hh + e%4.  Two transposed reads per block: lane 4e' + q of each
+      // 16-lane group addresses token row 16 kc + 8 half + 4 hh + e' and the
+      // 8 bytes holding columns 32 b + 16 (group % 2) + 4 q .. + 3.
+      const int gsub = (lane >> 4) & 1, e4 = (lane >> 2) & 3, q = lane & 3;
       bf16x8 va[DB];
 #pragma unroll
       for (int b = 0; b < DB; ++b) {
-        // rows 16 kc + 8 (e/4) + 4 hh + e%4: bit 2 of every such row is hh, so
-        // the lane's address is one base plus a compile-time row offset
-        const unsigned char* vb = vs + VLayout<DP>::off(4 * hh, 4 * b + (r >> 3)) + (r & 7) * 2;
+        s16x4 part[2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tl = 16 * kc + 8 * (e >> 2) + (e & 3);
-          va[b][e] = *reinterpret_cast<const __bf16*>(vb + tl * L::ROWB);
+        for (int half = 0; half < 2; ++half) {
+          const int row = 16 * kc + 8 * half + 4 * hh + e4;
+          const int chunk = 4 * b + 2 * gsub + (q >> 1);
+          part[half] = lds_read_tr16(vs + VLayout<DP>::off(row, chunk) + 8 * (q & 1));
         }
+        va[b] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3,
+                                                                   4, 5, 6, 7));
       }
       // the DB accumulators are independent: issue them back to back
 #pragma unroll
