@@ -94,6 +94,10 @@ constexpr int kThreads = 64 * kWaves;
 #ifndef DROPKV_P2_OVERLAP
 #define DROPKV_P2_OVERLAP 0
 #endif
+#ifndef DROPKV_ATTN_TILES
+#define DROPKV_ATTN_TILES 1
+#endif
+constexpr int kAttnTiles = DROPKV_ATTN_TILES;   // K tiles loaded per iteration (attention-only mode)
 #ifndef DROPKV_P1_WG_WAVES
 #define DROPKV_P1_WG_WAVES 4
 #endif

@@ -917,7 +917,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
 // recomputes the logits, adds p over the rows of each token, divides by G and
 // pools / protects like pass 2.  Only K is read, twice.
 template <int DP, bool FULLD>
-__global__ __launch_bounds__(kThreads, (DP <= 128 ? 4 : 2)) void attn_pass1_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kThreads, (DP <= 128 ? (kAttnTiles > 1 ? 3 : 4) : 2)) void attn_pass1_kernel(ScoreArgs a) {
   constexpr int NC = DP / 16;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ float sm_m[kWaves][kRows], sm_S[kWaves][kRows];
@@ -939,17 +939,29 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? 4 : 2)) void attn_pass1_kern
 
   // S^T = K Q^T as in pass 1: lane l owns row l%32 and 16 of the tile's tokens
   float m = -INFINITY, S = 0.f, chk = 0.f;
-  bf16x8 kk[NC];
-  for (int t = wid; t < ntiles; t += kWaves) {
+  // kAttnTiles tiles per iteration: all their loads are issued before the first
+  // is consumed (more bytes in flight per wave); the tiles are still visited in
+  // the order t, t + 4, t + 8, ... so the result does not depend on it
+  for (int t0 = wid; t0 < ntiles; t0 += kWaves * kAttnTiles) {
+    bf16x8 kk[kAttnTiles][NC];
+#pragma unroll
+    for (int u = 0; u < kAttnTiles; ++u) {
+      const int t = t0 + u * kWaves;
+      const int64_t j0 = jbeg + (int64_t)t * kTile;
+      if (t < ntiles) load_k_tile<NC, FULLD>(kg, j0 + r, j0 + r < jend, j0 + kTile > jend, hh, d, kk[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kAttnTiles; ++u) {
+    const int t = t0 + u * kWaves;
+    if (t >= ntiles) break;
     const int64_t j0 = jbeg + (int64_t)t * kTile;
-    load_k_tile<NC, FULLD>(kg, j0 + r, j0 + r < jend, j0 + kTile > jend, hh, d, kk);
     f32x16 st, st1;
 #pragma unroll
     for (int v = 0; v < 16; ++v) { st[v] = 0.f; st1[v] = 0.f; }
 #pragma unroll
     for (int c = 0; c < NC; c += 2) {
-      st = mfma32(kk[c], lds8<DP>(qs, r, 2 * c + hh), st);
-      if (c + 1 < NC) st1 = mfma32(kk[c + 1], lds8<DP>(qs, r, 2 * c + 2 + hh), st1);
+      st = mfma32(kk[u][c], lds8<DP>(qs, r, 2 * c + hh), st);
+      if (c + 1 < NC) st1 = mfma32(kk[u][c + 1], lds8<DP>(qs, r, 2 * c + 2 + hh), st1);
     }
     const bool interior = (j0 + kTile <= jend) && (j0 + kTile - 1 <= all_see);
     float s2[16];
@@ -973,6 +985,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? 4 : 2)) void attn_pass1_kern
       ts += __shfl_xor(ts, 32);
       S = S * alpha + ts;
       m = mn;
+    }
     }
   }
   int bad = (chk == 0.f) ? 0 : 1;
@@ -1005,7 +1018,7 @@ constexpr size_t attn_pass2_lds_bytes() {
 }
 
 template <int DP, bool FULLD>
-__global__ __launch_bounds__(kThreads, (DP <= 128 ? 4 : 2)) void attn_pass2_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kThreads, (DP <= 128 ? (kAttnTiles > 1 ? 3 : 4) : 2)) void attn_pass2_kernel(ScoreArgs a) {
   constexpr int NC = DP / 16;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ float lse_s[kRows];
@@ -1063,20 +1076,30 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? 4 : 2)) void attn_pass2_kern
   __syncthreads();
   const float invG = 1.f / (float)a.G;
 
-  // S = Q K^T as in pass 2: lane l owns token l%32 and 16 rows
-  bf16x8 kB[NC];
-  for (int t = wid; t < next; t += kWaves) {
+  // S = Q K^T as in pass 2: lane l owns token l%32 and 16 rows; kAttnTiles
+  // tiles' loads are issued before the first is consumed
+  for (int t0 = wid; t0 < next; t0 += kWaves * kAttnTiles) {
+    bf16x8 kB[kAttnTiles][NC];
+#pragma unroll
+    for (int u = 0; u < kAttnTiles; ++u) {
+      const int t = t0 + u * kWaves;
+      const int64_t j0 = e0 + (int64_t)t * kTile;
+      if (t < next) load_k_tile<NC, FULLD>(kg, j0 + r, j0 + r < e1, j0 + kTile > e1, hh, d, kB[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kAttnTiles; ++u) {
+    const int t = t0 + u * kWaves;
+    if (t >= next) break;
     const int64_t j0 = e0 + (int64_t)t * kTile;
     const int64_t tok = j0 + r;
     const bool tok_ok = tok < e1;
-    load_k_tile<NC, FULLD>(kg, tok, tok_ok, j0 + kTile > e1, hh, d, kB);
     f32x16 sacc, sacc1;
 #pragma unroll
     for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; sacc1[v] = 0.f; }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      if (c & 1) sacc1 = mfma32(lds8<DP>(qs, r, 2 * c + hh), kB[c], sacc1);
-      else sacc = mfma32(lds8<DP>(qs, r, 2 * c + hh), kB[c], sacc);
+      if (c & 1) sacc1 = mfma32(lds8<DP>(qs, r, 2 * c + hh), kB[u][c], sacc1);
+      else sacc = mfma32(lds8<DP>(qs, r, 2 * c + hh), kB[u][c], sacc);
     }
     const bool interior = (j0 + kTile <= e1) && (j0 + kTile - 1 <= all_see);
     float sum = 0.f;
@@ -1098,6 +1121,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? 4 : 2)) void attn_pass2_kern
     }
     sum += __shfl_xor(sum, 32);
     if (hh == 0 && tok_ok) rawbuf[tok - e0] = sum * invG;
+    }
   }
   __syncthreads();
   for (int64_t j = c0 + tid; j < c1; j += kThreads) {
