@@ -156,7 +156,7 @@ int score_common(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
   if (pool < 1 || pool % 2 == 0 || pool > 129) return DROPKV_EINVAL;
   if (d < 8 || d % 8 != 0 || d > 256) return DROPKV_EINVAL;
   const int G = Hq / Hkv;
-  if ((int64_t)G * w > kRows) return DROPKV_EINVAL;
+  if ((int64_t)G * w > (int64_t)kRows * kMaxRowGroups) return DROPKV_EINVAL;
   DeviceGuard guard(c->device);
   if (!guard.ok) return DROPKV_EDEVICE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -165,13 +165,16 @@ int score_common(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
   a.q = q_win; a.k = k_cache; a.v = v_cache; a.scores = scores;
   a.n = n; a.w = w; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.G = G; a.M = G * w; a.pool = pool;
   a.DP = (d + 31) / 32 * 32;
-  a.splits = plan_splits(n, Hkv, &a.split_len, attention_only ? kTargetWGAttn : kTargetWG1);
+  a.R = (a.M + kRows - 1) / kRows;
+  if (!attention_only && !score_fits(a.DP, a.R)) return DROPKV_EINVAL;
+  // the first pass runs per (KV head, row group): plan its splits over all of them
+  a.splits = plan_splits(n, Hkv * a.R, &a.split_len, attention_only ? kTargetWGAttn : kTargetWG1);
   a.chunks2 = plan_chunks2(n, Hkv, &a.chunk2_len);
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
   a.latch = c->latch;
   a.out_a = out_a;
   a.out_lse = out_lse;
-  const size_t need = score_scratch_bytes(Hkv, a.splits, a.DP);
+  const size_t need = score_scratch_bytes(Hkv * a.R, a.splits, a.DP);
   if (need > c->scratch_bytes) {
     if (c->scratch) {
       (void)hipStreamSynchronize(s);
@@ -184,7 +187,7 @@ int score_common(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
     if (e != hipSuccess) { c->scratch = nullptr; return DROPKV_ENOMEM; }
     c->scratch_bytes = need;
   }
-  carve_scratch(c->scratch, Hkv, a.splits, a.DP, &a.part, &a.rs);
+  carve_scratch(c->scratch, Hkv * a.R, a.splits, a.DP, &a.part, &a.rs);
   return to_status(attention_only ? launch_score_attention(c, a, s) : launch_score(c, a, s));
 }
 

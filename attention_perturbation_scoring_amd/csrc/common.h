@@ -75,7 +75,8 @@ enum : uint32_t {
   LATCH_TIMEOUT = 8u,   // a workgroup barrier of the single-launch selection gave up waiting
 };
 
-constexpr int kRows = 32;        // window-query rows per KV head handled by one MFMA tile (G*w <= 32)
+constexpr int kRows = 32;        // window-query rows of one row group (one MFMA tile)
+constexpr int kMaxRowGroups = 4; // G*w <= 128 rows per KV head
 constexpr int kTile = 32;        // tokens per MFMA tile
 constexpr int kWaves = 4;        // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
@@ -152,6 +153,7 @@ struct ScoreArgs {
   float* scores;
   int64_t n;
   int w, Hq, Hkv, d, G, M, pool, DP;
+  int R;                // 32-row groups per KV head: ceil(M / 32), at most kMaxRowGroups
   int splits;
   int64_t split_len;
   int chunks2;          // pass-2 workgroups per head
@@ -207,6 +209,7 @@ size_t score_scratch_bytes(int Hkv, int splits, int DP);
 void carve_scratch(void* base, int Hkv, int splits, int DP, Partials* p, RowState* rs);
 int plan_splits(int64_t n, int Hkv, int64_t* split_len, int target = kTargetWG1);
 hipError_t launch_score_attention(void* ctx, const ScoreArgs& a, hipStream_t s);
+bool score_fits(int DP, int R);
 constexpr int kTargetWGAttn = 1024;   // attention-only pass A: four small workgroups per CU
 int plan_chunks2(int64_t n, int Hkv, int64_t* chunk_len);
 

@@ -235,22 +235,24 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
-  const int g = blockIdx.x / a.splits, s = blockIdx.x % a.splits;
+  // a virtual head is one 32-row group of one KV head
+  const int hv = blockIdx.x / a.splits, s = blockIdx.x % a.splits;
+  const int g = hv / a.R, row0 = kRows * (hv % a.R);
   const int64_t jbeg = (int64_t)s * a.split_len;
   const int64_t jend = min(a.n, jbeg + a.split_len);
   const int ntiles = (int)((jend - jbeg + kTile - 1) / kTile);
   const int d = a.d;
   const u16* kg = a.k + (size_t)g * a.n * d;
   const u16* vg = a.v + (size_t)g * a.n * d;
-  const bool row_ok = r < a.M;
-  const int64_t causal = row_ok ? a.n - a.w + (r % a.w) : -1;
+  const bool row_ok = row0 + r < a.M;
+  const int64_t causal = row_ok ? a.n - a.w + ((row0 + r) % a.w) : -1;
   const int64_t all_see = a.n - a.w;   // every window query sees keys 0..n-w
   unsigned char* qs = smem_raw;                                  // Q rows of the group
   unsigned char* vslot0 =   // this wave's V tile(s)
       smem_raw + (size_t)kRows * L::ROWB * (1 + (kP1Overlap ? 2 : 1) * wid);
   unsigned char* vslot1 = vslot0 + (size_t)kRows * L::ROWB;
 
-  stage_rows<DP, NT>(qs, a.q + (size_t)g * a.M * d, a.M, d, d);
+  stage_rows<DP, NT>(qs, a.q + ((size_t)g * a.M + row0) * d, min(kRows, a.M - row0), d, d);
   __syncthreads();
 
   float m = -INFINITY, S = 0.f, Sx = 0.f, chk = 0.f;
@@ -463,7 +465,7 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
       slab[r * SP + dd] = acc[b][v] * myf;
     }
   __syncthreads();
-  const size_t pb = ((size_t)g * a.splits + s) * kRows;
+  const size_t pb = ((size_t)hv * a.splits + s) * kRows;
   if (tid < kRows) {
     a.part.m2[pb + r] = Mf;
     a.part.S[pb + r] = Sf;
@@ -472,7 +474,7 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
     a.part.bad[pb + r] = badf;
   }
   const float* slabs = reinterpret_cast<const float*>(smem_raw);
-  for (int i = tid; i < a.M * DP; i += NT) {
+  for (int i = tid; i < kRows * DP; i += NT) {   // the group's 32 rows (padding rows are ignored later)
     const int rr = i / DP, dd = i - rr * DP;
     float x = slabs[rr * SP + dd];
 #pragma unroll
@@ -606,9 +608,12 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
   __shared__ float rsx[16];
   __shared__ float tmp[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int g = blockIdx.x / kRows, r = blockIdx.x % kRows;
-  const size_t ro = (size_t)g * kRows + r;
-  if (r >= a.M) {  // padded rows: zero operands so pass 2's MFMA rows stay inert
+  // virtual head hv = (KV head g, row group); r is the row within the group and
+  // rg_row the window query row within the KV head
+  const int hv = blockIdx.x / kRows, r = blockIdx.x % kRows;
+  const int g = hv / a.R, rg_row = kRows * (hv % a.R) + r;
+  const size_t ro = (size_t)hv * kRows + r;
+  if (rg_row >= a.M) {  // padded rows: zero operands so pass 2's MFMA rows stay inert
     for (int dd = tid; dd < DP; dd += kThreads) {
       a.rs.a_hi[ro * DP + dd] = 0;
       a.rs.a_lo[ro * DP + dd] = 0;
@@ -620,7 +625,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
     return;
   }
   const int S = a.splits;
-  const size_t base = (size_t)g * S * kRows;
+  const size_t base = (size_t)hv * S * kRows;
 
   // Issue the first PF partial-a loads of this thread (they need no weights yet)
   // together with every split's statistics: one memory round trip.
@@ -715,7 +720,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
     a.rs.a_hi[ro * DP + tid] = __builtin_bit_cast(u16, hi);
     a.rs.a_lo[ro * DP + tid] = __builtin_bit_cast(u16, lo);
     // row r of head g is window query (g * G + r / w, r % w): [Hq][w][d] order
-    if (a.out_a && tid < a.d) a.out_a[((size_t)g * a.M + r) * a.d + tid] = avv;
+    if (a.out_a && tid < a.d) a.out_a[((size_t)g * a.M + rg_row) * a.d + tid] = avv;
     if (tid < a.d && jst >= 0) {
       const float df = avv - vstar;
       dist = df * df;
@@ -734,12 +739,12 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
   const bool singular = !nonfin && !(Sx > 0x1p-53f);
   const bool fix = !nonfin && !singular && Sx < kFixupThreshold;
   float cstar = (nonfin || singular) ? 0.f : dist / (Sx * Sx);
-  if (fix) cstar = exclusion_term<DP>(a, g, r, jst, M, Sf, red, rsx, tmp);
+  if (fix) cstar = exclusion_term<DP>(a, g, rg_row, jst, M, Sf, red, rsx, tmp);
   if (tid == 0) {
     a.rs.m2[ro] = M;
     a.rs.S[ro] = Sf;
     a.rs.lse2[ro] = M + log2f(Sf);
-    if (a.out_lse) a.out_lse[(size_t)g * a.M + r] = (M + log2f(Sf)) * 0.6931471805599453f;
+    if (a.out_lse) a.out_lse[(size_t)g * a.M + rg_row] = (M + log2f(Sf)) * 0.6931471805599453f;
     a.rs.an2[ro] = an2;
     a.rs.jstar[ro] = jst;
     a.rs.fix[ro] = fix ? 1 : 0;
@@ -757,9 +762,16 @@ constexpr int kMaxRadius = 64;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// LDS of pass 2 for R row groups: per group the Q, a_hi and a_lo rows, then per
+// group and row lse, ||a||^2, the arg-max token and its term, then the chunk's
+// raw scores with the pooling halo.
 template <int DP>
-constexpr size_t pass2_lds_bytes() {
-  return (size_t)3 * kRows * RowLayout<DP>::ROWB + 2 * kRows * 4 +
+constexpr size_t pass2_group_bytes() {
+  return (size_t)3 * kRows * RowLayout<DP>::ROWB;
+}
+template <int DP>
+constexpr size_t pass2_lds_bytes(int R) {
+  return (size_t)R * pass2_group_bytes<DP>() + (size_t)R * 4 * kRows * 4 +
          (size_t)(kChunk2 + 2 * kMaxRadius + kTile) * 4;
 }
 
@@ -768,12 +780,12 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
   using L = RowLayout<DP>;
   constexpr int NC = DP / 16;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  unsigned char* qs = smem_raw;                       // Q rows
-  unsigned char* hs = qs + kRows * L::ROWB;           // a (bf16 high part) rows
-  unsigned char* ls = hs + kRows * L::ROWB;           // a (bf16 remainder) rows
-  float* lse_s = reinterpret_cast<float*>(ls + kRows * L::ROWB);
-  float* an2_s = lse_s + kRows;
-  float* rawbuf = an2_s + kRows;
+  const int R = a.R;
+  float* lse_s = reinterpret_cast<float*>(smem_raw + (size_t)R * pass2_group_bytes<DP>());
+  float* an2_s = lse_s + R * kRows;
+  int* js_s = reinterpret_cast<int*>(an2_s + R * kRows);   // arg-max token per row
+  float* cs_s = reinterpret_cast<float*>(js_s + R * kRows);  // and its precomputed term
+  float* rawbuf = cs_s + R * kRows;
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
   const int64_t n = a.n;
@@ -785,19 +797,23 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
   const int d = a.d;
   const u16* kg = a.k + (size_t)g * n * d;
   const u16* vg = a.v + (size_t)g * n * d;
-  const size_t ro0 = (size_t)g * kRows;
   const int64_t all_see = n - a.w;
 
-  stage_rows<DP>(qs, a.q + (size_t)g * a.M * d, a.M, d, d);
-  stage_rows<DP>(hs, a.rs.a_hi + ro0 * DP, kRows, DP, DP);
-  stage_rows<DP>(ls, a.rs.a_lo + ro0 * DP, kRows, DP, DP);
-  // rows >= M carry lse = +inf (set by the merge): their p and contribution are 0
-  if (tid < kRows) {
-    lse_s[tid] = a.rs.lse2[ro0 + tid];
-    an2_s[tid] = a.rs.an2[ro0 + tid];
+  for (int rg = 0; rg < R; ++rg) {
+    unsigned char* qs = smem_raw + (size_t)rg * pass2_group_bytes<DP>();
+    const size_t ro0 = ((size_t)g * R + rg) * kRows;   // this group's row state
+    const int row0 = kRows * rg;
+    stage_rows<DP>(qs, a.q + ((size_t)g * a.M + row0) * d, min(kRows, a.M - row0), d, d);
+    stage_rows<DP>(qs + kRows * L::ROWB, a.rs.a_hi + ro0 * DP, kRows, DP, DP);
+    stage_rows<DP>(qs + 2 * kRows * L::ROWB, a.rs.a_lo + ro0 * DP, kRows, DP, DP);
+    // rows >= M carry lse = +inf (set by the merge): their p and contribution are 0
+    if (tid < kRows) {
+      lse_s[rg * kRows + tid] = a.rs.lse2[ro0 + tid];
+      an2_s[rg * kRows + tid] = a.rs.an2[ro0 + tid];
+      js_s[rg * kRows + tid] = a.rs.jstar[ro0 + tid];
+      cs_s[rg * kRows + tid] = a.rs.cstar[ro0 + tid];
+    }
   }
-  const int jsl = (lane < kRows) ? a.rs.jstar[ro0 + lane] : -1;
-  const float csl = (lane < kRows) ? a.rs.cstar[ro0 + lane] : 0.f;
   const float invG = 1.f / (float)a.G;
   uint32_t flags = 0;
   __syncthreads();
@@ -809,7 +825,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
   // Each wave walks its tiles in order; the next tile's K and V are loaded into
   // the same registers as soon as the matrix products have consumed them, so
   // they fly during this tile's vector work.  Three workgroups per CU cover the
-  // rest of the latency.
+  // rest of the latency.  Every row group of the head uses the same K/V tile.
   bf16x8 kB[NC], vB[NC];
   if (kP2Overlap && wid < next) issue(wid, kB, vB);
   for (int t = wid; t < next; t += kWaves) {
@@ -817,20 +833,6 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
     const int64_t tok = j0 + r;
     const bool tok_ok = tok < e1;
     if (!kP2Overlap) issue(t, kB, vB);
-    // four independent accumulation chains (logits split in two, a.v split
-    // into its hi and lo parts) keep the matrix core busy
-    f32x16 sacc, sacc1, av, av1;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; sacc1[v] = 0.f; av[v] = 0.f; av1[v] = 0.f; }
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (c & 1) sacc1 = mfma32(lds8<DP>(qs, r, 2 * c + hh), kB[c], sacc1);
-      else sacc = mfma32(lds8<DP>(qs, r, 2 * c + hh), kB[c], sacc);
-      av = mfma32(lds8<DP>(hs, r, 2 * c + hh), vB[c], av);
-      av1 = mfma32(lds8<DP>(ls, r, 2 * c + hh), vB[c], av1);
-    }
-#pragma unroll
-    for (int v = 0; v < 16; ++v) { sacc[v] += sacc1[v]; av[v] += av1[v]; }
     float vn2 = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -841,58 +843,81 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
       }
     }
     vn2 += __shfl_xor(vn2, 32);
-    if (kP2Overlap && t + kWaves < next) issue(t + kWaves, kB, vB);
-    float cc[16];
-    float ovf = 0.f;   // becomes NaN if an expansion term overflowed fp32
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      // this lane's rows 8*q4 + 4*hh + 0..3
-      const float4 l4 = *reinterpret_cast<const float4*>(lse_s + 8 * q4 + 4 * hh);
-      const float4 n4 = *reinterpret_cast<const float4*>(an2_s + 8 * q4 + 4 * hh);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float nv[4] = {n4.x, n4.y, n4.z, n4.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int v = 4 * q4 + i;
-        const float p = ex2(sacc[v] * a.scale_log2 - lv[i]);
-        const float odds = p * __builtin_amdgcn_rcpf(1.f - p);
-        const float d0 = nv[i] - 2.f * av[v] + vn2;
-        ovf = fmaf(d0, 0.f, ovf);
-        cc[v] = odds * odds * fmaxf(d0, 0.f);
-      }
-    }
-    if (tok_ok && !(ovf == 0.f)) flags |= LATCH_RANGE;
     const bool interior = (j0 + kTile <= e1) && (j0 + kTile - 1 <= all_see);
-    if (!interior) {
-      const int itok = (int)tok;
+    float tsum = 0.f;   // this token's sum over every row of the head
+#pragma unroll 1
+    for (int rg = 0; rg < R; ++rg) {
+      const unsigned char* qs = smem_raw + (size_t)rg * pass2_group_bytes<DP>();
+      const unsigned char* hs = qs + kRows * L::ROWB;
+      const unsigned char* ls = hs + kRows * L::ROWB;
+      // four independent accumulation chains (logits split in two, a.v split
+      // into its hi and lo parts) keep the matrix core busy
+      f32x16 sacc, sacc1, av, av1;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rv = 8 * (v >> 2) + 4 * hh + (v & 3);
-        const int lim = rv < a.M ? (int)(n - a.w + (rv % a.w)) : -1;
-        cc[v] = (tok_ok && itok <= lim) ? cc[v] : 0.f;
+      for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; sacc1[v] = 0.f; av[v] = 0.f; av1[v] = 0.f; }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        if (c & 1) sacc1 = mfma32(lds8<DP>(qs, r, 2 * c + hh), kB[c], sacc1);
+        else sacc = mfma32(lds8<DP>(qs, r, 2 * c + hh), kB[c], sacc);
+        av = mfma32(lds8<DP>(hs, r, 2 * c + hh), vB[c], av);
+        av1 = mfma32(lds8<DP>(ls, r, 2 * c + hh), vB[c], av1);
       }
-    }
-    // the arg-max token of a row takes the value computed by the merge instead
-    const bool hit = (jsl >= j0) && (jsl < j0 + kTile);
-    uint64_t bal = __ballot(hit);
-    while (bal) {
-      const int rr = __ffsll((unsigned long long)bal) - 1;
-      bal &= bal - 1;
-      const int js = __shfl(jsl, rr);
-      const float cs = __shfl(csl, rr);
-      const int Ln = (int)(js - j0) + 32 * ((rr >> 2) & 1);
-      const int vr = 4 * (rr >> 3) + (rr & 3);
-      if (lane == Ln && tok_ok) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (v == vr) cc[v] = cs;
+      for (int v = 0; v < 16; ++v) { sacc[v] += sacc1[v]; av[v] += av1[v]; }
+      float cc[16];
+      float ovf = 0.f;   // becomes NaN if an expansion term overflowed fp32
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        // this lane's rows 8*q4 + 4*hh + 0..3 of the group
+        const float4 l4 = *reinterpret_cast<const float4*>(lse_s + rg * kRows + 8 * q4 + 4 * hh);
+        const float4 n4 = *reinterpret_cast<const float4*>(an2_s + rg * kRows + 8 * q4 + 4 * hh);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float nv[4] = {n4.x, n4.y, n4.z, n4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int v = 4 * q4 + i;
+          const float p = ex2(sacc[v] * a.scale_log2 - lv[i]);
+          const float odds = p * __builtin_amdgcn_rcpf(1.f - p);
+          const float d0 = nv[i] - 2.f * av[v] + vn2;
+          ovf = fmaf(d0, 0.f, ovf);
+          cc[v] = odds * odds * fmaxf(d0, 0.f);
+        }
       }
-    }
-    float sum = 0.f;
+      if (tok_ok && !(ovf == 0.f)) flags |= LATCH_RANGE;
+      if (!interior) {
+        const int itok = (int)tok;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) sum += cc[v];
-    sum += __shfl_xor(sum, 32);
-    const float raw = sum * invG;
+        for (int v = 0; v < 16; ++v) {
+          const int rv = kRows * rg + 8 * (v >> 2) + 4 * hh + (v & 3);   // row within the head
+          const int lim = rv < a.M ? (int)(n - a.w + (rv % a.w)) : -1;
+          cc[v] = (tok_ok && itok <= lim) ? cc[v] : 0.f;
+        }
+      }
+      // the arg-max token of a row takes the value computed by the merge instead
+      const int jsl = (lane < kRows) ? js_s[rg * kRows + lane] : -1;
+      const bool hit = (jsl >= j0) && (jsl < j0 + kTile);
+      uint64_t bal = __ballot(hit);
+      while (bal) {
+        const int rr = __ffsll((unsigned long long)bal) - 1;
+        bal &= bal - 1;
+        const int js = js_s[rg * kRows + rr];
+        const float cs = cs_s[rg * kRows + rr];
+        const int Ln = (int)(js - j0) + 32 * ((rr >> 2) & 1);
+        const int vr = 4 * (rr >> 3) + (rr & 3);
+        if (lane == Ln && tok_ok) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (v == vr) cc[v] = cs;
+        }
+      }
+      float sum = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sum += cc[v];
+      sum += __shfl_xor(sum, 32);
+      tsum += sum;
+    }
+    if (kP2Overlap && t + kWaves < next) issue(t + kWaves, kB, vB);
+    const float raw = tsum * invG;
     // inputs were checked finite by pass 1 / merge, so an inf or NaN here is an
     // fp32 overflow of a score or of its terms
     if (tok_ok && !(raw <= FLT_MAX)) flags |= LATCH_RANGE;
@@ -924,17 +949,18 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? (kAttnTiles > 1 ? 3 : 4) : 2
   __shared__ int sm_bad[kWaves][kRows];
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
-  const int g = blockIdx.x / a.splits, s = blockIdx.x % a.splits;
+  const int hv = blockIdx.x / a.splits, s = blockIdx.x % a.splits;   // (KV head, row group)
+  const int g = hv / a.R, row0 = kRows * (hv % a.R);
   const int64_t jbeg = (int64_t)s * a.split_len;
   const int64_t jend = min(a.n, jbeg + a.split_len);
   const int ntiles = (int)((jend - jbeg + kTile - 1) / kTile);
   const int d = a.d;
   const u16* kg = a.k + (size_t)g * a.n * d;
-  const bool row_ok = r < a.M;
-  const int64_t causal = row_ok ? a.n - a.w + (r % a.w) : -1;
+  const bool row_ok = row0 + r < a.M;
+  const int64_t causal = row_ok ? a.n - a.w + ((row0 + r) % a.w) : -1;
   const int64_t all_see = a.n - a.w;
   unsigned char* qs = smem_raw;
-  stage_rows<DP>(qs, a.q + (size_t)g * a.M * d, a.M, d, d);
+  stage_rows<DP>(qs, a.q + ((size_t)g * a.M + row0) * d, min(kRows, a.M - row0), d, d);
   __syncthreads();
 
   // S^T = K Q^T as in pass 1: lane l owns row l%32 and 16 of the tile's tokens
@@ -1005,7 +1031,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? (kAttnTiles > 1 ? 3 : 4) : 2
 #pragma unroll
     for (int w = 0; w < kWaves; ++w)
       Sf += (sm_m[w][tid] > -INFINITY) ? sm_S[w][tid] * ex2(sm_m[w][tid] - Mf) : 0.f;
-    const size_t pb = ((size_t)g * a.splits + s) * kRows + tid;
+    const size_t pb = ((size_t)hv * a.splits + s) * kRows + tid;
     a.part.m2[pb] = Mf;
     a.part.S[pb] = Sf;
     a.part.bad[pb] = badf;
@@ -1013,17 +1039,17 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? (kAttnTiles > 1 ? 3 : 4) : 2
 }
 
 template <int DP>
-constexpr size_t attn_pass2_lds_bytes() {
-  return (size_t)kRows * RowLayout<DP>::ROWB + (size_t)(kChunk2 + 2 * kMaxRadius + kTile) * 4;
+constexpr size_t attn_pass2_lds_bytes(int R) {
+  return (size_t)R * kRows * RowLayout<DP>::ROWB + (size_t)(kChunk2 + 2 * kMaxRadius + kTile) * 4;
 }
 
 template <int DP, bool FULLD>
 __global__ __launch_bounds__(kThreads, (DP <= 128 ? (kAttnTiles > 1 ? 3 : 4) : 2)) void attn_pass2_kernel(ScoreArgs a) {
   constexpr int NC = DP / 16;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  __shared__ float lse_s[kRows];
-  unsigned char* qs = smem_raw;
-  float* rawbuf = reinterpret_cast<float*>(qs + kRows * RowLayout<DP>::ROWB);
+  __shared__ float lse_s[kMaxRowGroups * kRows];
+  const int R = a.R;
+  float* rawbuf = reinterpret_cast<float*>(smem_raw + (size_t)R * kRows * RowLayout<DP>::ROWB);
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
   const int64_t n = a.n;
@@ -1036,11 +1062,13 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? (kAttnTiles > 1 ? 3 : 4) : 2
   const u16* kg = a.k + (size_t)g * n * d;
   const int64_t all_see = n - a.w;
 
-  stage_rows<DP>(qs, a.q + (size_t)g * a.M * d, a.M, d, d);
-  {   // each row's log2-sum-exp from the split states: 8 threads per row take
+  for (int rg = 0; rg < R; ++rg)
+    stage_rows<DP>(smem_raw + (size_t)rg * kRows * RowLayout<DP>::ROWB,
+                   a.q + ((size_t)g * a.M + kRows * rg) * d, min(kRows, a.M - kRows * rg), d, d);
+  for (int rg = 0; rg < R; ++rg) {   // each row's log2-sum-exp from the split states: 8 threads per row take
       // every 8th split (online max/sum), then a fixed shuffle tree combines them
     const int row = tid >> 3, part = tid & 7;
-    const size_t base = (size_t)g * a.splits * kRows + row;
+    const size_t base = ((size_t)g * R + rg) * a.splits * kRows + row;
     float M = -INFINITY, Ssum = 0.f;
     int bad = 0;
 #pragma unroll 4
@@ -1066,10 +1094,11 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? (kAttnTiles > 1 ? 3 : 4) : 2
       Ssum = ((tid & o) == 0) ? x + y : y + x;
       M = Mn;
     }
+    const int hrow = kRows * rg + row;   // row within the head
     if (part == 0) {
       // rows >= M have no query: lse = +inf makes every p of theirs 0
-      lse_s[row] = (row < a.M && M > -INFINITY) ? M + log2f(Ssum) : INFINITY;
-      if (row < a.M && (bad || !(M > -INFINITY) || !(Ssum <= FLT_MAX)) && ch == 0)
+      lse_s[hrow] = (hrow < a.M && M > -INFINITY) ? M + log2f(Ssum) : INFINITY;
+      if (hrow < a.M && (bad || !(M > -INFINITY) || !(Ssum <= FLT_MAX)) && ch == 0)
         atomicOr(a.latch, LATCH_NONFINITE);
     }
   }
@@ -1093,30 +1122,34 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? (kAttnTiles > 1 ? 3 : 4) : 2
     const int64_t j0 = e0 + (int64_t)t * kTile;
     const int64_t tok = j0 + r;
     const bool tok_ok = tok < e1;
-    f32x16 sacc, sacc1;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; sacc1[v] = 0.f; }
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (c & 1) sacc1 = mfma32(lds8<DP>(qs, r, 2 * c + hh), kB[u][c], sacc1);
-      else sacc = mfma32(lds8<DP>(qs, r, 2 * c + hh), kB[u][c], sacc);
-    }
     const bool interior = (j0 + kTile <= e1) && (j0 + kTile - 1 <= all_see);
     float sum = 0.f;
+#pragma unroll 1
+    for (int rg = 0; rg < R; ++rg) {
+      const unsigned char* qs = smem_raw + (size_t)rg * kRows * RowLayout<DP>::ROWB;
+      f32x16 sacc, sacc1;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 l4 = *reinterpret_cast<const float4*>(lse_s + 8 * q4 + 4 * hh);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; sacc1[v] = 0.f; }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int v = 4 * q4 + i;
-        float p = ex2((sacc[v] + sacc1[v]) * a.scale_log2 - lv[i]);
-        if (!interior) {
-          const int rv = 8 * q4 + 4 * hh + i;
-          const int64_t lim = rv < a.M ? n - a.w + (rv % a.w) : -1;
-          p = (tok_ok && tok <= lim) ? p : 0.f;
+      for (int c = 0; c < NC; ++c) {
+        if (c & 1) sacc1 = mfma32(lds8<DP>(qs, r, 2 * c + hh), kB[u][c], sacc1);
+        else sacc = mfma32(lds8<DP>(qs, r, 2 * c + hh), kB[u][c], sacc);
+      }
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 l4 = *reinterpret_cast<const float4*>(lse_s + kRows * rg + 8 * q4 + 4 * hh);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int v = 4 * q4 + i;
+          float p = ex2((sacc[v] + sacc1[v]) * a.scale_log2 - lv[i]);
+          if (!interior) {
+            const int rv = kRows * rg + 8 * q4 + 4 * hh + i;   // row within the head
+            const int64_t lim = rv < a.M ? n - a.w + (rv % a.w) : -1;
+            p = (tok_ok && tok <= lim) ? p : 0.f;
+          }
+          sum += p;
         }
-        sum += p;
       }
     }
     sum += __shfl_xor(sum, 32);
@@ -1135,10 +1168,17 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? (kAttnTiles > 1 ? 3 : 4) : 2
 template <int DP, bool FULLD>
 static hipError_t launch_attn_dp(void* ctx, const ScoreArgs& a, hipStream_t s) {
   const size_t lds1 = (size_t)kRows * RowLayout<DP>::ROWB;
-  const size_t lds2 = attn_pass2_lds_bytes<DP>();
+  const size_t lds2 = attn_pass2_lds_bytes<DP>(a.R);
+  static size_t granted2 = 65536;
+  if (lds2 > granted2) {
+    hipError_t e = hipFuncSetAttribute((const void*)attn_pass2_kernel<DP, FULLD>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
+    if (e != hipSuccess) return e;
+    granted2 = lds2;
+  }
   prof_begin(ctx, "attn_pass1", s);
-  hipLaunchKernelGGL((attn_pass1_kernel<DP, FULLD>), dim3(a.Hkv * a.splits), dim3(kThreads), lds1,
-                     s, a);
+  hipLaunchKernelGGL((attn_pass1_kernel<DP, FULLD>), dim3(a.Hkv * a.R * a.splits), dim3(kThreads),
+                     lds1, s, a);
   prof_end(ctx, "attn_pass1", s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1152,6 +1192,23 @@ static hipError_t launch_attn_dp(void* ctx, const ScoreArgs& a, hipStream_t s) {
 template <int DP>
 static hipError_t launch_attn_d(void* ctx, const ScoreArgs& a, hipStream_t s) {
   return a.d == DP ? launch_attn_dp<DP, true>(ctx, a, s) : launch_attn_dp<DP, false>(ctx, a, s);
+}
+
+// Whether pass 2's LDS (the row groups' Q / a rows and the chunk buffer) fits a
+// workgroup for this padded head dimension and number of row groups.
+bool score_fits(int DP, int R) {
+  constexpr size_t kLdsMax = 160 * 1024;
+  switch (DP) {
+    case 32: return pass2_lds_bytes<32>(R) <= kLdsMax;
+    case 64: return pass2_lds_bytes<64>(R) <= kLdsMax;
+    case 96: return pass2_lds_bytes<96>(R) <= kLdsMax;
+    case 128: return pass2_lds_bytes<128>(R) <= kLdsMax;
+    case 160: return pass2_lds_bytes<160>(R) <= kLdsMax;
+    case 192: return pass2_lds_bytes<192>(R) <= kLdsMax;
+    case 224: return pass2_lds_bytes<224>(R) <= kLdsMax;
+    case 256: return pass2_lds_bytes<256>(R) <= kLdsMax;
+    default: return false;
+  }
 }
 
 hipError_t launch_score_attention(void* ctx, const ScoreArgs& a, hipStream_t s) {
@@ -1229,28 +1286,29 @@ template <int DP, bool FULLD>
 static hipError_t launch_score_dp(void* ctx, const ScoreArgs& a, hipStream_t s) {
   const size_t red = (size_t)p1_waves(DP) * kRows * (DP + 1) * 4;   // the combine's slabs
   const size_t lds1 = pass1_lds_bytes<DP>() > red ? pass1_lds_bytes<DP>() : red;
-  const size_t lds2 = pass2_lds_bytes<DP>();
-  static bool attr_done = false;
-  if (!attr_done) {
-    if (lds1 > 65536) {
-      hipError_t e = hipFuncSetAttribute((const void*)pass1_kernel<DP, FULLD>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
-      if (e != hipSuccess) return e;
-    }
-    if (lds2 > 65536) {
-      hipError_t e = hipFuncSetAttribute((const void*)pass2_kernel<DP, FULLD>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
-      if (e != hipSuccess) return e;
-    }
-    attr_done = true;
+  const size_t lds2 = pass2_lds_bytes<DP>(a.R);
+  // dynamic LDS above the 64 KB default is granted per kernel, raised as needed
+  static size_t granted1 = 65536, granted2 = 65536;
+  if (lds1 > granted1) {
+    hipError_t e = hipFuncSetAttribute((const void*)pass1_kernel<DP, FULLD>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
+    if (e != hipSuccess) return e;
+    granted1 = lds1;
+  }
+  if (lds2 > granted2) {
+    hipError_t e = hipFuncSetAttribute((const void*)pass2_kernel<DP, FULLD>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
+    if (e != hipSuccess) return e;
+    granted2 = lds2;
   }
   prof_begin(ctx, "pass1", s);
-  hipLaunchKernelGGL((pass1_kernel<DP, FULLD>), dim3(a.Hkv * a.splits), dim3(64 * p1_waves(DP)), lds1, s, a);
+  hipLaunchKernelGGL((pass1_kernel<DP, FULLD>), dim3(a.Hkv * a.R * a.splits), dim3(64 * p1_waves(DP)),
+                     lds1, s, a);
   prof_end(ctx, "pass1", s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   prof_begin(ctx, "merge", s);
-  hipLaunchKernelGGL(merge_kernel<DP>, dim3(a.Hkv * kRows), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(merge_kernel<DP>, dim3(a.Hkv * a.R * kRows), dim3(kThreads), 0, s, a);
   prof_end(ctx, "merge", s);
   prof_begin(ctx, "pass2", s);
   hipLaunchKernelGGL((pass2_kernel<DP, FULLD>), dim3((unsigned)a.Hkv * a.chunks2), dim3(kThreads), lds2,

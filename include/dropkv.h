@@ -77,8 +77,9 @@ int dropkv_destroy(dropkv_ctx *ctx);
  *   No attention weights, distances or per-token intermediates are materialised:
  *   scratch is O(Hq * w * d * splits).
  * EINVAL if: a pointer is NULL or not 16-byte aligned; Hq % Hkv != 0; w < 1 or
- *   w > n; n < 1 or n >= 2^31; pool < 1 or pool even; d % 8 != 0 or d > 256;
- *   G * w > 32.
+ *   w > n; n < 1 or n >= 2^31; pool < 1, pool even or pool > 129; d % 8 != 0 or
+ *   d > 256; G * w > 128 (the window rows of one KV head, in groups of 32; the
+ *   first pass reads K and V once per group); for d > 128, G * w > 96.
  * Latched: ESINGULAR if for some window query the mass off its arg-max key,
  *   relative to the arg-max, is <= 2^-53 (so p_max rounds to 1 in binary64);
  *   ENONFINITE if an input element is not finite; ERANGE if a score exceeds

@@ -77,6 +77,9 @@ SHAPES = [
     (3, 1, 72, 1500, 5, 129),
     (1, 1, 16, 4096, 32, 3),
     (6, 2, 200, 1100, 7, 11),
+    (28, 4, 128, 3000, 8, 7),    # 56 rows per KV head
+    (9, 1, 40, 700, 5, 3),       # 45 rows
+    (16, 1, 64, 1500, 8, 5),     # 128 rows
 ]
 
 

@@ -75,6 +75,12 @@ SHAPES = [
     (3, 1, 72, 1500, 5, 129),
     (1, 1, 16, 4096, 32, 3),
     (6, 2, 200, 1100, 7, 11),
+    # more than 32 window rows per KV head: row groups of 32
+    (28, 4, 128, 3000, 8, 7),    # G = 7, w = 8: 56 rows (Qwen2.5-7B-shaped)
+    (64, 8, 128, 2000, 8, 7),    # 64 rows, two full groups
+    (9, 1, 40, 700, 5, 3),       # 45 rows, w does not divide 32
+    (33, 1, 32, 300, 1, 3),      # 33 rows: one row in the second group
+    (16, 1, 64, 1500, 8, 5),     # 128 rows, four groups
 ]
 
 
@@ -232,7 +238,8 @@ def test_host_argument_checks(ctx):
     sc = torch.empty((2, 64), dtype=torch.float32, device="cuda")
     bad = [
         dict(Hq=3, Hkv=2), dict(w=0), dict(w=65), dict(pool=2), dict(pool=0), dict(pool=131),
-        dict(d=12), dict(d=264), dict(n=0), dict(Hq=64, Hkv=2, w=2),
+        dict(d=12), dict(d=264), dict(n=0), dict(Hq=130, Hkv=2, w=2),   # G*w = 130 > 128
+        dict(Hq=98, Hkv=2, w=2, d=256),                                 # 98 rows at d = 256
     ]
     for b in bad:
         args = dict(n=64, w=2, Hq=4, Hkv=2, d=16, pool=3)

@@ -48,7 +48,8 @@ def _run(ctx, q, k, v, pool):
 
 
 CASES = [("tiny", None), ("shape", (8, 2, 40, 777, 2, 9)), ("shape", (32, 8, 128, 3000, 8, 7)),
-         ("shape", (4, 1, 256, 700, 5, 3)), ("llama4k", None)]
+         ("shape", (4, 1, 256, 700, 5, 3)), ("shape", (28, 4, 128, 1000, 8, 7)),
+         ("shape", (9, 1, 40, 700, 5, 3)), ("llama4k", None)]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c[0] if c[1] is None else "x".join(map(str, c[1])))
