@@ -330,12 +330,16 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str):
     fetch = load(fetch_csv, "FETCH_SIZE")
     write = load(write_csv, "WRITE_SIZE")
 
+    def matches(name, key):
+        # "dropkv::pass1_kernel<" must not match "dropkv::attn_pass1_kernel<"
+        return key in name if key == "copyBuffer" else f"::{key}" in name
+
     def pick(rows, key):
-        vals = [v for name, vs in rows.items() if key in name for v in vs]
+        vals = [v for name, vs in rows.items() if matches(name, key) for v in vs]
         return sum(vals) / len(vals) if vals else None
 
     def largest(rows, key):
-        vals = [v for name, vs in rows.items() if key in name for v in vs]
+        vals = [v for name, vs in rows.items() if matches(name, key) for v in vs]
         return max(vals) if vals else None
 
     # the calibration copy is the runtime's device-to-device blit of COPY_BYTES,
@@ -349,7 +353,8 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str):
     sel = ("select_fused",) if pick(fetch, "select_fused") is not None else (
         "select_s1", "select_s2", "select_s3", "select_s4")
     families = (("pass1", ("pass1_kernel",)), ("merge", ("merge_kernel",)),
-                ("pass2", ("pass2_kernel",)), ("select", sel), ("compact", ("compact_kernel",)))
+                ("pass2", ("pass2_kernel",)), ("select", sel), ("compact", ("compact_kernel",)),
+                ("attn_pass1", ("attn_pass1_kernel",)), ("attn_pass2", ("attn_pass2_kernel",)))
     for short, keys in families:
         # a family of several kernels launched once each per call: sum per-launch means
         fks = [pick(fetch, k) for k in keys]
