@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libdropkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["score_kernels.hip", "select_compact.hip", "api.cpp"]
+SOURCES = ["score_kernels.hip", "select_compact.hip", "measure.hip", "api.cpp"]
 
 # Packed fp32 instructions are disabled: hand-written float code must not be
 # turned into v_pk_* forms on this target.

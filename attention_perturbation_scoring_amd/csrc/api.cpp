@@ -300,6 +300,14 @@ int dropkv_compact(dropkv_ctx* c, const uint16_t* k, const uint16_t* v, int32_t 
                                   static_cast<hipStream_t>(stream)));
 }
 
+int dropkv_stream_read(dropkv_ctx* c, const void* p, int64_t bytes, void* stream) {
+  if (!c || bytes <= 0 || bytes % 16 != 0 || !aligned16(p)) return DROPKV_EINVAL;
+  DeviceGuard guard(c->device);
+  if (!guard.ok) return DROPKV_EDEVICE;
+  // the sink is the spare tail of the latch block (words 32..39 of 64)
+  return to_status(launch_stream_read(c, p, bytes, c->latch + 32, static_cast<hipStream_t>(stream)));
+}
+
 int dropkv_sync(dropkv_ctx* c, void* stream) {
   if (!c) return DROPKV_EINVAL;
   DeviceGuard guard(c->device);

@@ -210,6 +210,10 @@ void carve_scratch(void* base, int Hkv, int splits, int DP, Partials* p, RowStat
 int plan_splits(int64_t n, int Hkv, int64_t* split_len, int target = kTargetWG1);
 hipError_t launch_score_attention(void* ctx, const ScoreArgs& a, hipStream_t s);
 bool score_fits(int DP, int R);
+// sink: device memory of at least 8 words, written only in the
+// practically impossible case that the buffer's XOR equals a fixed constant
+hipError_t launch_stream_read(void* ctx, const void* p, int64_t bytes, uint32_t* sink,
+                              hipStream_t s);
 constexpr int kTargetWGAttn = 1024;   // attention-only pass A: four small workgroups per CU
 int plan_chunks2(int64_t n, int Hkv, int64_t* chunk_len);
 

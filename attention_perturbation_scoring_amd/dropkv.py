@@ -17,7 +17,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdropkv.so")
 
 OK, EINVAL, ESINGULAR, ENONFINITE, ERANGE, EDEVICE, ENOMEM = range(7)
-KERNELS = ("pass1", "merge", "pass2", "select", "compact", "attn_pass1", "attn_pass2")
+KERNELS = ("pass1", "merge", "pass2", "select", "compact", "attn_pass1", "attn_pass2",
+           "stream_read")
 
 
 class DropKVError(RuntimeError):
@@ -53,6 +54,7 @@ def lib():
             "dropkv_profile_read": [P, ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_int64)],
             "dropkv_plan_splits": [i64, i32, ctypes.POINTER(i32)],
+            "dropkv_stream_read": [P, P, i64, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -158,6 +160,12 @@ class Context:
         _check(lib().dropkv_compact(self._h, _ptr(k), _ptr(v), Hkv, n, d, _ptr(keep), budget,
                                     _ptr(k_out), _ptr(v_out), _stream(stream)), "dropkv_compact")
 
+    def stream_read(self, buf, nbytes=None, stream=None):
+        """Read a device buffer once (the achievable-bandwidth reference)."""
+        nbytes = buf.numel() * buf.element_size() if nbytes is None else nbytes
+        _check(lib().dropkv_stream_read(self._h, _ptr(buf), nbytes, _stream(stream)),
+               "dropkv_stream_read")
+
     def sync(self, stream=None) -> int:
         """Wait for the stream; return (and clear) the latched device status."""
         return lib().dropkv_sync(self._h, _stream(stream))
@@ -202,6 +210,10 @@ def dropkv_select_layer(ctx: Context, *args, **kw):
 
 def dropkv_compact(ctx: Context, *args, **kw):
     return ctx.compact(*args, **kw)
+
+
+def dropkv_stream_read(ctx: Context, *args, **kw):
+    return ctx.stream_read(*args, **kw)
 
 
 def dropkv_sync(ctx: Context, stream=None) -> int:

@@ -16,6 +16,8 @@ Also:
                                         WRITE_SIZE) into profiles/traffic_<workload>.json
   --copy-calibration                    run one 1 GiB device-to-device copy after the
                                         timed steps (the counters' scale reference)
+  --summarize-util CSV COMMAND          rocprofv3 --pmc VALUBusy MfmaUtil output ->
+                                        profiles/util_<workload>.txt
 """
 from __future__ import annotations
 
@@ -258,6 +260,55 @@ def run(args):
     if L == 1:
         layer_select_us = time_layer_select(ctx, scores, Hkv, n, budget, stream, args)
 
+    # ---- per-call distribution with the caches flushed before every call ----
+    # Streaming 1 GiB through the caches evicts the 4 MB L2s and the 256 MB
+    # last-level cache, so each call starts cold.  A read flush leaves clean
+    # lines behind; a write flush (the fill) leaves up to the last-level
+    # cache's size in dirty lines, whose write-back then lands inside the timed
+    # call.  HIP events on the launch stream bracket score + select and
+    # compaction separately.
+    flush = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    flush.fill_(1.0)
+
+    def cold_calls(how):
+        ss_us, cp_us = [], []
+        for i in range(args.steps):
+            q, k, v = copies[i % len(copies)]
+            if how == "read":
+                ctx.stream_read(flush, stream=stream)
+            else:
+                flush.fill_(float(i))
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev[0].record(stream)
+            ctx.score(q, k, v, n, w, Hq, Hkv, d, pool, scores, stream)
+            ctx.select(scores, Hkv, n, budget, keep, stream)
+            ev[1].record(stream)
+            ctx.compact(k, v, Hkv, n, d, keep, budget, k_out, v_out, stream)
+            ev[2].record(stream)
+            ev[2].synchronize()
+            ss_us.append(1e3 * ev[0].elapsed_time(ev[1]))
+            cp_us.append(1e3 * ev[1].elapsed_time(ev[2]))
+        ctx.check(stream)
+        dist = lambda x: {"median": float(np.median(x)), "min": float(min(x)),
+                          "p90": float(np.percentile(x, 90))}
+        return {"score_select_us": dist(ss_us), "compact_us": dist(cp_us), "calls": args.steps}
+
+    cold = {"read_flush": cold_calls("read"), "write_flush": cold_calls("write")}
+
+    # ---- achievable read bandwidth: one streaming scan of the 1 GiB buffer ----
+    for _ in range(3):
+        ctx.stream_read(flush, stream=stream)
+    ctx.profile(True)
+    ctx.profile_reset()
+    for _ in range(10):
+        ctx.stream_read(flush, stream=stream)
+    torch.cuda.synchronize()
+    tot, cnt = ctx.profile_read("stream_read")
+    ctx.profile(False)
+    ctx.check(stream)
+    achievable_gbs = COPY_BYTES / (1e-3 * tot / cnt) / 1e9
+    del flush
+
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 2, dtype=torch.int16, device="cuda")
         dst = torch.empty_like(src)
@@ -299,6 +350,10 @@ def run(args):
         "score_select_us": score_select_us,
         "score_select_algorithmic_GBs": path_gbs,
         "score_select_frac_of_peak": path_gbs / HBM_PEAK_GBS,
+        "cold_cache_calls": cold,
+        "achievable_read_GBs": achievable_gbs,
+        "dominant_frac_of_achievable": achieved / achievable_gbs,
+        "score_select_frac_of_achievable": path_gbs / achievable_gbs,
         "token_heads_per_s": Hkv * n / (ms_per_step * 1e-3),
         "profiled_ms_per_step": prof_wall * 1e3 / args.steps,
         "attention_mode": attention_mode,
@@ -374,6 +429,35 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str):
     log(f"[bench] wrote {path}")
 
 
+def summarize_util(csv_glob: str, workload: str, command: str):
+    """rocprofv3 --pmc VALUBusy MfmaUtil CSV -> profiles/util_<workload>.txt:
+    per kernel, the mean over dispatches of the percentage of the dispatch's
+    GPU time the vector ALUs and the matrix cores were busy."""
+    files = sorted(glob.glob(csv_glob)) if any(c in csv_glob for c in "*?[") else [csv_glob]
+    vals = {}
+    for p in files:
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                name = r.get("Kernel_Name", "").replace("(anonymous namespace)::", "")
+                name = name.split("(")[0].replace("void ", "")
+                name = name.replace("dropkv::", "")
+                vals.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+    lines = [f"rocprofv3 VALUBusy / MfmaUtil per dispatch, workload {workload}",
+             f"kernel sources sha256[:16] {kernel_source_hash()}",
+             f"command: {command}", "",
+             f"{'kernel':<40}{'dispatches':>11}{'VALUBusy%':>11}{'MfmaUtil%':>11}"]
+    for name, c in sorted(vals.items()):
+        vb, mu = c.get("VALUBusy", []), c.get("MfmaUtil", [])
+        nd = max(len(vb), len(mu))
+        fmt = lambda xs: f"{sum(xs) / len(xs):>11.1f}" if xs else f"{'-':>11}"
+        lines.append(f"{name[:39]:<40}{nd:>11}{fmt(vb)}{fmt(mu)}")
+    path = os.path.join(ROOT, "profiles", f"util_{workload}.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log(f"[bench] wrote {path}")
+
+
 def summarize_kt(stats_csv: str, workload: str, command: str):
     """rocprofv3 --kernel-trace --stats CSV -> profiles/kernel_stats_<workload>.txt."""
     with open(stats_csv) as f:
@@ -406,7 +490,11 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--summarize-kt", nargs=2, metavar=("STATS_CSV", "COMMAND"))
+    ap.add_argument("--summarize-util", nargs=2, metavar=("COUNTER_CSV", "COMMAND"))
     args = ap.parse_args()
+    if args.summarize_util:
+        summarize_util(args.summarize_util[0], args.workload, args.summarize_util[1])
+        return
     if args.summarize_kt:
         summarize_kt(args.summarize_kt[0], args.workload, args.summarize_kt[1])
         return

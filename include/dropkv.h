@@ -186,12 +186,23 @@ const char *dropkv_strerror(int code);
  * Per-kernel timing for measurement.  While enabled, every kernel the library
  * launches is bracketed by HIP events on the caller's stream; dropkv_profile_read
  * returns, for the kernel family `name` ("pass1", "merge", "pass2",
- * "select", "compact", "attn_pass1", "attn_pass2"), the summed milliseconds and launch count since the last
+ * "select", "compact", "attn_pass1", "attn_pass2", "stream_read"), the summed milliseconds and launch count since the last
  * reset (it synchronises on the recorded events).  Disabled by default.
  */
 int dropkv_profile_enable(dropkv_ctx *ctx, int on);
 int dropkv_profile_reset(dropkv_ctx *ctx);
 int dropkv_profile_read(dropkv_ctx *ctx, const char *name, double *total_ms, int64_t *launches);
+
+/*
+ * Measurement reference: read `bytes` of device memory at `p` once, as one
+ * coalesced streaming scan (eight workgroups per CU, each over a contiguous
+ * slice), and write nothing the caller can observe.  Timed with the profile
+ * name "stream_read", it gives the read bandwidth the device actually reaches,
+ * the yardstick for the two score passes, which each stream K and V once.
+ * `p` is caller-owned device memory, 16-byte aligned; `bytes` a positive
+ * multiple of 16, else EINVAL.  Asynchronous on `stream`.
+ */
+int dropkv_stream_read(dropkv_ctx *ctx, const void *p, int64_t bytes, void *stream);
 
 /* Launch geometry dropkv_score would use for these sizes (for tests/diagnostics):
  * number of sequence splits of the first pass. */

@@ -48,6 +48,7 @@ def test_host_only_entry_points():
     L = dropkv.lib()
     assert L.dropkv_score(None, None, None, None, 10, 1, 1, 1, 8, 1, None, None) == dropkv.EINVAL
     assert L.dropkv_sync(None, None) == dropkv.EINVAL
+    assert L.dropkv_stream_read(None, None, 16, None) == dropkv.EINVAL
 
 
 def test_binding_has_no_fallback(monkeypatch, tmp_path):
