@@ -142,8 +142,8 @@ __device__ __forceinline__ void load_kv_tile(const u16* kg, const u16* vg, int64
 
 template <int DP>
 constexpr size_t pass1_lds_bytes() {
-  // Q rows, then one V slot per wave (two when the next tile is prefetched)
-  return (size_t)kRows * RowLayout<DP>::ROWB * (1 + (kP1Overlap ? 2 : 1) * p1_waves(DP));
+  // Q rows, then one V slot per wave
+  return (size_t)kRows * RowLayout<DP>::ROWB * (1 + p1_waves(DP));
 }
 
 // K tile into registers (operand layout as load_kv_tile).
@@ -162,14 +162,14 @@ __device__ __forceinline__ void load_k_tile(const u16* kg, int64_t tok, bool tok
   }
 }
 
-// One direct global->LDS load of 16 bytes per lane: lane l's bytes land at LDS
-// address `lds` + 16 l.  Issued from inline assembly so that the compiler does
-// not order every later LDS access after it; the caller waits explicitly
-// (vector-memory counter) before reading the destination.
-__device__ __forceinline__ void dma16(const void* gaddr, unsigned char* lds_generic) {
-  const unsigned lds = __builtin_amdgcn_readfirstlane(
-      (unsigned)(size_t)((__attribute__((address_space(3))) unsigned char*)lds_generic));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds)
+// One direct global->LDS load of 16 bytes per lane from a wave-uniform base
+// address (scalar registers) plus a 32-bit per-lane byte offset: lane l's
+// bytes land at LDS address `lds` + 16 l.  Issued from inline assembly so that
+// the compiler does not order every later LDS access after it; the caller waits
+// explicitly (vector-memory counter) before reading the destination.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(lds)
                : "memory");
 }
 
@@ -201,6 +201,36 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* p) {
       (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) unsigned char*)p));
 }
 
+// V tile of tokens [t0, t0+32) into registers, already in the order of its
+// LDS slot (VLayout): register i of lane l is the 16 bytes the lane later
+// stores at byte 1024 i + 16 l of the slot.  Padding chunks (column >= d) and
+// tokens past `end` read some in-range row of the tile instead; they are
+// multiplied by p = 0 or never used.
+template <int DP>
+__device__ __forceinline__ void load_v_tile(const u16* vg, int64_t t0, int64_t end, int d, int lane,
+                                            u32x4 (&vr)[VLayout<DP>::CHP / 2]) {
+  using L = VLayout<DP>;
+  constexpr int RPI = 64 / L::CHP;   // token rows one register covers
+  const int row0 = lane / L::CHP, pc = lane % L::CHP;
+  const int nrow = (int)min((int64_t)kTile, end - t0);
+#pragma unroll
+  for (int i = 0; i < L::CHP / 2; ++i) {
+    const int row = RPI * i + row0;
+    int c = pc ^ L::sw(row);
+    if (c * 8 >= d) c = 0;
+    const int rr = row < nrow ? row : 0;
+    vr[i] = *reinterpret_cast<const u32x4*>(vg + (t0 + rr) * d + c * 8);
+  }
+}
+
+template <int DP>
+__device__ __forceinline__ void store_v_tile(unsigned char* slot, int lane,
+                                             const u32x4 (&vr)[VLayout<DP>::CHP / 2]) {
+#pragma unroll
+  for (int i = 0; i < VLayout<DP>::CHP / 2; ++i)
+    *reinterpret_cast<u32x4*>(slot + 1024 * i + 16 * lane) = vr[i];
+}
+
 // V tile of tokens [t0, t0+32) straight into an LDS slot (no registers), in
 // VLayout order: instruction i fills bytes [1024 i, 1024 i + 1024) of the slot,
 // lane l the 16 bytes at 1024 i + 16 l.  Padding chunks (column >= d) and
@@ -210,17 +240,31 @@ template <int DP>
 __device__ __forceinline__ void dma_v_tile(const u16* vg, int64_t t0, int64_t end, int d,
                                            unsigned char* slot, int lane) {
   using L = VLayout<DP>;
+  constexpr int RPI = 64 / L::CHP;   // token rows one instruction fills
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+      (unsigned)(size_t)((__attribute__((address_space(3))) unsigned char*)slot));
+  const int row0 = lane / L::CHP, pc = lane % L::CHP;
+  if (t0 + kTile <= end) {
+    // whole tile: the row offset of instruction i goes into the scalar base
 #pragma unroll
-  for (int i = 0; i < L::CHP / 2; ++i) {
-    const int P = 64 * i + lane;
-    const int row = P / L::CHP, pc = P % L::CHP;
-    int c = pc ^ L::sw(row);
-    int64_t tok = t0 + row;
-    if (tok >= end) tok = t0;
-    if (c * 8 >= d) c = 0;
-    dma16(vg + tok * d + c * 8, slot + 1024 * i);
+    for (int i = 0; i < L::CHP / 2; ++i) {
+      int c = pc ^ L::sw(RPI * i + row0);
+      if (c * 8 >= d) c = 0;
+      dma16s(vg + (t0 + RPI * i) * d, (uint32_t)(row0 * d + c * 8) * 2u, lds0 + 1024u * i);
+    }
+  } else {
+    const int nrow = (int)(end - t0);
+#pragma unroll
+    for (int i = 0; i < L::CHP / 2; ++i) {
+      const int row = RPI * i + row0;
+      int c = pc ^ L::sw(row);
+      if (c * 8 >= d) c = 0;
+      const int rr = row < nrow ? row : 0;
+      dma16s(vg + t0 * d, (uint32_t)(rr * d + c * 8) * 2u, lds0 + 1024u * i);
+    }
   }
 }
+
 
 template <int DP, bool FULLD>
 __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void pass1_kernel(
@@ -233,7 +277,7 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
   __shared__ float sm_m[NWV][kRows], sm_S[NWV][kRows], sm_Sx[NWV][kRows];
   __shared__ int sm_j[NWV][kRows], sm_bad[NWV][kRows];
 
-  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
   // a virtual head is one 32-row group of one KV head
   const int hv = blockIdx.x / a.splits, s = blockIdx.x % a.splits;
@@ -248,9 +292,7 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
   const int64_t causal = row_ok ? a.n - a.w + ((row0 + r) % a.w) : -1;
   const int64_t all_see = a.n - a.w;   // every window query sees keys 0..n-w
   unsigned char* qs = smem_raw;                                  // Q rows of the group
-  unsigned char* vslot0 =   // this wave's V tile(s)
-      smem_raw + (size_t)kRows * L::ROWB * (1 + (kP1Overlap ? 2 : 1) * wid);
-  unsigned char* vslot1 = vslot0 + (size_t)kRows * L::ROWB;
+  unsigned char* vs = smem_raw + (size_t)kRows * L::ROWB * (1 + wid);   // this wave's V tile
 
   stage_rows<DP, NT>(qs, a.q + ((size_t)g * a.M + row0) * d, min(kRows, a.M - row0), d, d);
   __syncthreads();
@@ -264,76 +306,85 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
 
-  // Each wave walks its tiles in order.  The next tile's K goes into the same
-  // registers as soon as the logits have consumed them, and its V into the
-  // other LDS slot, so those loads fly during this tile's softmax and PV; the
-  // second workgroup on the CU covers the rest of the latency.
-  constexpr int kLoadsPerTile = NC + L::CHP / 2;
+  // Each wave walks its tiles in order.  K and V of a tile come straight into
+  // registers; V then goes through the wave's LDS slot, from which the PV
+  // product gathers it transposed.  With the overlap option the next tile's K
+  // is loaded into the same registers as soon as the logits have consumed
+  // them, and its V as soon as this tile's V is in LDS, so those loads fly
+  // during this tile's softmax and PV.  The second workgroup on the CU covers
+  // the rest of the latency.
+  // Head dimensions above 128 have no registers to spare for V: it goes from
+  // memory straight into the LDS slot (direct loads), without prefetch.
+  constexpr bool kVRegs = DP <= 128;
+  constexpr bool kPre = kP1Overlap && kVRegs;
   bf16x8 kk[NC];
-  if (kP1Overlap && wid < ntiles) {
-    const int64_t f0 = jbeg + (int64_t)wid * kTile;
-    load_k_tile<NC, FULLD>(kg, f0 + r, f0 + r < jend, f0 + kTile > jend, hh, d, kk);
-    dma_v_tile<DP>(vg, f0, jend, d, vslot0, lane);
+  u32x4 vr[kVRegs ? L::CHP / 2 : 1];
+  if constexpr (kPre) {
+    if (wid < ntiles) {
+      const int64_t f0 = jbeg + (int64_t)wid * kTile;
+      load_k_tile<NC, FULLD>(kg, f0 + r, f0 + r < jend, f0 + kTile > jend, hh, d, kk);
+      load_v_tile<DP>(vg, f0, jend, d, lane, vr);
+    }
   }
-  int slot = 0;
   for (int t = wid; t < ntiles; t += NWV) {
     const int64_t j0 = jbeg + (int64_t)t * kTile;
-    unsigned char* vs = slot ? vslot1 : vslot0;
-    if (!kP1Overlap) {
-      load_k_tile<NC, FULLD>(kg, j0 + r, j0 + r < jend, j0 + kTile > jend, hh, d, kk);
-      dma_v_tile<DP>(vg, j0, jend, d, vslot0, lane);
+    // lane-derived addresses are recomputed every tile (two or three integer
+    // operations each) instead of being held in registers across the loop
+    int lx = lane;
+    asm volatile("" : "+v"(lx));
+    const int rx = lx & 31, hx = lx >> 5;
+    if (!kPre) {
+      load_k_tile<NC, FULLD>(kg, j0 + rx, j0 + rx < jend, j0 + kTile > jend, hx, d, kk);
+      if constexpr (kVRegs) load_v_tile<DP>(vg, j0, jend, d, lx, vr);
+      else dma_v_tile<DP>(vg, j0, jend, d, vs, lx);
     }
-    // two independent accumulation chains keep the matrix core busy
-    f32x16 st, st1;
+    f32x16 st;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) { st[v] = 0.f; st1[v] = 0.f; }
+    for (int v = 0; v < 16; ++v) st[v] = 0.f;
 #pragma unroll
-    for (int c = 0; c < NC; c += 2) {
-      st = mfma32(kk[c], lds8<DP>(qs, r, 2 * c + hh), st);
-      if (c + 1 < NC) st1 = mfma32(kk[c + 1], lds8<DP>(qs, r, 2 * c + 2 + hh), st1);
+    for (int c = 0; c < NC; ++c) {
+      st = mfma32(kk[c], lds8<DP>(qs, rx, 2 * c + hx), st);
     }
-#pragma unroll
-    for (int v = 0; v < 16; ++v) st[v] += st1[v];
     const bool more = t + NWV < ntiles;
-    if (kP1Overlap && more) {
-      const int64_t n0 = j0 + (int64_t)NWV * kTile;
-      load_k_tile<NC, FULLD>(kg, n0 + r, n0 + r < jend, n0 + kTile > jend, hh, d, kk);
-      dma_v_tile<DP>(vg, n0, jend, d, slot ? vslot0 : vslot1, lane);
-    }
+    const int64_t n0 = j0 + (int64_t)NWV * kTile;
+    if (kPre && more)
+      load_k_tile<NC, FULLD>(kg, n0 + rx, n0 + rx < jend, n0 + kTile > jend, hx, d, kk);
 
-    // logits in log2 units; masks only on tiles that reach past the split end
-    // or into the window (rows >= M have zero queries and are never read)
+    // logits in log2 units, in place; masks only on tiles that reach past the
+    // split end or into the window (rows >= M have zero queries and are never
+    // read).  Token offsets within the tile are small integers: register v of
+    // lane (r, hh) holds offset 8 (v / 4) + 4 hh + v % 4.
     const bool interior = (j0 + kTile <= jend) && (j0 + kTile - 1 <= all_see);
-    float s2[16];
     float lm = -INFINITY;
     if (interior) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         chk = fmaf(st[v], 0.f, chk);          // becomes NaN on any inf / NaN logit
-        s2[v] = st[v] * a.scale_log2;
-        lm = fmaxf(lm, s2[v]);
+        st[v] *= a.scale_log2;
+        lm = fmaxf(lm, st[v]);
       }
     } else {
+      // last valid offset of this row in this tile (-1: none)
+      const int64_t lim64 = min(min(jend - j0 - 1, causal - j0), (int64_t)kTile);
+      const int lim = (int)max(lim64, (int64_t)-1);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t tv = j0 + 8 * (v >> 2) + 4 * hh + (v & 3);
-        const bool valid = row_ok && tv < jend && tv <= causal;
+        const bool valid = 8 * (v >> 2) + 4 * hx + (v & 3) <= lim;
         if (valid) chk = fmaf(st[v], 0.f, chk);
-        s2[v] = valid ? st[v] * a.scale_log2 : -INFINITY;
-        lm = fmaxf(lm, s2[v]);
+        st[v] = valid ? st[v] * a.scale_log2 : -INFINITY;
+        lm = fmaxf(lm, st[v]);
       }
     }
     lm = fmaxf(lm, __shfl_xor(lm, 32));
     const bool newmax = lm > m;
-    float p[16];
     if (__any(newmax)) {
       // some row's running maximum moves: find the tile arg-max (lowest index)
       // and rescale; the old arg-max's unit mass joins S_excl
       int lj = INT_MAX;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int tv = (int)(j0 + 8 * (v >> 2) + 4 * hh + (v & 3));
-        if (s2[v] == lm && lm > -INFINITY) lj = min(lj, tv);
+        const int off = 8 * (v >> 2) + 4 * hx + (v & 3);
+        if (st[v] == lm && lm > -INFINITY) lj = min(lj, off);
       }
       lj = min(lj, __shfl_xor(lj, 32));
       const float mn = newmax ? lm : m;
@@ -342,16 +393,16 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
       float ts = 0.f, tx = 0.f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int tv = (int)(j0 + 8 * (v >> 2) + 4 * hh + (v & 3));
-        p[v] = live ? ex2(s2[v] - mn) : 0.f;
-        ts += p[v];
-        tx += (tv == lj) ? 0.f : p[v];
+        const int off = 8 * (v >> 2) + 4 * hx + (v & 3);
+        st[v] = live ? ex2(st[v] - mn) : 0.f;
+        ts += st[v];
+        tx += (off == lj) ? 0.f : st[v];
       }
       ts += __shfl_xor(ts, 32);
       tx += __shfl_xor(tx, 32);
       if (newmax) {
         Sx = (Sx + (has ? 1.f : 0.f)) * alpha + tx;
-        jst = lj;
+        jst = (int)j0 + lj;
         has = true;
       } else {
         Sx = Sx + ts;
@@ -368,8 +419,8 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
       float ts = 0.f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        p[v] = ex2(s2[v] - mref);
-        ts += p[v];
+        st[v] = ex2(st[v] - mref);
+        ts += st[v];
       }
       ts += __shfl_xor(ts, 32);
       S += ts;
@@ -381,14 +432,18 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = p[8 * kc + e];
+        const float x = st[8 * kc + e];
         const __bf16 hi = (__bf16)x;
         ph[kc][e] = hi;
         pl[kc][e] = (__bf16)(x - (float)hi);
       }
     // this tile's V has landed once at most the loads issued above are pending
-    if (kP1Overlap && more) wait_vmem_below<kLoadsPerTile>();
-    else wait_vmem_below<0>();
+    if constexpr (kVRegs) {
+      store_v_tile<DP>(vs, lx, vr);
+      if (kPre && more) load_v_tile<DP>(vg, n0, jend, d, lx, vr);
+    } else {
+      wait_vmem_below<0>();   // this tile's V has landed in the slot
+    }
     wave_sync_lds();
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
@@ -396,14 +451,14 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
       // 4 hh + e%4.  Two transposed reads per block: lane 4e' + q of each
       // 16-lane group addresses token row 16 kc + 8 half + 4 hh + e' and the
       // 8 bytes holding columns 32 b + 16 (group % 2) + 4 q .. + 3.
-      const int gsub = (lane >> 4) & 1, e4 = (lane >> 2) & 3, q = lane & 3;
+      const int gsub = (lx >> 4) & 1, e4 = (lx >> 2) & 3, q = lx & 3;
       bf16x8 va[DB];
 #pragma unroll
       for (int b = 0; b < DB; ++b) {
         s16x4 part[2];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const int row = 16 * kc + 8 * half + 4 * hh + e4;
+          const int row = 16 * kc + 8 * half + 4 * hx + e4;
           const int chunk = 4 * b + 2 * gsub + (q >> 1);
           part[half] = lds_read_tr16(vs + VLayout<DP>::off(row, chunk) + 8 * (q & 1));
         }
@@ -417,7 +472,6 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
       for (int b = 0; b < DB; ++b) acc[b] = mfma32(va[b], pl[kc], acc[b]);
     }
     wave_sync_lds();
-    if (kP1Overlap) slot ^= 1;
   }
   if (!(chk == 0.f)) bad = 1;
 
