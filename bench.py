@@ -12,7 +12,8 @@ d=128, w=8, pool 7, 5 % budget), bf16 inputs drawn by the seeded generator.
 Prints ONE JSON line on stdout; everything else goes to stderr.
 
 Also:
-  --summarize-pmc FETCH.csv WRITE.csv   turn two rocprofv3 --pmc runs (FETCH_SIZE,
+  --summarize-pmc FETCH.csv WRITE.csv [FETCH_CMD WRITE_CMD]
+                                        turn two rocprofv3 --pmc runs (FETCH_SIZE,
                                         WRITE_SIZE) into profiles/traffic_<workload>.json
   --copy-calibration                    run one 1 GiB device-to-device copy after the
                                         timed steps (the counters' scale reference)
@@ -367,7 +368,7 @@ def run(args):
     return out
 
 
-def summarize_pmc(fetch_csv: str, write_csv: str, workload: str):
+def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, commands=()):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) from rocprofv3 counter CSVs,
     scaled by the same counters on the 1 GiB calibration copy."""
     def load(path, counter):
@@ -422,7 +423,8 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str):
     out = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
            "copy_bytes": COPY_BYTES, "copy_fetch_kib": copy_fetch, "copy_write_kib": copy_write,
            "fetch_scale": f_scale, "write_scale": w_scale, "kernels": kernels,
-           "made_by": f"python bench.py --summarize-pmc {fetch_csv} {write_csv}"}
+           "counter_runs": list(commands),
+           "made_by": f"python bench.py --summarize-pmc {fetch_csv} {write_csv} ..."}
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
@@ -438,9 +440,7 @@ def summarize_util(csv_glob: str, workload: str, command: str):
     for p in files:
         with open(p) as f:
             for r in csv.DictReader(f):
-                name = r.get("Kernel_Name", "").replace("(anonymous namespace)::", "")
-                name = name.split("(")[0].replace("void ", "")
-                name = name.replace("dropkv::", "")
+                name = _short_name(r.get("Kernel_Name", ""))
                 vals.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(
                     float(r["Counter_Value"]))
     lines = [f"rocprofv3 VALUBusy / MfmaUtil per dispatch, workload {workload}",
@@ -458,18 +458,56 @@ def summarize_util(csv_glob: str, workload: str, command: str):
     log(f"[bench] wrote {path}")
 
 
+def _short_name(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "")
+    return name.split("(")[0].replace("void ", "").replace("dropkv::", "")
+
+
 def summarize_kt(stats_csv: str, workload: str, command: str):
-    """rocprofv3 --kernel-trace --stats CSV -> profiles/kernel_stats_<workload>.txt."""
+    """rocprofv3 --kernel-trace --stats CSV -> profiles/kernel_stats_<workload>.txt.
+
+    The first table averages each kernel over the K timed steps and over the K
+    event-profiled steps that follow them (the window between the pass-1
+    launches that open those steps, read from the per-dispatch trace next to
+    the statistics file); the second is rocprofv3's whole-run table, which
+    also counts the warm-up, the cold-cache calls and the attention-only mode."""
+    import re
     with open(stats_csv) as f:
         rows = list(csv.DictReader(f))
+    steps = int(re.search(r"--steps (\d+)", command).group(1))
+    warm = int(re.search(r"--warmup (\d+)", command).group(1))
+    trace_csv = stats_csv.replace("_kernel_stats.csv", "_kernel_trace.csv")
+    with open(trace_csv) as f:
+        tr = [(_short_name(r["Kernel_Name"]), int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+              for r in csv.DictReader(f)]
+    tr.sort(key=lambda x: x[1])
+    p1 = [t for t in tr if t[0].startswith("pass1_kernel")]
     lines = [f"rocprofv3 kernel statistics, workload {workload}",
              f"kernel sources sha256[:16] {kernel_source_hash()}",
-             f"command: {command}", "",
-             f"{'kernel':<34}{'calls':>7}{'avg_us':>11}{'min_us':>11}{'max_us':>11}{'share%':>9}"]
+             f"command: {command}", ""]
+    for label, a, b in (("timed steps", warm, warm + steps),
+                        ("event-profiled steps", warm + steps, warm + 2 * steps)):
+        if len(p1) < b:
+            continue
+        # from the pass-1 launch opening step a to the end of the compaction
+        # closing step b - 1
+        lo = p1[a][1]
+        hi = min(t[2] for t in tr if t[0].startswith("compact_kernel") and t[1] > p1[b - 1][1])
+        per = {}
+        for name, t0, t1 in tr:
+            if lo <= t0 < hi and t1 <= hi:
+                per.setdefault(name, []).append((t1 - t0) / 1e3)
+        lines.append(f"{label} ({steps} steps, pass-1 launches {a}..{b - 1}):")
+        lines.append(f"{'kernel':<34}{'calls':>7}{'avg_us':>11}{'min_us':>11}{'max_us':>11}")
+        for name, d in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            lines.append(f"{name[:33]:<34}{len(d):>7}{sum(d) / len(d):>11.2f}{min(d):>11.2f}"
+                         f"{max(d):>11.2f}")
+        lines.append("")
+    lines.append("whole run (rocprofv3 --stats):")
+    lines.append(f"{'kernel':<34}{'calls':>7}{'avg_us':>11}{'min_us':>11}{'max_us':>11}{'share%':>9}")
     for r in rows:
-        name = r["Name"]
-        short = name.split("(")[0].replace("void ", "").replace("dropkv::", "")
-        lines.append(f"{short[:33]:<34}{int(r['Calls']):>7}{float(r['AverageNs']) / 1e3:>11.2f}"
+        lines.append(f"{_short_name(r['Name'])[:33]:<34}{int(r['Calls']):>7}"
+                     f"{float(r['AverageNs']) / 1e3:>11.2f}"
                      f"{float(r['MinNs']) / 1e3:>11.2f}{float(r['MaxNs']) / 1e3:>11.2f}"
                      f"{float(r['Percentage']):>9.2f}")
     path = os.path.join(ROOT, "profiles", f"kernel_stats_{workload}.txt")
@@ -488,7 +526,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=2,
                     help="copies of the layer that consecutive steps cycle through")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-pmc", nargs="+",
+                    metavar="FETCH_CSV WRITE_CSV [FETCH_COMMAND WRITE_COMMAND]")
     ap.add_argument("--summarize-kt", nargs=2, metavar=("STATS_CSV", "COMMAND"))
     ap.add_argument("--summarize-util", nargs=2, metavar=("COUNTER_CSV", "COMMAND"))
     args = ap.parse_args()
@@ -499,7 +538,8 @@ def main():
         summarize_kt(args.summarize_kt[0], args.workload, args.summarize_kt[1])
         return
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload)
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
+                      args.summarize_pmc[2:])
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
