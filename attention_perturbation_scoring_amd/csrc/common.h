@@ -106,6 +106,10 @@ constexpr int kP1Waves = DROPKV_P1_WAVES;
 constexpr int kP2Waves = DROPKV_P2_WAVES;
 constexpr bool kP1Overlap = DROPKV_P1_OVERLAP != 0;
 constexpr bool kP2Overlap = DROPKV_P2_OVERLAP != 0;
+#ifndef DROPKV_P1_GRANULE
+#define DROPKV_P1_GRANULE 1
+#endif
+constexpr int kP1Granule = DROPKV_P1_GRANULE;   // first-pass split interleave granule (tiles; 0 = contiguous)
 constexpr int kChunk2 = 2048;                // most tokens per pass-2 workgroup (before the pooling halo)
 // Pass 1 runs kP1WgWaves waves per workgroup: with 4 * kP1Waves of them, one
 // workgroup fills a CU, so no second workgroup on the CU trails the first.
