@@ -657,16 +657,8 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
   const uint32_t keep_before = gt_before + ties_before - ev_before;
 
   // The whole team is past its last barrier, so nobody reads the histograms or
-  // the candidate count again: clear this member's share of the histograms;
-  // the last member to get here resets the counters.
+  // the candidate count again: clear this member's share of the histograms.
   for (int i = b * kFusedThreads + tid; i < kFusedBins; i += (int)nblk * kFusedThreads) fh[i] = 0u;
-  if (tid == 0) {
-    if (atomicAdd(a.sc.done + g, 1u) == nblk - 1u) {
-      __hip_atomic_store(bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.sc.cand_cnt + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.sc.done + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
 
   // ordered emission (thread order is index order within the member): the
   // threads before this one hold gt_pre keys above T and tie_pre ties, of which
@@ -689,12 +681,21 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
     keepbits |= keepit ? 1u << i : 0u;
   }
   uint32_t pos = keep_before + gt_pre + (tie_pre > ev ? tie_pre - ev : 0u);
+  // count this member out (its reply arrives while the keep list is written);
+  // the last member of the team resets the counters
+  uint32_t done_before = 0u;
+  if (tid == 0) done_before = atomicAdd(a.sc.done + g, 1u);
   int32_t* kg = a.keep + (size_t)g * a.budget;
   while (keepbits) {   // one store per kept token, in index order
     const int i = __builtin_ctz(keepbits);
     keepbits &= keepbits - 1u;
     if (pos < (uint32_t)a.budget) kg[pos] = (int32_t)(base + i);
     ++pos;
+  }
+  if (tid == 0 && done_before == nblk - 1u) {
+    __hip_atomic_store(bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.sc.cand_cnt + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.sc.done + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

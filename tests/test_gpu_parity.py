@@ -204,6 +204,26 @@ def test_near_singular_rows_match(ctx, pstar, n):
     _full_check(ctx, q, k, v, 1, max(1, n // 4), f"p*={pstar} n={n}")
 
 
+def test_tied_maxima_across_splits(ctx):
+    """Three copies of the dominant key (each holding ~30 % of every row's
+    mass) in tiles that the first pass gives to different splits, the lowest
+    token in the highest-numbered split: the arg-max is the lowest index and the
+    scores match the oracle."""
+    d, n = 8, 9000
+    splits = dropkv.plan_splits(n, 1)
+    rng = np.random.default_rng(11)
+    q = np.zeros((2, 2, d), np.float32); q[:, :, 0] = 1.0
+    k = np.zeros((1, n, d), np.float32); k[0, :, 1:] = rng.standard_normal((n, d - 1))
+    L = math.log(0.3 * n / 0.1)
+    tiles = [splits - 1, splits + 1, 3 * splits - 8]   # splits (splits-1), 1, splits-8
+    for t in tiles:
+        k[0, 32 * t + 3, :] = 0.0
+        k[0, 32 * t + 3, 0] = L * math.sqrt(d)
+    v = rng.standard_normal((1, n, d)).astype(np.float32)
+    q, k, v = wl.bf16_bits(q), wl.bf16_bits(k), wl.bf16_bits(v)
+    _full_check(ctx, q, k, v, 3, n // 5, "tied maxima across splits")
+
+
 def test_nonfinite_rejected(ctx):
     q, k, v = _rand(4, 4, 2, 16, 100, 2)
     for which, idx, val in (("k", 333, 0x7F80), ("v", 17, 0x7FC0), ("q", 5, 0xFF80), ("k", 1500, 0xFF80)):
