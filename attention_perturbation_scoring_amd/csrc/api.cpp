@@ -169,7 +169,7 @@ int score_common(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
   if (!attention_only && !score_fits(a.DP, a.R)) return DROPKV_EINVAL;
   // the first pass runs per (KV head, row group): plan its splits over all of them
   a.splits = plan_splits(n, Hkv * a.R, &a.split_len, attention_only ? kTargetWGAttn : kTargetWG1);
-  a.chunks2 = plan_chunks2(n, Hkv, &a.chunk2_len);
+  a.chunks2 = plan_chunks2(n, Hkv, &a.chunk2_len, attention_only ? kTargetWGAttnB : kTargetWG2);
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
   a.latch = c->latch;
   a.out_a = out_a;

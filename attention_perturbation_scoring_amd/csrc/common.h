@@ -219,6 +219,10 @@ bool score_fits(int DP, int R);
 hipError_t launch_stream_read(void* ctx, const void* p, int64_t bytes, uint32_t* sink,
                               hipStream_t s);
 constexpr int kTargetWGAttn = 1024;   // attention-only pass A: four small workgroups per CU
-int plan_chunks2(int64_t n, int Hkv, int64_t* chunk_len);
+#ifndef DROPKV_ATTN_B_TARGET
+#define DROPKV_ATTN_B_TARGET 512
+#endif
+constexpr int kTargetWGAttnB = DROPKV_ATTN_B_TARGET;   // attention-only pass B: two chunks of up to 2048 tokens per CU
+int plan_chunks2(int64_t n, int Hkv, int64_t* chunk_len, int target = kTargetWG2);
 
 }  // namespace dropkv

@@ -1337,9 +1337,9 @@ int plan_splits(int64_t n, int Hkv, int64_t* split_len, int target) {
   return (int)((n + len - 1) / len);
 }
 
-int plan_chunks2(int64_t n, int Hkv, int64_t* chunk_len) {
-  // about kTargetWG2 workgroups over the chip, whole tiles, at most kChunk2 tokens
-  int64_t want = (kTargetWG2 + Hkv - 1) / Hkv;
+int plan_chunks2(int64_t n, int Hkv, int64_t* chunk_len, int target) {
+  // about `target` workgroups over the chip, whole tiles, at most kChunk2 tokens
+  int64_t want = (target + Hkv - 1) / Hkv;
   if (want < 1) want = 1;
   int64_t len = (n + want - 1) / want;
   len = (len + kTile - 1) / kTile * kTile;
