@@ -122,7 +122,10 @@ constexpr int p1_waves(int DP) { return DP <= 128 ? kP1WgWaves : 4; }
 #endif
 constexpr int kTargetWG1 =   // pass-1 workgroups aimed for
     DROPKV_P1_SPLIT_MULT * 256 * 4 * kP1Waves / kP1WgWaves;
-constexpr int kTargetWG2 = 256 * kP2Waves;   // pass-2 workgroups aimed for over all heads
+#ifndef DROPKV_P2_TARGET
+#define DROPKV_P2_TARGET (256 * DROPKV_P2_WAVES)
+#endif
+constexpr int kTargetWG2 = DROPKV_P2_TARGET;   // pass-2 workgroups aimed for over all heads
 
 // S_excl below this (argmax probability above ~0.94) routes the arg-max term
 // through the exact exclusion kernel instead of the fp32 output a.
