@@ -99,6 +99,26 @@ constexpr int kThreads = 64 * kWaves;
 #define DROPKV_ATTN_TILES 1
 #endif
 constexpr int kAttnTiles = DROPKV_ATTN_TILES;   // K tiles loaded per iteration (attention-only mode)
+// Non-temporal loads/stores per site (bit mask).  On MI355X a 1 GiB streaming
+// read whose every load instruction covers whole 128-byte lines reaches
+// ~6.9 TB/s with non-temporal loads against ~6.1 TB/s with ordinary ones; loads
+// that cover a line in several instructions (the K/V tiles in MFMA operand
+// layout) run far slower non-temporal, since the line is not kept between them.
+// Bits: 1 pass-1 V tile (whole rows per 16 lanes), 2 K/V tiles in MFMA operand
+// layout, 4 compaction loads, 8 compaction stores, 16 the streaming-read
+// reference.
+#ifndef DROPKV_NT
+#define DROPKV_NT 25
+#endif
+constexpr bool kNTV1 = (DROPKV_NT & 1) != 0;
+constexpr bool kNTMfma = (DROPKV_NT & 2) != 0;
+constexpr bool kNTCompactLd = (DROPKV_NT & 4) != 0;
+constexpr bool kNTCompactSt = (DROPKV_NT & 8) != 0;
+constexpr bool kNTStream = (DROPKV_NT & 16) != 0;
+#ifndef DROPKV_P1_KLDS
+#define DROPKV_P1_KLDS 0
+#endif
+constexpr bool kP1KLds = DROPKV_P1_KLDS != 0;   // pass 1: K tile through LDS (whole-line loads)
 #ifndef DROPKV_P1_WG_WAVES
 #define DROPKV_P1_WG_WAVES 4
 #endif

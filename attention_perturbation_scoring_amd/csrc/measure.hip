@@ -19,7 +19,8 @@ constexpr int kReadUnroll = 8;
 constexpr int kReadBlocks = 2048;   // eight workgroups per CU on 256 CUs
 
 // Each workgroup scans one contiguous slice of the buffer, eight 16-byte loads
-// per thread in flight per step.  The XOR of everything it read is stored only
+// per thread in flight per step, non-temporal like the K/V streams of the
+// score passes (on MI355X the faster form: ~6.9 against ~6.1 TB/s).  The XOR of everything it read is stored only
 // if it equals a fixed constant, so the loads cannot be dropped while nothing
 // is written in practice.
 __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4* __restrict__ p,
@@ -33,7 +34,11 @@ __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4* 
   for (; i + kStep <= b1; i += kStep) {
     u32x4 x[kReadUnroll];
 #pragma unroll
-    for (int u = 0; u < kReadUnroll; ++u) x[u] = p[i + (int64_t)u * kReadThreads + threadIdx.x];
+    for (int u = 0; u < kReadUnroll; ++u) {
+      const u32x4* a = p + i + (int64_t)u * kReadThreads + threadIdx.x;
+      if constexpr (kNTStream) x[u] = __builtin_nontemporal_load(a);
+      else x[u] = *a;
+    }
 #pragma unroll
     for (int u = 0; u < kReadUnroll; ++u) acc ^= x[u].x ^ x[u].y ^ x[u].z ^ x[u].w;
   }

@@ -31,8 +31,15 @@
 
 namespace dropkv {
 
+// 16 bytes of K or V, optionally non-temporal.
+template <bool NT>
+__device__ __forceinline__ u32x4 stream16(const u16* p) {
+  const u32x4* a = reinterpret_cast<const u32x4*>(p);
+  if constexpr (NT) return __builtin_nontemporal_load(a);
+  return *a;
+}
 __device__ __forceinline__ bf16x8 load8(const u16* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+  return __builtin_bit_cast(bf16x8, stream16<kNTMfma>(p));
 }
 __device__ __forceinline__ bf16x8 zero8() {
   u32x4 z = {0u, 0u, 0u, 0u};
@@ -206,7 +213,11 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* p) {
 // stores at byte 1024 i + 16 l of the slot.  Padding chunks (column >= d) and
 // tokens past `end` read some in-range row of the tile instead; they are
 // multiplied by p = 0 or never used.
-template <int DP>
+// With ROWL the registers are in RowLayout order instead (the layout MFMA
+// operands are read from with lds8): a K tile loaded this way and stored with
+// store_v_tile is read back in operand layout.  Either way each load
+// instruction covers whole rows (CHP lanes per row), i.e. whole cache lines.
+template <int DP, bool ROWL = false>
 __device__ __forceinline__ void load_v_tile(const u16* vg, int64_t t0, int64_t end, int d, int lane,
                                             u32x4 (&vr)[VLayout<DP>::CHP / 2]) {
   using L = VLayout<DP>;
@@ -216,10 +227,10 @@ __device__ __forceinline__ void load_v_tile(const u16* vg, int64_t t0, int64_t e
 #pragma unroll
   for (int i = 0; i < L::CHP / 2; ++i) {
     const int row = RPI * i + row0;
-    int c = pc ^ L::sw(row);
+    int c = ROWL ? pc ^ (row & RowLayout<DP>::MASK) : pc ^ L::sw(row);
     if (c * 8 >= d) c = 0;
     const int rr = row < nrow ? row : 0;
-    vr[i] = *reinterpret_cast<const u32x4*>(vg + (t0 + rr) * d + c * 8);
+    vr[i] = stream16<kNTV1>(vg + (t0 + rr) * d + c * 8);
   }
 }
 
@@ -350,6 +361,9 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
   // memory straight into the LDS slot (direct loads), without prefetch.
   constexpr bool kVRegs = DP <= 128;
   constexpr bool kPre = kP1Overlap && kVRegs;
+  // K through the wave's LDS slot as well (whole-line loads), read back in
+  // operand layout; the slot then takes the tile's V.
+  constexpr bool kKLds = kP1KLds && kVRegs && !kPre;
   bf16x8 kk[NC];
   u32x4 vr[kVRegs ? L::CHP / 2 : 1];
   if constexpr (kPre) {
@@ -366,7 +380,13 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
     int lx = lane;
     asm volatile("" : "+v"(lx));
     const int rx = lx & 31, hx = lx >> 5;
-    if (!kPre) {
+    if constexpr (kKLds) {
+      u32x4 kr[L::CHP / 2];
+      load_v_tile<DP, true>(kg, j0, jend, d, lx, kr);
+      load_v_tile<DP>(vg, j0, jend, d, lx, vr);
+      store_v_tile<DP>(vs, lx, kr);
+      wave_sync_lds();
+    } else if (!kPre) {
       load_k_tile<NC, FULLD>(kg, j0 + rx, j0 + rx < jend, j0 + kTile > jend, hx, d, kk);
       if constexpr (kVRegs) load_v_tile<DP>(vg, j0, jend, d, lx, vr);
       else dma_v_tile<DP>(vg, j0, jend, d, vs, lx);
@@ -376,8 +396,10 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
     for (int v = 0; v < 16; ++v) st[v] = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      st = mfma32(kk[c], lds8<DP>(qs, rx, 2 * c + hx), st);
+      const bf16x8 kc = kKLds ? lds8<DP>(vs, rx, 2 * c + hx) : kk[c];
+      st = mfma32(kc, lds8<DP>(qs, rx, 2 * c + hx), st);
     }
+    if constexpr (kKLds) wave_sync_lds();   // K read out before V takes the slot
     const bool more = t + NWV < ntiles;
     const int64_t n0 = sp.start(t + NWV);
     if (kPre && more)

@@ -744,6 +744,16 @@ size_t select_zero_prefix_bytes(int Hkv) {
          al256((size_t)Hkv * kFusedBins * 4) + 2 * al256((size_t)Hkv * 4);
 }
 
+// Row copies, optionally non-temporal.
+__device__ __forceinline__ u32x4 ld_stream(const u32x4* p) {
+  if constexpr (kNTCompactLd) return __builtin_nontemporal_load(p);
+  return *p;
+}
+__device__ __forceinline__ void st_stream(u32x4* p, u32x4 x) {
+  if constexpr (kNTCompactSt) __builtin_nontemporal_store(x, p);
+  else *p = x;
+}
+
 __global__ __launch_bounds__(256) void compact_kernel(const u16* __restrict__ k,
                                                       const u16* __restrict__ v, int64_t n, int d,
                                                       const int32_t* __restrict__ keep,
@@ -762,14 +772,14 @@ __global__ __launch_bounds__(256) void compact_kernel(const u16* __restrict__ k,
     u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
     if (j >= 0 && j < n) {
       const size_t src = ((size_t)g * n + j) * d + (size_t)c * 8;
-      kx = *reinterpret_cast<const u32x4*>(k + src);
-      vx = *reinterpret_cast<const u32x4*>(v + src);
+      kx = ld_stream(reinterpret_cast<const u32x4*>(k + src));
+      vx = ld_stream(reinterpret_cast<const u32x4*>(v + src));
     } else {
       bad = 1;
     }
     const size_t dst = (size_t)row * d + (size_t)c * 8;
-    *reinterpret_cast<u32x4*>(k_out + dst) = kx;
-    *reinterpret_cast<u32x4*>(v_out + dst) = vx;
+    st_stream(reinterpret_cast<u32x4*>(k_out + dst), kx);
+    st_stream(reinterpret_cast<u32x4*>(v_out + dst), vx);
   }
   if (bad) atomicOr(latch, LATCH_RANGE);
 }
