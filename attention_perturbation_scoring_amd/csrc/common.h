@@ -87,7 +87,7 @@ constexpr int kThreads = 64 * kWaves;
 #define DROPKV_P1_WAVES 2
 #endif
 #ifndef DROPKV_P2_WAVES
-#define DROPKV_P2_WAVES 3
+#define DROPKV_P2_WAVES 2
 #endif
 #ifndef DROPKV_P1_OVERLAP
 #define DROPKV_P1_OVERLAP 0
@@ -119,6 +119,12 @@ constexpr bool kNTStream = (DROPKV_NT & 16) != 0;
 #define DROPKV_P1_KLDS 0
 #endif
 constexpr bool kP1KLds = DROPKV_P1_KLDS != 0;   // pass 1: K tile through LDS (whole-line loads)
+#ifndef DROPKV_P2_VLDS
+#define DROPKV_P2_VLDS 2
+#endif
+// pass 2: V tile (1) or K and V tiles (2) through LDS (whole-line loads)
+constexpr bool kP2VLds = DROPKV_P2_VLDS != 0;
+constexpr bool kP2KLds = DROPKV_P2_VLDS >= 2;
 #ifndef DROPKV_P1_WG_WAVES
 #define DROPKV_P1_WG_WAVES 4
 #endif

@@ -217,7 +217,8 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* p) {
 // operands are read from with lds8): a K tile loaded this way and stored with
 // store_v_tile is read back in operand layout.  Either way each load
 // instruction covers whole rows (CHP lanes per row), i.e. whole cache lines.
-template <int DP, bool ROWL = false>
+// With ZPAD, chunks past the head dimension are zero instead.
+template <int DP, bool ROWL = false, bool ZPAD = false>
 __device__ __forceinline__ void load_v_tile(const u16* vg, int64_t t0, int64_t end, int d, int lane,
                                             u32x4 (&vr)[VLayout<DP>::CHP / 2]) {
   using L = VLayout<DP>;
@@ -228,9 +229,11 @@ __device__ __forceinline__ void load_v_tile(const u16* vg, int64_t t0, int64_t e
   for (int i = 0; i < L::CHP / 2; ++i) {
     const int row = RPI * i + row0;
     int c = ROWL ? pc ^ (row & RowLayout<DP>::MASK) : pc ^ L::sw(row);
-    if (c * 8 >= d) c = 0;
+    const bool pad = c * 8 >= d;
+    if (pad) c = 0;
     const int rr = row < nrow ? row : 0;
     vr[i] = stream16<kNTV1>(vg + (t0 + rr) * d + c * 8);
+    if (ZPAD && pad) vr[i] = u32x4{0u, 0u, 0u, 0u};
   }
 }
 
@@ -890,9 +893,16 @@ constexpr size_t pass2_group_bytes() {
   return (size_t)3 * kRows * RowLayout<DP>::ROWB;
 }
 template <int DP>
-constexpr size_t pass2_lds_bytes(int R) {
+constexpr bool pass2_vlds() { return kP2VLds && DP <= 128 && !kP2Overlap; }
+template <int DP>
+constexpr size_t pass2_lds_base(int R) {
   return (size_t)R * pass2_group_bytes<DP>() + (size_t)R * 4 * kRows * 4 +
          (size_t)(kChunk2 + 2 * kMaxRadius + kTile) * 4;
+}
+// ... and, with V through LDS, one V tile slot per wave
+template <int DP>
+constexpr size_t pass2_lds_bytes(int R) {
+  return pass2_lds_base<DP>(R) + (pass2_vlds<DP>() ? (size_t)kWaves * kRows * RowLayout<DP>::ROWB : 0);
 }
 
 template <int DP, bool FULLD>
@@ -952,7 +962,32 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
     const int64_t j0 = e0 + (int64_t)t * kTile;
     const int64_t tok = j0 + r;
     const bool tok_ok = tok < e1;
-    if (!kP2Overlap) issue(t, kB, vB);
+    if constexpr (pass2_vlds<DP>()) {
+      // V in whole-line loads, through this wave's slot into operand layout
+      unsigned char* vslot = smem_raw + pass2_lds_base<DP>(R) + (size_t)wid * kRows * L::ROWB;
+      u32x4 vr[L::CHP / 2];
+      if constexpr (kP2KLds) {
+        // K the same way first, through the same slot
+        u32x4 kr[L::CHP / 2];
+        load_v_tile<DP, true, !FULLD>(kg, j0, e1, d, lane, kr);
+        load_v_tile<DP, true, !FULLD>(vg, j0, e1, d, lane, vr);
+        store_v_tile<DP>(vslot, lane, kr);
+        wave_sync_lds();
+#pragma unroll
+        for (int c = 0; c < NC; ++c) kB[c] = lds8<DP>(vslot, r, 2 * c + hh);
+        wave_sync_lds();
+      } else {
+        load_k_tile<NC, FULLD>(kg, tok, tok_ok, j0 + kTile > e1, hh, d, kB);
+        load_v_tile<DP, true, !FULLD>(vg, j0, e1, d, lane, vr);
+      }
+      store_v_tile<DP>(vslot, lane, vr);
+      wave_sync_lds();
+#pragma unroll
+      for (int c = 0; c < NC; ++c) vB[c] = lds8<DP>(vslot, r, 2 * c + hh);
+      wave_sync_lds();
+    } else if (!kP2Overlap) {
+      issue(t, kB, vB);
+    }
     float vn2 = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
