@@ -247,7 +247,14 @@ bool score_fits(int DP, int R);
 // practically impossible case that the buffer's XOR equals a fixed constant
 hipError_t launch_stream_read(void* ctx, const void* p, int64_t bytes, uint32_t* sink,
                               hipStream_t s);
-constexpr int kTargetWGAttn = 1024;   // attention-only pass A: four small workgroups per CU
+// Attention-only passes: K tile in whole-line loads through a per-wave LDS
+// slot (then three workgroups per CU instead of four).
+#ifndef DROPKV_ATTN_KLDS
+#define DROPKV_ATTN_KLDS 0
+#endif
+constexpr bool kAttnKLds = DROPKV_ATTN_KLDS != 0 && kAttnTiles == 1;
+constexpr int kAttnWaves = kAttnKLds ? 3 : (kAttnTiles > 1 ? 3 : 4);   // waves per SIMD (d <= 128)
+constexpr int kTargetWGAttn = 256 * kAttnWaves;   // attention-only pass A: one small workgroup per wave slot
 #ifndef DROPKV_ATTN_B_TARGET
 #define DROPKV_ATTN_B_TARGET 512
 #endif

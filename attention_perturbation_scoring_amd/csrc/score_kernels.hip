@@ -1096,8 +1096,13 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
 // Pass B turns the split states into each row's log-sum-exp (fixed order),
 // recomputes the logits, adds p over the rows of each token, divides by G and
 // pools / protects like pass 2.  Only K is read, twice.
+template <int DP>
+constexpr bool attn_klds() { return kAttnKLds && DP <= 128; }
+template <int DP>
+constexpr size_t attn_slot_bytes() { return attn_klds<DP>() ? (size_t)kWaves * kRows * RowLayout<DP>::ROWB : 0; }
+
 template <int DP, bool FULLD>
-__global__ __launch_bounds__(kThreads, (DP <= 128 ? (kAttnTiles > 1 ? 3 : 4) : 2)) void attn_pass1_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kThreads, (DP <= 128 ? kAttnWaves : 2)) void attn_pass1_kernel(ScoreArgs a) {
   constexpr int NC = DP / 16;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ float sm_m[kWaves][kRows], sm_S[kWaves][kRows];
@@ -1125,11 +1130,23 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? (kAttnTiles > 1 ? 3 : 4) : 2
   // the order t, t + 4, t + 8, ... so the result does not depend on it
   for (int t0 = wid; t0 < ntiles; t0 += kWaves * kAttnTiles) {
     bf16x8 kk[kAttnTiles][NC];
+    if constexpr (attn_klds<DP>()) {
+      // one tile per iteration (t0 < ntiles): whole-line loads through the wave's slot
+      unsigned char* ks = smem_raw + (size_t)(1 + wid) * kRows * RowLayout<DP>::ROWB;
+      u32x4 kr[RowLayout<DP>::CHP / 2];
+      load_v_tile<DP, true, !FULLD>(kg, sp.start(t0), jend, d, lane, kr);
+      store_v_tile<DP>(ks, lane, kr);
+      wave_sync_lds();
 #pragma unroll
-    for (int u = 0; u < kAttnTiles; ++u) {
-      const int t = t0 + u * kWaves;
-      const int64_t j0 = sp.start(t);
-      if (t < ntiles) load_k_tile<NC, FULLD>(kg, j0 + r, j0 + r < jend, j0 + kTile > jend, hh, d, kk[u]);
+      for (int c = 0; c < NC; ++c) kk[0][c] = lds8<DP>(ks, r, 2 * c + hh);
+      wave_sync_lds();
+    } else {
+#pragma unroll
+      for (int u = 0; u < kAttnTiles; ++u) {
+        const int t = t0 + u * kWaves;
+        const int64_t j0 = sp.start(t);
+        if (t < ntiles) load_k_tile<NC, FULLD>(kg, j0 + r, j0 + r < jend, j0 + kTile > jend, hh, d, kk[u]);
+      }
     }
 #pragma unroll
     for (int u = 0; u < kAttnTiles; ++u) {
@@ -1194,12 +1211,16 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? (kAttnTiles > 1 ? 3 : 4) : 2
 }
 
 template <int DP>
-constexpr size_t attn_pass2_lds_bytes(int R) {
+constexpr size_t attn_pass2_base(int R) {
   return (size_t)R * kRows * RowLayout<DP>::ROWB + (size_t)(kChunk2 + 2 * kMaxRadius + kTile) * 4;
+}
+template <int DP>
+constexpr size_t attn_pass2_lds_bytes(int R) {
+  return attn_pass2_base<DP>(R) + attn_slot_bytes<DP>();
 }
 
 template <int DP, bool FULLD>
-__global__ __launch_bounds__(kThreads, (DP <= 128 ? (kAttnTiles > 1 ? 3 : 4) : 2)) void attn_pass2_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kThreads, (DP <= 128 ? kAttnWaves : 2)) void attn_pass2_kernel(ScoreArgs a) {
   constexpr int NC = DP / 16;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ float lse_s[kMaxRowGroups * kRows];
@@ -1264,11 +1285,22 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? (kAttnTiles > 1 ? 3 : 4) : 2
   // tiles' loads are issued before the first is consumed
   for (int t0 = wid; t0 < next; t0 += kWaves * kAttnTiles) {
     bf16x8 kB[kAttnTiles][NC];
+    if constexpr (attn_klds<DP>()) {
+      unsigned char* ks = smem_raw + attn_pass2_base<DP>(R) + (size_t)wid * kRows * RowLayout<DP>::ROWB;
+      u32x4 kr[RowLayout<DP>::CHP / 2];
+      load_v_tile<DP, true, !FULLD>(kg, e0 + (int64_t)t0 * kTile, e1, d, lane, kr);
+      store_v_tile<DP>(ks, lane, kr);
+      wave_sync_lds();
 #pragma unroll
-    for (int u = 0; u < kAttnTiles; ++u) {
-      const int t = t0 + u * kWaves;
-      const int64_t j0 = e0 + (int64_t)t * kTile;
-      if (t < next) load_k_tile<NC, FULLD>(kg, j0 + r, j0 + r < e1, j0 + kTile > e1, hh, d, kB[u]);
+      for (int c = 0; c < NC; ++c) kB[0][c] = lds8<DP>(ks, r, 2 * c + hh);
+      wave_sync_lds();
+    } else {
+#pragma unroll
+      for (int u = 0; u < kAttnTiles; ++u) {
+        const int t = t0 + u * kWaves;
+        const int64_t j0 = e0 + (int64_t)t * kTile;
+        if (t < next) load_k_tile<NC, FULLD>(kg, j0 + r, j0 + r < e1, j0 + kTile > e1, hh, d, kB[u]);
+      }
     }
 #pragma unroll
     for (int u = 0; u < kAttnTiles; ++u) {
@@ -1322,7 +1354,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? (kAttnTiles > 1 ? 3 : 4) : 2
 
 template <int DP, bool FULLD>
 static hipError_t launch_attn_dp(void* ctx, const ScoreArgs& a, hipStream_t s) {
-  const size_t lds1 = (size_t)kRows * RowLayout<DP>::ROWB;
+  const size_t lds1 = (size_t)kRows * RowLayout<DP>::ROWB + attn_slot_bytes<DP>();
   const size_t lds2 = attn_pass2_lds_bytes<DP>(a.R);
   static size_t granted2 = 65536;
   if (lds2 > granted2) {

@@ -35,8 +35,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["attention_perturbation_scoring_amd/csrc/score_kernels.hip",
-                  "attention_perturbation_scoring_amd/csrc/select_compact.hip"]
+KERNEL_SOURCES = ["attention_perturbation_scoring_amd/csrc/common.h",
+                  "attention_perturbation_scoring_amd/csrc/score_kernels.hip",
+                  "attention_perturbation_scoring_amd/csrc/select_compact.hip",
+                  "attention_perturbation_scoring_amd/csrc/measure.hip"]
 COPY_BYTES = 1 << 30
 
 

@@ -134,7 +134,7 @@ int dropkv_score_attention(dropkv_ctx *ctx, const uint16_t *q_win, const uint16_
  *   budget < 0 or budget > n.  (dropkv_score's protected window survives any
  *   budget >= w.)
  * If the context has a latched device error, nothing is written.
- * When Hkv * ceil(n / 32768) workgroups of 1024 threads fit on the device at
+ * When Hkv * ceil(n / 16384) workgroups of 1024 threads fit on the device at
  * once, this is one launch whose workgroups wait for each other (bounded: see
  * dropkv_sync); otherwise four launches.  Both give the same result.
  */
