@@ -106,7 +106,7 @@ constexpr int kAttnTiles = DROPKV_ATTN_TILES;   // K tiles loaded per iteration 
 // layout) run far slower non-temporal, since the line is not kept between them.
 // Bits: 1 pass-1 V tile (whole rows per 16 lanes), 2 K/V tiles in MFMA operand
 // layout, 4 compaction loads, 8 compaction stores, 16 the streaming-read
-// reference.
+// reference, 32 the pass-1 K tile when it goes through LDS.
 #ifndef DROPKV_NT
 #define DROPKV_NT 25
 #endif
@@ -115,6 +115,7 @@ constexpr bool kNTMfma = (DROPKV_NT & 2) != 0;
 constexpr bool kNTCompactLd = (DROPKV_NT & 4) != 0;
 constexpr bool kNTCompactSt = (DROPKV_NT & 8) != 0;
 constexpr bool kNTStream = (DROPKV_NT & 16) != 0;
+constexpr bool kNTP1K = (DROPKV_NT & 32) != 0;   // pass-1 K tile when it goes through LDS
 #ifndef DROPKV_P1_KLDS
 #define DROPKV_P1_KLDS 0
 #endif

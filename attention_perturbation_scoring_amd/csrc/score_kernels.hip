@@ -218,7 +218,7 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* p) {
 // store_v_tile is read back in operand layout.  Either way each load
 // instruction covers whole rows (CHP lanes per row), i.e. whole cache lines.
 // With ZPAD, chunks past the head dimension are zero instead.
-template <int DP, bool ROWL = false, bool ZPAD = false>
+template <int DP, bool ROWL = false, bool ZPAD = false, bool NT = kNTV1>
 __device__ __forceinline__ void load_v_tile(const u16* vg, int64_t t0, int64_t end, int d, int lane,
                                             u32x4 (&vr)[VLayout<DP>::CHP / 2]) {
   using L = VLayout<DP>;
@@ -232,7 +232,7 @@ __device__ __forceinline__ void load_v_tile(const u16* vg, int64_t t0, int64_t e
     const bool pad = c * 8 >= d;
     if (pad) c = 0;
     const int rr = row < nrow ? row : 0;
-    vr[i] = stream16<kNTV1>(vg + (t0 + rr) * d + c * 8);
+    vr[i] = stream16<NT>(vg + (t0 + rr) * d + c * 8);
     if (ZPAD && pad) vr[i] = u32x4{0u, 0u, 0u, 0u};
   }
 }
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
     const int rx = lx & 31, hx = lx >> 5;
     if constexpr (kKLds) {
       u32x4 kr[L::CHP / 2];
-      load_v_tile<DP, true>(kg, j0, jend, d, lx, kr);
+      load_v_tile<DP, true, false, kNTP1K>(kg, j0, jend, d, lx, kr);
       load_v_tile<DP>(vg, j0, jend, d, lx, vr);
       store_v_tile<DP>(vs, lx, kr);
       wave_sync_lds();
@@ -952,10 +952,13 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
     const int64_t t0 = e0 + (int64_t)t * kTile;
     load_kv_tile<NC, FULLD>(kg, vg, t0 + r, t0 + r < e1, t0 + kTile > e1, hh, d, kk, vv);
   };
-  // Each wave walks its tiles in order; the next tile's K and V are loaded into
-  // the same registers as soon as the matrix products have consumed them, so
-  // they fly during this tile's vector work.  Three workgroups per CU cover the
-  // rest of the latency.  Every row group of the head uses the same K/V tile.
+  // Each wave walks its tiles in order.  By default (d <= 128) a tile's K and V
+  // rows arrive in whole-line non-temporal loads and pass through the wave's
+  // LDS slot into operand layout; the other waves of the CU (two workgroups)
+  // cover the latency.  With the overlap option (register operands loaded
+  // directly) the next tile's K and V are loaded into the same registers as
+  // soon as the matrix products have consumed them.  Every row group of the
+  // head uses the same K/V tile.
   bf16x8 kB[NC], vB[NC];
   if (kP2Overlap && wid < next) issue(wid, kB, vB);
   for (int t = wid; t < next; t += kWaves) {
