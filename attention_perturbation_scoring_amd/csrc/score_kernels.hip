@@ -332,7 +332,7 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
   const SplitTiles sp(a.n, s, a.splits, a.split_len);
   const int64_t jend = sp.jend;
   const int ntiles = sp.ntiles;
-  const int d = a.d;
+  const int d = FULLD ? DP : a.d;   // a compile-time constant in the full-width instance
   const u16* kg = a.k + (size_t)g * a.n * d;
   const u16* vg = a.v + (size_t)g * a.n * d;
   const bool row_ok = row0 + r < a.M;
@@ -924,7 +924,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
   const int rad = (a.pool - 1) / 2;
   const int64_t e0 = max((int64_t)0, c0 - rad), e1 = min(n, c1 + rad);
   const int next = (int)((e1 - e0 + kTile - 1) / kTile);
-  const int d = a.d;
+  const int d = FULLD ? DP : a.d;   // a compile-time constant in the full-width instance
   const u16* kg = a.k + (size_t)g * n * d;
   const u16* vg = a.v + (size_t)g * n * d;
   const int64_t all_see = n - a.w;
@@ -1117,7 +1117,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kAttnWaves : 2)) void attn_p
   const SplitTiles sp(a.n, s, a.splits, a.split_len);
   const int64_t jend = sp.jend;
   const int ntiles = sp.ntiles;
-  const int d = a.d;
+  const int d = FULLD ? DP : a.d;   // a compile-time constant in the full-width instance
   const u16* kg = a.k + (size_t)g * a.n * d;
   const bool row_ok = row0 + r < a.M;
   const int64_t causal = row_ok ? a.n - a.w + ((row0 + r) % a.w) : -1;
@@ -1237,7 +1237,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kAttnWaves : 2)) void attn_p
   const int rad = (a.pool - 1) / 2;
   const int64_t e0 = max((int64_t)0, c0 - rad), e1 = min(n, c1 + rad);
   const int next = (int)((e1 - e0 + kTile - 1) / kTile);
-  const int d = a.d;
+  const int d = FULLD ? DP : a.d;   // a compile-time constant in the full-width instance
   const u16* kg = a.k + (size_t)g * n * d;
   const int64_t all_see = n - a.w;
 
