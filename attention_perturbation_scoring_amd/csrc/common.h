@@ -126,6 +126,10 @@ constexpr bool kP1KLds = DROPKV_P1_KLDS != 0;   // pass 1: K tile through LDS (w
 // pass 2: V tile (1) or K and V tiles (2) through LDS (whole-line loads)
 constexpr bool kP2VLds = DROPKV_P2_VLDS != 0;
 constexpr bool kP2KLds = DROPKV_P2_VLDS >= 2;
+#ifndef DROPKV_P1_XCDSWZ
+#define DROPKV_P1_XCDSWZ 1
+#endif
+constexpr bool kP1XcdSwz = DROPKV_P1_XCDSWZ != 0;   // pass 1: XCD-aware split deal
 #ifndef DROPKV_P1_WG_WAVES
 #define DROPKV_P1_WG_WAVES 4
 #endif
