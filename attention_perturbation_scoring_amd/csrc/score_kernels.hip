@@ -917,7 +917,10 @@ constexpr size_t pass2_lds_bytes(int R) {
   return pass2_lds_base<DP>(R) + (pass2_vlds<DP>() ? (size_t)kWaves * kRows * RowLayout<DP>::ROWB : 0);
 }
 
-template <int DP, bool FULLD>
+// NB8: 8-row blocks of the row group that can hold window rows (rows >= M have
+// p = 0 and are skipped in the per-row vector work): 4 in general, 1 for an
+// instance launched only when G * w <= 8 (multi-head attention with w <= 8).
+template <int DP, bool FULLD, int NB8 = 4>
 __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_kernel(ScoreArgs a) {
   using L = RowLayout<DP>;
   constexpr int NC = DP / 16;
@@ -1035,9 +1038,11 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
 #pragma unroll
       for (int v = 0; v < 16; ++v) { sacc[v] += sacc1[v]; av[v] += av1[v]; }
       float cc[16];
+#pragma unroll
+      for (int v = 4 * NB8; v < 16; ++v) cc[v] = 0.f;
       float ovf = 0.f;   // becomes NaN if an expansion term overflowed fp32
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
+      for (int q4 = 0; q4 < NB8; ++q4) {
         // this lane's rows 8*q4 + 4*hh + 0..3 of the group
         const float4 l4 = *reinterpret_cast<const float4*>(lse_s + rg * kRows + 8 * q4 + 4 * hh);
         const float4 n4 = *reinterpret_cast<const float4*>(an2_s + rg * kRows + 8 * q4 + 4 * hh);
@@ -1234,7 +1239,7 @@ constexpr size_t attn_pass2_lds_bytes(int R) {
   return attn_pass2_base<DP>(R) + attn_slot_bytes<DP>();
 }
 
-template <int DP, bool FULLD>
+template <int DP, bool FULLD, int NB8 = 4>   // NB8 as in pass2_kernel
 __global__ __launch_bounds__(kThreads, (DP <= 128 ? kAttnWaves : 2)) void attn_pass2_kernel(ScoreArgs a) {
   constexpr int NC = DP / 16;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -1338,7 +1343,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kAttnWaves : 2)) void attn_p
         else sacc = mfma32(lds8<DP>(qs, r, 2 * c + hh), kB[u][c], sacc);
       }
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
+      for (int q4 = 0; q4 < NB8; ++q4) {
         const float4 l4 = *reinterpret_cast<const float4*>(lse_s + kRows * rg + 8 * q4 + 4 * hh);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
@@ -1367,17 +1372,42 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kAttnWaves : 2)) void attn_p
   }
 }
 
+// Dynamic LDS above the 64 KB default is granted per kernel, raised as needed.
+template <auto KERN>
+static hipError_t grant_lds(size_t bytes) {
+  static size_t granted = 65536;
+  if (bytes <= granted) return hipSuccess;
+  const hipError_t e =
+      hipFuncSetAttribute((const void*)KERN, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) granted = bytes;
+  return e;
+}
+
+// The second pass's instance: one 8-row block when G * w <= 8 (d <= 128).
+template <int DP, bool FULLD, template <int, bool, int> class K>
+static hipError_t launch_second(const ScoreArgs& a, size_t lds, hipStream_t s) {
+  if constexpr (DP <= 128) {
+    if (a.M <= 8) {
+      hipError_t e = grant_lds<K<DP, FULLD, 1>::fn>(lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((K<DP, FULLD, 1>::fn), dim3((unsigned)a.Hkv * a.chunks2), dim3(kThreads), lds, s, a);
+      return hipGetLastError();
+    }
+  }
+  hipError_t e = grant_lds<K<DP, FULLD, 4>::fn>(lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((K<DP, FULLD, 4>::fn), dim3((unsigned)a.Hkv * a.chunks2), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+template <int DP, bool FULLD, int NB8>
+struct Pass2K { static constexpr auto fn = pass2_kernel<DP, FULLD, NB8>; };
+template <int DP, bool FULLD, int NB8>
+struct AttnPass2K { static constexpr auto fn = attn_pass2_kernel<DP, FULLD, NB8>; };
+
 template <int DP, bool FULLD>
 static hipError_t launch_attn_dp(void* ctx, const ScoreArgs& a, hipStream_t s) {
   const size_t lds1 = (size_t)kRows * RowLayout<DP>::ROWB + attn_slot_bytes<DP>();
   const size_t lds2 = attn_pass2_lds_bytes<DP>(a.R);
-  static size_t granted2 = 65536;
-  if (lds2 > granted2) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_pass2_kernel<DP, FULLD>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
-    if (e != hipSuccess) return e;
-    granted2 = lds2;
-  }
   prof_begin(ctx, "attn_pass1", s);
   hipLaunchKernelGGL((attn_pass1_kernel<DP, FULLD>), dim3(a.Hkv * a.R * a.splits), dim3(kThreads),
                      lds1, s, a);
@@ -1385,10 +1415,9 @@ static hipError_t launch_attn_dp(void* ctx, const ScoreArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   prof_begin(ctx, "attn_pass2", s);
-  hipLaunchKernelGGL((attn_pass2_kernel<DP, FULLD>), dim3((unsigned)a.Hkv * a.chunks2),
-                     dim3(kThreads), lds2, s, a);
+  e = launch_second<DP, FULLD, AttnPass2K>(a, lds2, s);
   prof_end(ctx, "attn_pass2", s);
-  return hipGetLastError();
+  return e;
 }
 
 template <int DP>
@@ -1489,34 +1518,23 @@ static hipError_t launch_score_dp(void* ctx, const ScoreArgs& a, hipStream_t s) 
   const size_t red = (size_t)p1_waves(DP) * kRows * (DP + 1) * 4;   // the combine's slabs
   const size_t lds1 = pass1_lds_bytes<DP>() > red ? pass1_lds_bytes<DP>() : red;
   const size_t lds2 = pass2_lds_bytes<DP>(a.R);
-  // dynamic LDS above the 64 KB default is granted per kernel, raised as needed
-  static size_t granted1 = 65536, granted2 = 65536;
-  if (lds1 > granted1) {
-    hipError_t e = hipFuncSetAttribute((const void*)pass1_kernel<DP, FULLD>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
-    if (e != hipSuccess) return e;
-    granted1 = lds1;
-  }
-  if (lds2 > granted2) {
-    hipError_t e = hipFuncSetAttribute((const void*)pass2_kernel<DP, FULLD>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
-    if (e != hipSuccess) return e;
-    granted2 = lds2;
-  }
+  hipError_t e = grant_lds<pass1_kernel<DP, FULLD>>(lds1);
+  if (e != hipSuccess) return e;
   prof_begin(ctx, "pass1", s);
   hipLaunchKernelGGL((pass1_kernel<DP, FULLD>), dim3(a.Hkv * a.R * a.splits), dim3(64 * p1_waves(DP)),
                      lds1, s, a);
   prof_end(ctx, "pass1", s);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   prof_begin(ctx, "merge", s);
   hipLaunchKernelGGL(merge_kernel<DP>, dim3(a.Hkv * a.R * kRows), dim3(kThreads), 0, s, a);
   prof_end(ctx, "merge", s);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   prof_begin(ctx, "pass2", s);
-  hipLaunchKernelGGL((pass2_kernel<DP, FULLD>), dim3((unsigned)a.Hkv * a.chunks2), dim3(kThreads), lds2,
-                     s, a);
+  e = launch_second<DP, FULLD, Pass2K>(a, lds2, s);
   prof_end(ctx, "pass2", s);
-  return hipGetLastError();
+  return e;
 }
 
 template <int DP>

@@ -77,6 +77,10 @@ SHAPES = [
     (3, 1, 72, 1500, 5, 129),
     (1, 1, 16, 4096, 32, 3),
     (6, 2, 200, 1100, 7, 11),
+    # G * w = 8 (one 8-row block: the reduced second-pass instance) and 9 (not)
+    (4, 4, 96, 2500, 8, 7),      # Phi-3-mini-shaped heads: G = 1, w = 8
+    (8, 4, 128, 1700, 4, 3),     # G = 2, w = 4
+    (3, 3, 64, 900, 9, 5),       # G = 1, w = 9
     (28, 4, 128, 3000, 8, 7),    # 56 rows per KV head
     (9, 1, 40, 700, 5, 3),       # 45 rows
     (16, 1, 64, 1500, 8, 5),     # 128 rows
