@@ -135,7 +135,9 @@ constexpr bool kP1XcdSwz = DROPKV_P1_XCDSWZ != 0;   // pass 1: XCD-aware split d
 #endif
 constexpr int kP1Waves = DROPKV_P1_WAVES;
 constexpr int kP2Waves = DROPKV_P2_WAVES;
-constexpr bool kP1Overlap = DROPKV_P1_OVERLAP != 0;
+// pass 1 prefetch of the next tile: 1 K and V, 2 V only, 3 K only
+constexpr bool kP1PreK = DROPKV_P1_OVERLAP == 1 || DROPKV_P1_OVERLAP == 3;
+constexpr bool kP1PreV = DROPKV_P1_OVERLAP == 1 || DROPKV_P1_OVERLAP == 2;
 constexpr bool kP2Overlap = DROPKV_P2_OVERLAP != 0;
 #ifndef DROPKV_P1_GRANULE
 #define DROPKV_P1_GRANULE 1

@@ -375,18 +375,16 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
   // Head dimensions above 128 have no registers to spare for V: it goes from
   // memory straight into the LDS slot (direct loads), without prefetch.
   constexpr bool kVRegs = DP <= 128;
-  constexpr bool kPre = kP1Overlap && kVRegs;
+  constexpr bool kPreK = kP1PreK && kVRegs, kPreV = kP1PreV && kVRegs;
   // K through the wave's LDS slot as well (whole-line loads), read back in
   // operand layout; the slot then takes the tile's V.
-  constexpr bool kKLds = kP1KLds && kVRegs && !kPre;
+  constexpr bool kKLds = kP1KLds && kVRegs && !kPreK && !kPreV;
   bf16x8 kk[NC];
   u32x4 vr[kVRegs ? L::CHP / 2 : 1];
-  if constexpr (kPre) {
-    if (wid < ntiles) {
-      const int64_t f0 = sp.start(wid);
-      load_k_tile<NC, FULLD>(kg, f0 + r, f0 + r < jend, f0 + kTile > jend, hh, d, kk);
-      load_v_tile<DP>(vg, f0, jend, d, lane, vr);
-    }
+  if (wid < ntiles) {
+    const int64_t f0 = sp.start(wid);
+    if constexpr (kPreK) load_k_tile<NC, FULLD>(kg, f0 + r, f0 + r < jend, f0 + kTile > jend, hh, d, kk);
+    if constexpr (kPreV) load_v_tile<DP>(vg, f0, jend, d, lane, vr);
   }
   for (int t = wid; t < ntiles; t += NWV) {
     const int64_t j0 = sp.start(t);
@@ -401,10 +399,10 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
       load_v_tile<DP>(vg, j0, jend, d, lx, vr);
       store_v_tile<DP>(vs, lx, kr);
       wave_sync_lds();
-    } else if (!kPre) {
-      load_k_tile<NC, FULLD>(kg, j0 + rx, j0 + rx < jend, j0 + kTile > jend, hx, d, kk);
-      if constexpr (kVRegs) load_v_tile<DP>(vg, j0, jend, d, lx, vr);
-      else dma_v_tile<DP>(vg, j0, jend, d, vs, lx);
+    } else {
+      if constexpr (!kPreK) load_k_tile<NC, FULLD>(kg, j0 + rx, j0 + rx < jend, j0 + kTile > jend, hx, d, kk);
+      if constexpr (!kVRegs) dma_v_tile<DP>(vg, j0, jend, d, vs, lx);
+      else if constexpr (!kPreV) load_v_tile<DP>(vg, j0, jend, d, lx, vr);
     }
     f32x16 st;
 #pragma unroll
@@ -417,7 +415,7 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
     if constexpr (kKLds) wave_sync_lds();   // K read out before V takes the slot
     const bool more = t + NWV < ntiles;
     const int64_t n0 = sp.start(t + NWV);
-    if (kPre && more)
+    if (kPreK && more)
       load_k_tile<NC, FULLD>(kg, n0 + rx, n0 + rx < jend, n0 + kTile > jend, hx, d, kk);
 
     // logits in log2 units, in place; masks only on tiles that reach past the
@@ -510,7 +508,7 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
     // this tile's V has landed once at most the loads issued above are pending
     if constexpr (kVRegs) {
       store_v_tile<DP>(vs, lx, vr);
-      if (kPre && more) load_v_tile<DP>(vg, n0, jend, d, lx, vr);
+      if (kPreV && more) load_v_tile<DP>(vg, n0, jend, d, lx, vr);
     } else {
       wait_vmem_below<0>();   // this tile's V has landed in the slot
     }
