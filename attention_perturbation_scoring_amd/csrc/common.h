@@ -261,7 +261,12 @@ hipError_t launch_stream_read(void* ctx, const void* p, int64_t bytes, uint32_t*
 #endif
 constexpr bool kAttnKLds = DROPKV_ATTN_KLDS != 0 && kAttnTiles == 1;
 constexpr int kAttnWaves = kAttnKLds ? 3 : (kAttnTiles > 1 ? 3 : 4);   // waves per SIMD (d <= 128)
-constexpr int kTargetWGAttn = 256 * kAttnWaves;   // attention-only pass A: one small workgroup per wave slot
+// attention-only pass A: 512 workgroups (64 splits per head at 8 heads) beat
+// one per wave slot (1024): pass B then merges half the split states per row
+#ifndef DROPKV_ATTN_A_TARGET
+#define DROPKV_ATTN_A_TARGET 512
+#endif
+constexpr int kTargetWGAttn = DROPKV_ATTN_A_TARGET;
 #ifndef DROPKV_ATTN_B_TARGET
 #define DROPKV_ATTN_B_TARGET 512
 #endif
