@@ -106,7 +106,7 @@ constexpr int kAttnTiles = DROPKV_ATTN_TILES;   // K tiles loaded per iteration 
 // layout) run far slower non-temporal, since the line is not kept between them.
 // Bits: 1 pass-1 V tile (whole rows per 16 lanes), 2 K/V tiles in MFMA operand
 // layout, 4 compaction loads, 8 compaction stores, 16 the streaming-read
-// reference, 32 the pass-1 K tile when it goes through LDS.
+// reference.
 #ifndef DROPKV_NT
 #define DROPKV_NT 25
 #endif
@@ -115,11 +115,6 @@ constexpr bool kNTMfma = (DROPKV_NT & 2) != 0;
 constexpr bool kNTCompactLd = (DROPKV_NT & 4) != 0;
 constexpr bool kNTCompactSt = (DROPKV_NT & 8) != 0;
 constexpr bool kNTStream = (DROPKV_NT & 16) != 0;
-constexpr bool kNTP1K = (DROPKV_NT & 32) != 0;   // pass-1 K tile when it goes through LDS
-#ifndef DROPKV_P1_KLDS
-#define DROPKV_P1_KLDS 0
-#endif
-constexpr bool kP1KLds = DROPKV_P1_KLDS != 0;   // pass 1: K tile through LDS (whole-line loads)
 #ifndef DROPKV_P2_VLDS
 #define DROPKV_P2_VLDS 2
 #endif
@@ -254,13 +249,7 @@ bool score_fits(int DP, int R);
 // practically impossible case that the buffer's XOR equals a fixed constant
 hipError_t launch_stream_read(void* ctx, const void* p, int64_t bytes, uint32_t* sink,
                               hipStream_t s);
-// Attention-only passes: K tile in whole-line loads through a per-wave LDS
-// slot (then three workgroups per CU instead of four).
-#ifndef DROPKV_ATTN_KLDS
-#define DROPKV_ATTN_KLDS 0
-#endif
-constexpr bool kAttnKLds = DROPKV_ATTN_KLDS != 0 && kAttnTiles == 1;
-constexpr int kAttnWaves = kAttnKLds ? 3 : (kAttnTiles > 1 ? 3 : 4);   // waves per SIMD (d <= 128)
+constexpr int kAttnWaves = kAttnTiles > 1 ? 3 : 4;   // attention-only passes: waves per SIMD (d <= 128)
 // attention-only pass A: 512 workgroups (64 splits per head at 8 heads) beat
 // one per wave slot (1024): pass B then merges half the split states per row
 #ifndef DROPKV_ATTN_A_TARGET

@@ -218,7 +218,7 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* p) {
 // store_v_tile is read back in operand layout.  Either way each load
 // instruction covers whole rows (CHP lanes per row), i.e. whole cache lines.
 // With ZPAD, chunks past the head dimension are zero instead.
-template <int DP, bool ROWL = false, bool ZPAD = false, bool NT = kNTV1>
+template <int DP, bool ROWL = false, bool ZPAD = false>
 __device__ __forceinline__ void load_v_tile(const u16* vg, int64_t t0, int64_t end, int d, int lane,
                                             u32x4 (&vr)[VLayout<DP>::CHP / 2]) {
   using L = VLayout<DP>;
@@ -232,7 +232,7 @@ __device__ __forceinline__ void load_v_tile(const u16* vg, int64_t t0, int64_t e
     const bool pad = c * 8 >= d;
     if (pad) c = 0;
     const int rr = row < nrow ? row : 0;
-    vr[i] = stream16<NT>(vg + (t0 + rr) * d + c * 8);
+    vr[i] = stream16<kNTV1>(vg + (t0 + rr) * d + c * 8);
     if (ZPAD && pad) vr[i] = u32x4{0u, 0u, 0u, 0u};
   }
 }
@@ -376,9 +376,6 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
   // memory straight into the LDS slot (direct loads), without prefetch.
   constexpr bool kVRegs = DP <= 128;
   constexpr bool kPreK = kP1PreK && kVRegs, kPreV = kP1PreV && kVRegs;
-  // K through the wave's LDS slot as well (whole-line loads), read back in
-  // operand layout; the slot then takes the tile's V.
-  constexpr bool kKLds = kP1KLds && kVRegs && !kPreK && !kPreV;
   bf16x8 kk[NC];
   u32x4 vr[kVRegs ? L::CHP / 2 : 1];
   if (wid < ntiles) {
@@ -393,26 +390,16 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
     int lx = lane;
     asm volatile("" : "+v"(lx));
     const int rx = lx & 31, hx = lx >> 5;
-    if constexpr (kKLds) {
-      u32x4 kr[L::CHP / 2];
-      load_v_tile<DP, true, false, kNTP1K>(kg, j0, jend, d, lx, kr);
-      load_v_tile<DP>(vg, j0, jend, d, lx, vr);
-      store_v_tile<DP>(vs, lx, kr);
-      wave_sync_lds();
-    } else {
-      if constexpr (!kPreK) load_k_tile<NC, FULLD>(kg, j0 + rx, j0 + rx < jend, j0 + kTile > jend, hx, d, kk);
-      if constexpr (!kVRegs) dma_v_tile<DP>(vg, j0, jend, d, vs, lx);
-      else if constexpr (!kPreV) load_v_tile<DP>(vg, j0, jend, d, lx, vr);
-    }
+    if constexpr (!kPreK) load_k_tile<NC, FULLD>(kg, j0 + rx, j0 + rx < jend, j0 + kTile > jend, hx, d, kk);
+    if constexpr (!kVRegs) dma_v_tile<DP>(vg, j0, jend, d, vs, lx);
+    else if constexpr (!kPreV) load_v_tile<DP>(vg, j0, jend, d, lx, vr);
     f32x16 st;
 #pragma unroll
     for (int v = 0; v < 16; ++v) st[v] = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const bf16x8 kc = kKLds ? lds8<DP>(vs, rx, 2 * c + hx) : kk[c];
-      st = mfma32(kc, lds8<DP>(qs, rx, 2 * c + hx), st);
+      st = mfma32(kk[c], lds8<DP>(qs, rx, 2 * c + hx), st);
     }
-    if constexpr (kKLds) wave_sync_lds();   // K read out before V takes the slot
     const bool more = t + NWV < ntiles;
     const int64_t n0 = sp.start(t + NWV);
     if (kPreK && more)
@@ -1114,11 +1101,6 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
 // Pass B turns the split states into each row's log-sum-exp (fixed order),
 // recomputes the logits, adds p over the rows of each token, divides by G and
 // pools / protects like pass 2.  Only K is read, twice.
-template <int DP>
-constexpr bool attn_klds() { return kAttnKLds && DP <= 128; }
-template <int DP>
-constexpr size_t attn_slot_bytes() { return attn_klds<DP>() ? (size_t)kWaves * kRows * RowLayout<DP>::ROWB : 0; }
-
 template <int DP, bool FULLD>
 __global__ __launch_bounds__(kThreads, (DP <= 128 ? kAttnWaves : 2)) void attn_pass1_kernel(ScoreArgs a) {
   constexpr int NC = DP / 16;
@@ -1148,23 +1130,11 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kAttnWaves : 2)) void attn_p
   // the order t, t + 4, t + 8, ... so the result does not depend on it
   for (int t0 = wid; t0 < ntiles; t0 += kWaves * kAttnTiles) {
     bf16x8 kk[kAttnTiles][NC];
-    if constexpr (attn_klds<DP>()) {
-      // one tile per iteration (t0 < ntiles): whole-line loads through the wave's slot
-      unsigned char* ks = smem_raw + (size_t)(1 + wid) * kRows * RowLayout<DP>::ROWB;
-      u32x4 kr[RowLayout<DP>::CHP / 2];
-      load_v_tile<DP, true, !FULLD>(kg, sp.start(t0), jend, d, lane, kr);
-      store_v_tile<DP>(ks, lane, kr);
-      wave_sync_lds();
 #pragma unroll
-      for (int c = 0; c < NC; ++c) kk[0][c] = lds8<DP>(ks, r, 2 * c + hh);
-      wave_sync_lds();
-    } else {
-#pragma unroll
-      for (int u = 0; u < kAttnTiles; ++u) {
-        const int t = t0 + u * kWaves;
-        const int64_t j0 = sp.start(t);
-        if (t < ntiles) load_k_tile<NC, FULLD>(kg, j0 + r, j0 + r < jend, j0 + kTile > jend, hh, d, kk[u]);
-      }
+    for (int u = 0; u < kAttnTiles; ++u) {
+      const int t = t0 + u * kWaves;
+      const int64_t j0 = sp.start(t);
+      if (t < ntiles) load_k_tile<NC, FULLD>(kg, j0 + r, j0 + r < jend, j0 + kTile > jend, hh, d, kk[u]);
     }
 #pragma unroll
     for (int u = 0; u < kAttnTiles; ++u) {
@@ -1234,7 +1204,7 @@ constexpr size_t attn_pass2_base(int R) {
 }
 template <int DP>
 constexpr size_t attn_pass2_lds_bytes(int R) {
-  return attn_pass2_base<DP>(R) + attn_slot_bytes<DP>();
+  return attn_pass2_base<DP>(R);
 }
 
 template <int DP, bool FULLD, int NB8 = 4>   // NB8 as in pass2_kernel
@@ -1303,22 +1273,11 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kAttnWaves : 2)) void attn_p
   // tiles' loads are issued before the first is consumed
   for (int t0 = wid; t0 < next; t0 += kWaves * kAttnTiles) {
     bf16x8 kB[kAttnTiles][NC];
-    if constexpr (attn_klds<DP>()) {
-      unsigned char* ks = smem_raw + attn_pass2_base<DP>(R) + (size_t)wid * kRows * RowLayout<DP>::ROWB;
-      u32x4 kr[RowLayout<DP>::CHP / 2];
-      load_v_tile<DP, true, !FULLD>(kg, e0 + (int64_t)t0 * kTile, e1, d, lane, kr);
-      store_v_tile<DP>(ks, lane, kr);
-      wave_sync_lds();
 #pragma unroll
-      for (int c = 0; c < NC; ++c) kB[0][c] = lds8<DP>(ks, r, 2 * c + hh);
-      wave_sync_lds();
-    } else {
-#pragma unroll
-      for (int u = 0; u < kAttnTiles; ++u) {
-        const int t = t0 + u * kWaves;
-        const int64_t j0 = e0 + (int64_t)t * kTile;
-        if (t < next) load_k_tile<NC, FULLD>(kg, j0 + r, j0 + r < e1, j0 + kTile > e1, hh, d, kB[u]);
-      }
+    for (int u = 0; u < kAttnTiles; ++u) {
+      const int t = t0 + u * kWaves;
+      const int64_t j0 = e0 + (int64_t)t * kTile;
+      if (t < next) load_k_tile<NC, FULLD>(kg, j0 + r, j0 + r < e1, j0 + kTile > e1, hh, d, kB[u]);
     }
 #pragma unroll
     for (int u = 0; u < kAttnTiles; ++u) {
@@ -1404,7 +1363,7 @@ struct AttnPass2K { static constexpr auto fn = attn_pass2_kernel<DP, FULLD, NB8>
 
 template <int DP, bool FULLD>
 static hipError_t launch_attn_dp(void* ctx, const ScoreArgs& a, hipStream_t s) {
-  const size_t lds1 = (size_t)kRows * RowLayout<DP>::ROWB + attn_slot_bytes<DP>();
+  const size_t lds1 = (size_t)kRows * RowLayout<DP>::ROWB;
   const size_t lds2 = attn_pass2_lds_bytes<DP>(a.R);
   prof_begin(ctx, "attn_pass1", s);
   hipLaunchKernelGGL((attn_pass1_kernel<DP, FULLD>), dim3(a.Hkv * a.R * a.splits), dim3(kThreads),
