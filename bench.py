@@ -101,6 +101,20 @@ def time_layer_select(ctx, scores, Hkv, n, budget, stream, args):
     return 1e3 * tot / max(cnt // 2, 1)
 
 
+def host_cpu() -> str:
+    """The host's CPU model and logical CPU count, for the baseline's description."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}, nproc {os.cpu_count()}"
+
+
 def cpu_baseline(cfg, inp, dev_inputs):
     """Time the float64 oracle (score + select) on the host: the full layer of a
     single-layer workload; for a multi-layer cache, the first KV heads of
@@ -123,8 +137,8 @@ def cpu_baseline(cfg, inp, dev_inputs):
         return {"value": cfg.layers * cfg.n / whole, "unit": "tokens/s", "cores": heads,
                 "kind": "oracle",
                 "sample": f"{heads} KV heads of layer 0 of {cfg.name} (n={cfg.n}), float64 score + "
-                          f"select in {dt:.2f} s on {heads} threads, projected to all "
-                          f"{cfg.layers * cfg.Hkv} heads"}
+                          f"select in {dt:.2f} s on {heads} threads ({host_cpu()}), projected "
+                          f"to all {cfg.layers * cfg.Hkv} heads"}
     threads = min(cfg.Hkv, orc.default_threads())
     t0 = time.perf_counter()
     s = orc.score(inp["q"], inp["k"], inp["v"], cfg.pool, nthreads=threads)
@@ -132,7 +146,8 @@ def cpu_baseline(cfg, inp, dev_inputs):
     dt = time.perf_counter() - t0
     return {"value": cfg.n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"full {cfg.name} layer (all {cfg.Hkv} KV heads, n={cfg.n}); "
-                      f"float64 score + select, {dt:.2f} s wall on {threads} threads"}
+                      f"float64 score + select, {dt:.2f} s wall on {threads} threads "
+                      f"(one per KV head; {host_cpu()})"}
 
 
 def run(args):
