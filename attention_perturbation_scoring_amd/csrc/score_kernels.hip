@@ -110,15 +110,38 @@ __device__ __forceinline__ bf16x8 lds8(const unsigned char* base, int row, int c
 
 // Stage rows [0, 32) of a row-major bf16 matrix (rows >= nrows and columns >= d
 // are zero) into LDS with the swizzled layout.  Whole workgroup.
+// A load phase and a store phase with compile-time trip counts, so that a
+// workgroup's staging loads (several blocks of rows) are all in flight at once
+// rather than one memory round trip per chunk per block.
+template <int DP, int NT = kThreads>
+struct RowStage {
+  static constexpr int IT = (kRows * RowLayout<DP>::CH + NT - 1) / NT;
+  u32x4 x[IT];
+  __device__ __forceinline__ void load(const u16* src, int nrows, int ld, int d) {
+    using L = RowLayout<DP>;
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int i = (int)threadIdx.x + k * NT;
+      const int row = i / L::CH, ch = i % L::CH;
+      x[k] = u32x4{0u, 0u, 0u, 0u};
+      if (i < kRows * L::CH && row < nrows && ch * 8 < d)
+        x[k] = *reinterpret_cast<const u32x4*>(src + (size_t)row * ld + ch * 8);
+    }
+  }
+  __device__ __forceinline__ void store(unsigned char* dst) const {
+    using L = RowLayout<DP>;
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int i = (int)threadIdx.x + k * NT;
+      if (i < kRows * L::CH) *reinterpret_cast<u32x4*>(dst + L::off(i / L::CH, i % L::CH)) = x[k];
+    }
+  }
+};
 template <int DP, int NT = kThreads>
 __device__ __forceinline__ void stage_rows(unsigned char* dst, const u16* src, int nrows, int ld, int d) {
-  using L = RowLayout<DP>;
-  for (int i = threadIdx.x; i < kRows * L::CH; i += NT) {
-    const int row = i / L::CH, ch = i % L::CH;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (row < nrows && ch * 8 < d) x = *reinterpret_cast<const u32x4*>(src + (size_t)row * ld + ch * 8);
-    *reinterpret_cast<u32x4*>(dst + L::off(row, ch)) = x;
-  }
+  RowStage<DP, NT> st;
+  st.load(src, nrows, ld, d);
+  st.store(dst);
 }
 
 // One 32-token K/V tile in MFMA operand layout: lane l holds 8 consecutive d
@@ -933,15 +956,28 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
     unsigned char* qs = smem_raw + (size_t)rg * pass2_group_bytes<DP>();
     const size_t ro0 = ((size_t)g * R + rg) * kRows;   // this group's row state
     const int row0 = kRows * rg;
-    stage_rows<DP>(qs, a.q + ((size_t)g * a.M + row0) * d, min(kRows, a.M - row0), d, d);
-    stage_rows<DP>(qs + kRows * L::ROWB, a.rs.a_hi + ro0 * DP, kRows, DP, DP);
-    stage_rows<DP>(qs + 2 * kRows * L::ROWB, a.rs.a_lo + ro0 * DP, kRows, DP, DP);
+    // Q, a_hi, a_lo and the row state: every load issued before any store
+    RowStage<DP> sq, sh, sl;
+    sq.load(a.q + ((size_t)g * a.M + row0) * d, min(kRows, a.M - row0), d, d);
+    sh.load(a.rs.a_hi + ro0 * DP, kRows, DP, DP);
+    sl.load(a.rs.a_lo + ro0 * DP, kRows, DP, DP);
     // rows >= M carry lse = +inf (set by the merge): their p and contribution are 0
+    float lse = 0.f, an2 = 0.f, cst = 0.f;
+    int jsv = 0;
     if (tid < kRows) {
-      lse_s[rg * kRows + tid] = a.rs.lse2[ro0 + tid];
-      an2_s[rg * kRows + tid] = a.rs.an2[ro0 + tid];
-      js_s[rg * kRows + tid] = a.rs.jstar[ro0 + tid];
-      cs_s[rg * kRows + tid] = a.rs.cstar[ro0 + tid];
+      lse = a.rs.lse2[ro0 + tid];
+      an2 = a.rs.an2[ro0 + tid];
+      jsv = a.rs.jstar[ro0 + tid];
+      cst = a.rs.cstar[ro0 + tid];
+    }
+    sq.store(qs);
+    sh.store(qs + kRows * L::ROWB);
+    sl.store(qs + 2 * kRows * L::ROWB);
+    if (tid < kRows) {
+      lse_s[rg * kRows + tid] = lse;
+      an2_s[rg * kRows + tid] = an2;
+      js_s[rg * kRows + tid] = jsv;
+      cs_s[rg * kRows + tid] = cst;
     }
   }
   const float invG = 1.f / (float)a.G;
