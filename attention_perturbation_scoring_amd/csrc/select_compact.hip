@@ -508,7 +508,9 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
   __shared__ uint32_t sh[NW];
   __shared__ uint32_t s_bin, s_below, s_count, s_base;
   __shared__ int s_ok;
-  if (latched(a.latch)) return;
+  // a latched device error withholds the keep list; the latch is read first and
+  // tested once the keys have been requested, so the reads overlap
+  const bool stop = latched(a.latch);
   const int g = blockIdx.x / a.nblk, b = blockIdx.x % a.nblk;
   const int tid = threadIdx.x;
   const uint32_t nblk = (uint32_t)a.nblk;
@@ -536,6 +538,7 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
     for (int i = 0; i < kFusedPer; ++i) key[i] = i < nv ? order_key(sg[base + i]) : 0u;
   }
   const uint32_t pad = nblk * (uint32_t)kFusedBlock - (uint32_t)a.n;
+  if (stop) return;   // nothing has been written yet
 
   // round 1: the 12-bit bin b1 holding the k-th smallest key, and its size
   uint32_t prefix = 0u, mask = 0u, krem = (uint32_t)(a.n - a.budget) + pad;
