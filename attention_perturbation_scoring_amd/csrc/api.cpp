@@ -107,6 +107,8 @@ int dropkv_create(dropkv_ctx** out, int device) {
   c->device = device;
   hipError_t e = hipMalloc(&c->latch, 256);
   if (e == hipSuccess) e = hipMemset(c->latch, 0, 256);
+  // complete before any call, whatever stream it uses
+  if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e == hipSuccess) e = hipHostMalloc(&c->latch_host, sizeof(uint32_t));
   if (e != hipSuccess) {
     if (c->latch) (void)hipFree(c->latch);
@@ -238,7 +240,9 @@ int sel_prepare(dropkv_ctx* c, dropkv_ctx::SelBuf& b, int Hkv, int64_t n, hipStr
       if (e != hipSuccess) { b.p = nullptr; return DROPKV_ENOMEM; }
       b.bytes = need;
     }
-    hipError_t e = hipMemset(b.p, 0, select_zero_prefix_bytes(Hkv));
+    // stream-ordered (a null-stream memset would not order with a
+    // non-blocking stream's kernels)
+    hipError_t e = launch_zero(b.p, select_zero_prefix_bytes(Hkv), s);
     if (e != hipSuccess) return to_status(e);
     b.hkv = Hkv;
   }

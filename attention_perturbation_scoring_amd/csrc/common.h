@@ -224,6 +224,8 @@ struct SelScratch {
 size_t select_scratch_bytes(int Hkv, int64_t n);
 void carve_select(void* base, int Hkv, int64_t n, SelScratch* sc);
 size_t select_zero_prefix_bytes(int Hkv);
+// Zeroes `bytes` (a multiple of 4) at device address p, ordered on stream s.
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
 // Profiling hooks implemented by the host library (no-ops unless enabled).
 struct ProfScope;

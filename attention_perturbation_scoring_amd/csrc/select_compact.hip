@@ -757,6 +757,25 @@ size_t select_zero_prefix_bytes(int Hkv) {
          al256((size_t)Hkv * kFusedBins * 4) + 2 * al256((size_t)Hkv * 4);
 }
 
+// Zero-fill of a scratch prefix (a multiple of 4 bytes), ordered on the caller's
+// stream: a kernel rather than a null-stream memset, which streams created
+// non-blocking do not wait for.
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int64_t words) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  const int64_t words = (int64_t)(bytes / 4);
+  if (words == 0) return hipSuccess;
+  int64_t blocks = (words + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<uint32_t*>(p), words);
+  return hipGetLastError();
+}
+
 // Row copies, optionally non-temporal.
 __device__ __forceinline__ u32x4 ld_stream(const u32x4* p) {
   if constexpr (kNTCompactLd) return __builtin_nontemporal_load(p);
