@@ -139,10 +139,10 @@ constexpr bool kP2Overlap = DROPKV_P2_OVERLAP != 0;
 #endif
 constexpr int kP1Granule = DROPKV_P1_GRANULE;   // first-pass split interleave granule (tiles; 0 = contiguous)
 constexpr int kChunk2 = 2048;                // most tokens per pass-2 workgroup (before the pooling halo)
-// Pass 1 runs kP1WgWaves waves per workgroup: with 4 * kP1Waves of them, one
-// workgroup fills a CU, so no second workgroup on the CU trails the first.
-// (Head dimensions above 128 need more than 256 VGPRs, one wave per SIMD:
-// their workgroups keep four waves.)
+// Pass 1 runs kP1WgWaves waves per workgroup: four by default, two
+// workgroups per CU at two waves per SIMD (4 * kP1Waves = 8 makes one
+// workgroup fill the CU; measured no faster).  Head dimensions above 128 need
+// more than 256 VGPRs, one wave per SIMD: their workgroups keep four waves.
 constexpr int kP1WgWaves = DROPKV_P1_WG_WAVES;
 constexpr int p1_waves(int DP) { return DP <= 128 ? kP1WgWaves : 4; }
 #ifndef DROPKV_P1_SPLIT_MULT
