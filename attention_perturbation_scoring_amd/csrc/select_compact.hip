@@ -86,11 +86,9 @@ __device__ __forceinline__ bool latched(const uint32_t* latch) {
 
 __global__ __launch_bounds__(kSelThreads) void select_s1(SelArgs a) {
   __shared__ uint32_t h[kBins1];
-  if (latched(a.latch)) return;
+  const bool stop = latched(a.latch);   // tested once the scores are requested
   const int g = blockIdx.x / a.nblk, b = blockIdx.x % a.nblk;
   const int tid = threadIdx.x;
-  for (int i = tid; i < kBins1; i += kSelThreads) h[i] = 0u;
-  __syncthreads();
   const float* sg = a.scores + (size_t)g * a.n;
   const int64_t base = (int64_t)b * kSelBlock;
   const bool full = base + kSelBlock <= a.n;
@@ -100,6 +98,9 @@ __global__ __launch_bounds__(kSelThreads) void select_s1(SelArgs a) {
     const int64_t j = base + i * kSelThreads + tid;
     x[i] = (j < a.n) ? sg[j] : 0.f;
   }
+  if (stop) return;
+  for (int i = tid; i < kBins1; i += kSelThreads) h[i] = 0u;
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < kSelPer; ++i) {
     const int64_t j = base + i * kSelThreads + tid;
@@ -166,20 +167,29 @@ __global__ __launch_bounds__(kSelThreads) void select_s2(SelArgs a) {
   __shared__ uint32_t s_cnt, s_base;
   __shared__ uint32_t lk[kSelBlock];
   __shared__ int32_t li[kSelBlock];
-  if (latched(a.latch)) return;
+  // every read (latch, this block's scores, the head's threshold bin) is
+  // requested before any is used: one memory round trip
+  const bool stop = latched(a.latch);
   const int g = blockIdx.x / a.nblk, b = blockIdx.x % a.nblk;
   const int tid = threadIdx.x;
-  const uint32_t b1 = a.sc.b1[g];
-  if (tid == 0) s_cnt = 0u;
-  __syncthreads();
   const float* sg = a.scores + (size_t)g * a.n;
   const int64_t base = (int64_t)b * kSelBlock;
+  float x[kSelPer];
+#pragma unroll
+  for (int i = 0; i < kSelPer; ++i) {
+    const int64_t j = base + i * kSelThreads + tid;
+    x[i] = (j < a.n) ? sg[j] : 0.f;
+  }
+  const uint32_t b1 = a.sc.b1[g];
+  if (stop) return;
+  if (tid == 0) s_cnt = 0u;
+  __syncthreads();
   uint32_t above = 0u;
 #pragma unroll
   for (int i = 0; i < kSelPer; ++i) {
     const int64_t j = base + i * kSelThreads + tid;
     if (j < a.n) {
-      const uint32_t key = order_key(sg[j]);
+      const uint32_t key = order_key(x[i]);
       const uint32_t bin = key >> 20;
       if (bin > b1) ++above;
       if (bin == b1) {
@@ -292,30 +302,37 @@ __global__ __launch_bounds__(kSelThreads) void select_s4(SelArgs a) {
   __shared__ uint32_t sh[2 * (kSelThreads / 64) + 1];
   const int g = blockIdx.x / a.nblk, b = blockIdx.x % a.nblk;
   const int tid = threadIdx.x;
+  // every read (latch, block parameters, this thread's scores) is requested
+  // before any is used: one memory round trip
   const bool skip = latched(a.latch);
-  if (!skip) {
-    const uint32_t T = a.sc.T[g];
-    const uint32_t off = a.sc.blk_off[(size_t)g * a.nblk + b];
-    const uint32_t ev = a.sc.blk_evt[(size_t)g * a.nblk + b];
-    const float* sg = a.scores + (size_t)g * a.n;
-    int32_t* kg = a.keep + (size_t)g * a.budget;
-    // thread owns kSelPer consecutive tokens so that index order = (thread, i)
-    const int64_t base = (int64_t)b * kSelBlock + (int64_t)tid * kSelPer;
-    uint32_t keys[kSelPer];
-    uint32_t nt = 0u;
-    if (base + kSelPer <= a.n && (((size_t)g * a.n + base) & 3) == 0) {   // 16-byte aligned run
+  const uint32_t T = a.sc.T[g];
+  const uint32_t off = a.sc.blk_off[(size_t)g * a.nblk + b];
+  const uint32_t ev = a.sc.blk_evt[(size_t)g * a.nblk + b];
+  const float* sg = a.scores + (size_t)g * a.n;
+  // thread owns kSelPer consecutive tokens so that index order = (thread, i)
+  const int64_t base = (int64_t)b * kSelBlock + (int64_t)tid * kSelPer;
+  uint32_t keys[kSelPer];
+  if (base + kSelPer <= a.n && (((size_t)g * a.n + base) & 3) == 0) {   // 16-byte aligned run
+    float4 x[kSelPer / 4];
 #pragma unroll
-      for (int q = 0; q < kSelPer / 4; ++q) {
-        const float4 x = *reinterpret_cast<const float4*>(sg + base + 4 * q);
-        keys[4 * q + 0] = order_key(x.x);
-        keys[4 * q + 1] = order_key(x.y);
-        keys[4 * q + 2] = order_key(x.z);
-        keys[4 * q + 3] = order_key(x.w);
-      }
-    } else {
+    for (int q = 0; q < kSelPer / 4; ++q) x[q] = *reinterpret_cast<const float4*>(sg + base + 4 * q);
 #pragma unroll
-      for (int i = 0; i < kSelPer; ++i) keys[i] = (base + i < a.n) ? order_key(sg[base + i]) : 0u;
+    for (int q = 0; q < kSelPer / 4; ++q) {
+      keys[4 * q + 0] = order_key(x[q].x);
+      keys[4 * q + 1] = order_key(x[q].y);
+      keys[4 * q + 2] = order_key(x[q].z);
+      keys[4 * q + 3] = order_key(x[q].w);
     }
+  } else {
+    float x[kSelPer];
+#pragma unroll
+    for (int i = 0; i < kSelPer; ++i) x[i] = (base + i < a.n) ? sg[base + i] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kSelPer; ++i) keys[i] = (base + i < a.n) ? order_key(x[i]) : 0u;
+  }
+  if (!skip) {
+    int32_t* kg = a.keep + (size_t)g * a.budget;
+    uint32_t nt = 0u;
 #pragma unroll
     for (int i = 0; i < kSelPer; ++i)
       if (base + i < a.n && keys[i] == T) ++nt;
