@@ -901,29 +901,50 @@ hipError_t launch_select(void* ctx, const float* scores, int Hkv, int64_t n, int
 }
 
 // Per-head counts of a layer-wide keep list (flat indices g*n + j, ascending):
-// head g owns the entries in [g*n, (g+1)*n), found by binary search.
+// head g owns the entries in [g*n, (g+1)*n).  One wave per head finds both
+// ends by two 64-way searches run in lockstep (each round trip probes 64
+// positions and narrows the range 64-fold) rather than binary searches of one
+// dependent load per step.
 __global__ __launch_bounds__(256) void layer_counts_kernel(const int32_t* keep, int64_t budget,
                                                            int64_t n, int Hkv, int32_t* counts,
                                                            const uint32_t* latch) {
-  if (latched(latch)) return;
-  const int g = blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= Hkv) return;
-  auto lower = [&](int64_t x) {
-    int64_t lo = 0, hi = budget;
-    while (lo < hi) {
-      const int64_t mid = (lo + hi) / 2;
-      if (keep[mid] < x) lo = mid + 1;
-      else hi = mid;
+  const bool stop = latched(latch);
+  const int g = blockIdx.x * 4 + (int)(threadIdx.x >> 6);   // wave-uniform
+  const int lane = threadIdx.x & 63;
+  if (stop || g >= Hkv) return;
+  // first index i with keep[i] >= x[s], for the two bounds s = 0, 1
+  const int64_t x[2] = {(int64_t)g * n, (int64_t)(g + 1) * n};
+  int64_t lo[2] = {0, 0}, hi[2] = {budget, budget};
+  while (lo[0] < hi[0] || lo[1] < hi[1]) {
+    bool p[2];
+    int64_t step[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      step[k] = (hi[k] - lo[k] + 63) / 64;
+      const int64_t idx = lo[k] + (int64_t)lane * step[k];
+      p[k] = lo[k] < hi[k] && idx < hi[k] && keep[idx] < x[k];
     }
-    return lo;
-  };
-  counts[g] = (int32_t)(lower((int64_t)(g + 1) * n) - lower((int64_t)g * n));
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (lo[k] >= hi[k]) continue;
+      // the predicate holds on a prefix of the probes: lanes 0 .. c-1
+      const int c = __popcll(__ballot(p[k]));
+      if (c == 0) {
+        hi[k] = lo[k];
+      } else {
+        const int64_t l0 = lo[k];
+        lo[k] = l0 + (int64_t)(c - 1) * step[k] + 1;
+        hi[k] = min(hi[k], l0 + (int64_t)c * step[k]);
+      }
+    }
+  }
+  if (lane == 0) counts[g] = (int32_t)(lo[1] - lo[0]);
 }
 
 hipError_t launch_layer_counts(void* ctx, const int32_t* keep, int64_t budget, int64_t n, int Hkv,
                                int32_t* counts, uint32_t* latch, hipStream_t s) {
   prof_begin(ctx, "select", s);
-  hipLaunchKernelGGL(layer_counts_kernel, dim3((unsigned)((Hkv + 255) / 256)), dim3(256), 0, s,
+  hipLaunchKernelGGL(layer_counts_kernel, dim3((unsigned)((Hkv + 3) / 4)), dim3(256), 0, s,
                      keep, budget, n, Hkv, counts, (const uint32_t*)latch);
   prof_end(ctx, "select", s);
   return hipGetLastError();
