@@ -603,14 +603,26 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
       if (tid == 0) atomicOr((uint32_t*)a.latch, LATCH_TIMEOUT);
       return;
     }
-    for (uint32_t i = tid; i < c1; i += kFusedThreads) {
-      const uint64_t v = load_agent64(cand + i);
-      ck[i] = (uint32_t)v;
-      cw[i] = (uint16_t)(v >> 32);
+    // every candidate and count load in flight at once (c1 <= kFusedCand)
+    constexpr int CU = kFusedCand / kFusedThreads;
+    uint64_t cv[CU];
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      const uint32_t i = (uint32_t)tid + (uint32_t)(u * kFusedThreads);
+      cv[u] = i < c1 ? load_agent64(cand + i) : 0u;
     }
-    for (uint32_t i = tid; i < nblk; i += kFusedThreads) {
-      gtc[i] = load_agent(blk_gt + i);
-      tiec[i] = 0u;
+    const uint32_t gv = (uint32_t)tid < nblk ? load_agent(blk_gt + tid) : 0u;
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      const uint32_t i = (uint32_t)tid + (uint32_t)(u * kFusedThreads);
+      if (i < c1) {
+        ck[i] = (uint32_t)cv[u];
+        cw[i] = (uint16_t)(cv[u] >> 32);
+      }
+    }
+    if ((uint32_t)tid < nblk) {
+      gtc[tid] = gv;
+      tiec[tid] = 0u;
     }
     __syncthreads();
     // the exact k-th smallest key: two 10-bit digits below the bin, in LDS
