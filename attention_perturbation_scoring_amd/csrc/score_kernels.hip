@@ -1271,16 +1271,32 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kAttnWaves : 2)) void attn_p
     const size_t base = ((size_t)g * R + rg) * a.splits * kRows + row;
     float M = -INFINITY, Ssum = 0.f;
     int bad = 0;
-#pragma unroll 4
-    for (int sp = part; sp < a.splits; sp += 8) {
-      const float ms = a.part.m2[base + (size_t)sp * kRows];
-      const float ss = a.part.S[base + (size_t)sp * kRows];
-      bad |= a.part.bad[base + (size_t)sp * kRows];
-      if (ms > M) {
-        Ssum = Ssum * ex2(M - ms) + ss;
-        M = ms;
-      } else if (ms > -INFINITY) {
-        Ssum += ss * ex2(ms - M);
+    // batches of eight splits: all their loads requested, then combined in
+    // split order (one memory round trip per batch, not per split)
+    constexpr int SB = 8;
+    for (int sp0 = part; sp0 < a.splits; sp0 += 8 * SB) {
+      float msv[SB], ssv[SB];
+      int bv[SB];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const int sp = sp0 + 8 * u;
+        const bool ok = sp < a.splits;
+        const size_t o = base + (size_t)(ok ? sp : 0) * kRows;   // split 0 always exists
+        msv[u] = a.part.m2[o];
+        ssv[u] = a.part.S[o];
+        bv[u] = a.part.bad[o];
+        if (!ok) { msv[u] = -INFINITY; ssv[u] = 0.f; bv[u] = 0; }
+      }
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const float ms = msv[u], ss = ssv[u];
+        bad |= bv[u];
+        if (ms > M) {
+          Ssum = Ssum * ex2(M - ms) + ss;
+          M = ms;
+        } else if (ms > -INFINITY) {
+          Ssum += ss * ex2(ms - M);
+        }
       }
     }
 #pragma unroll
