@@ -29,7 +29,11 @@
  *   - every pointer is caller-owned device memory, 16-byte aligned; outputs are
  *     preallocated by the caller; the library never frees or retains them.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call is
- *     asynchronous on that stream except dropkv_sync.
+ *     asynchronous on that stream except dropkv_sync.  Scratch the library
+ *     (re)initialises is cleared by kernels on the call's own stream, so streams
+ *     created non-blocking (which do not wait for the null stream) are fine.
+ *   - Calls on one context share its scratch: calls that may overlap in time
+ *     (streams with no ordering between them) need separate contexts.
  *   - Host-side argument checks happen before any launch and return EINVAL
  *     synchronously.  Conditions found on the device (ESINGULAR, ENONFINITE,
  *     ERANGE) are latched in the context and returned by dropkv_sync; while a
