@@ -144,10 +144,18 @@ def cpu_baseline(cfg, inp, dev_inputs):
     s = orc.score(inp["q"], inp["k"], inp["v"], cfg.pool, nthreads=threads)
     orc.select(s, cfg.budget)
     dt = time.perf_counter() - t0
+    # the per-core rate: one KV head on one thread, scaled to the layer
+    t1 = time.perf_counter()
+    G = cfg.Hq // cfg.Hkv
+    s1 = orc.score(inp["q"][:G], inp["k"][:1], inp["v"][:1], cfg.pool, nthreads=1)
+    orc.select(s1, cfg.budget)
+    dt1 = (time.perf_counter() - t1) * cfg.Hkv
     return {"value": cfg.n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "value_one_thread": cfg.n / dt1,
             "sample": f"full {cfg.name} layer (all {cfg.Hkv} KV heads, n={cfg.n}); "
                       f"float64 score + select, {dt:.2f} s wall on {threads} threads "
-                      f"(one per KV head; {host_cpu()})"}
+                      f"(one per KV head; {host_cpu()}); one thread: KV head 0 alone, "
+                      f"{dt1 / cfg.Hkv:.2f} s, scaled to the layer"}
 
 
 def run(args):
