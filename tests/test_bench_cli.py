@@ -1,0 +1,69 @@
+"""bench.py's contract pieces that need no GPU: the one-GPU refusal, the
+roofline's algorithmic byte accounting, and the counter-summary arithmetic."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""   # no JSON line for a configuration that is not measured
+
+
+@pytest.mark.parametrize("d", [8, 96, 128, 256])
+def test_algorithmic_bytes_add_up_to_8d_plus_8_per_token_head(d):
+    Hkv, n, budget = 8, 131072, 6553
+    per = lambda k: bench.algorithmic_bytes(k, Hkv, n, d, budget) / (Hkv * n)
+    # two bf16 reads of K and V, one fp32 score write (pass 2) and one read (select)
+    assert per("pass1") + per("pass2") + per("select") == 8 * d + 8
+    # compaction: K and V rows of the kept tokens, read once and written once
+    assert bench.algorithmic_bytes("compact", Hkv, n, d, budget) == 2 * 2 * Hkv * budget * d * 2
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for name, value in rows:
+            w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_traffic_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
+    # FETCH_SIZE counts half of what the calibration copy read, WRITE_SIZE all of it
+    copy_kib = bench.COPY_BYTES / 1024
+    fetch = tmp_path / "f.csv"
+    write = tmp_path / "w.csv"
+    _counter_csv(fetch, "FETCH_SIZE", [
+        ("__amd_rocclr_copyBuffer", copy_kib / 2), ("__amd_rocclr_copyBuffer", 3.0),
+        ("void dropkv::pass1_kernel<128, true>(dropkv::ScoreArgs)", 1000.0),
+        ("void dropkv::pass1_kernel<128, true>(dropkv::ScoreArgs)", 1200.0),
+        ("void dropkv::attn_pass1_kernel<128, true>(dropkv::ScoreArgs)", 50.0),
+    ])
+    _counter_csv(write, "WRITE_SIZE", [
+        ("__amd_rocclr_copyBuffer", copy_kib), ("__amd_rocclr_copyBuffer", 3.0),
+        ("void dropkv::pass1_kernel<128, true>(dropkv::ScoreArgs)", 10.0),
+        ("void dropkv::pass1_kernel<128, true>(dropkv::ScoreArgs)", 30.0),
+        ("void dropkv::attn_pass1_kernel<128, true>(dropkv::ScoreArgs)", 5.0),
+    ])
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "test")
+    bench.summarize_pmc(str(fetch), str(write), "unit")
+    with open(tmp_path / "profiles" / "traffic_unit.json") as f:
+        t = json.load(f)
+    assert t["fetch_scale"] == pytest.approx(2.0) and t["write_scale"] == pytest.approx(1.0)
+    # pass 1: mean 1100 KiB fetched (x2) + mean 20 KiB written; the attention
+    # kernel's name must not be mistaken for pass 1's
+    assert t["kernels"]["pass1"]["bytes_per_launch"] == pytest.approx((2 * 1100 + 20) * 1024)
+    assert t["kernels"]["attn_pass1"]["bytes_per_launch"] == pytest.approx((2 * 50 + 5) * 1024)
