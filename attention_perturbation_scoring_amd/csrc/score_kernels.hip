@@ -240,8 +240,9 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* p) {
 // operands are read from with lds8): a K tile loaded this way and stored with
 // store_v_tile is read back in operand layout.  Either way each load
 // instruction covers whole rows (CHP lanes per row), i.e. whole cache lines.
-// With ZPAD, chunks past the head dimension are zero instead.
-template <int DP, bool ROWL = false, bool ZPAD = false>
+// With ZPAD, chunks past the head dimension are zero instead.  NT selects
+// non-temporal loads.
+template <int DP, bool ROWL = false, bool ZPAD = false, bool NT = kNTV1>
 __device__ __forceinline__ void load_v_tile(const u16* vg, int64_t t0, int64_t end, int d, int lane,
                                             u32x4 (&vr)[VLayout<DP>::CHP / 2]) {
   using L = VLayout<DP>;
@@ -255,7 +256,7 @@ __device__ __forceinline__ void load_v_tile(const u16* vg, int64_t t0, int64_t e
     const bool pad = c * 8 >= d;
     if (pad) c = 0;
     const int rr = row < nrow ? row : 0;
-    vr[i] = stream16<kNTV1>(vg + (t0 + rr) * d + c * 8);
+    vr[i] = stream16<NT>(vg + (t0 + rr) * d + c * 8);
     if (ZPAD && pad) vr[i] = u32x4{0u, 0u, 0u, 0u};
   }
 }
@@ -1008,7 +1009,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
       if constexpr (kP2KLds) {
         // K the same way first, through the same slot
         u32x4 kr[L::CHP / 2];
-        load_v_tile<DP, true, !FULLD>(kg, j0, e1, d, lane, kr);
+        load_v_tile<DP, true, !FULLD, kNTP2K>(kg, j0, e1, d, lane, kr);
         load_v_tile<DP, true, !FULLD>(vg, j0, e1, d, lane, vr);
         store_v_tile<DP>(vslot, lane, kr);
         wave_sync_lds();
