@@ -658,45 +658,74 @@ __device__ __forceinline__ int block_min256(int x, int* red) {
 template <int DP>
 __device__ float exclusion_term(const ScoreArgs& a, int g, int r, int jst, float m2, float S,
                                 float* red /* [16][DP+1] */, float* rsx /* [16] */, float* tmp) {
-  constexpr int SL = DP / 16;
+  // 16 lanes per token: lane ds holds the 16-byte chunks ds, ds + 16, ... of
+  // the row (8 bf16 each); 16 tokens at a time per workgroup, and each lane
+  // keeps U tokens' K and V chunks in flight (tokens visited in index order)
+  constexpr int CH = DP / 8, NCH = (CH + 15) / 16, U = 4;
   const int tid = threadIdx.x, tg = tid >> 4, ds = tid & 15;
   const int d = a.d;
   const int64_t P = a.n - a.w + (r % a.w);
   const u16* kg = a.k + (size_t)g * a.n * d;
   const u16* vg = a.v + (size_t)g * a.n * d;
   const u16* qrow = a.q + ((size_t)g * a.M + r) * d;
-  float qv[SL], acc[SL];
+  auto elem = [](const u32x4& x, int e) {   // bf16 element e of a 16-byte chunk, as float
+    const uint32_t w = x[e >> 1];
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+  };
+  float qv[NCH][8], acc[NCH][8];
 #pragma unroll
-  for (int i = 0; i < SL; ++i) {
-    const int dd = ds * SL + i;
-    qv[i] = dd < d ? bf2f(qrow[dd]) : 0.f;
-    acc[i] = 0.f;
-  }
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int dd = (ds + 16 * c) * 8 + e;
+      qv[c][e] = dd < d ? bf2f(qrow[dd]) : 0.f;
+      acc[c][e] = 0.f;
+    }
   float sx = 0.f;
-  for (int64_t j = tg; j <= P; j += 16) {
-    const u16* kr = kg + j * d;
-    const u16* vr = vg + j * d;
-    float dot = 0.f;
+  for (int64_t j0 = tg; j0 <= P; j0 += 16 * U) {
+    u32x4 kx[U][NCH], vx[U][NCH];
 #pragma unroll
-    for (int i = 0; i < SL; ++i) {
-      const int dd = ds * SL + i;
-      if (dd < d) dot += qv[i] * bf2f(kr[dd]);
-    }
-    dot += __shfl_xor(dot, 1, 16);
-    dot += __shfl_xor(dot, 2, 16);
-    dot += __shfl_xor(dot, 4, 16);
-    dot += __shfl_xor(dot, 8, 16);
-    const float e = (j == jst) ? 0.f : ex2(dot * a.scale_log2 - m2);
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = j0 + 16 * u;
 #pragma unroll
-    for (int i = 0; i < SL; ++i) {
-      const int dd = ds * SL + i;
-      if (dd < d) acc[i] += e * bf2f(vr[dd]);
+      for (int c = 0; c < NCH; ++c) {
+        const int ch = ds + 16 * c;
+        kx[u][c] = u32x4{0u, 0u, 0u, 0u};
+        vx[u][c] = u32x4{0u, 0u, 0u, 0u};
+        if (j <= P && ch * 8 < d) {   // d is a multiple of 8: chunks are whole
+          kx[u][c] = *reinterpret_cast<const u32x4*>(kg + j * d + ch * 8);
+          vx[u][c] = *reinterpret_cast<const u32x4*>(vg + j * d + ch * 8);
+        }
+      }
     }
-    sx += e;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = j0 + 16 * u;
+      float dot = 0.f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot += qv[c][e] * elem(kx[u][c], e);
+      dot += __shfl_xor(dot, 1, 16);
+      dot += __shfl_xor(dot, 2, 16);
+      dot += __shfl_xor(dot, 4, 16);
+      dot += __shfl_xor(dot, 8, 16);
+      const float p = (j > P || j == jst) ? 0.f : ex2(dot * a.scale_log2 - m2);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[c][e] += p * elem(vx[u][c], e);
+      sx += p;
+    }
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < SL; ++i) red[tg * (DP + 1) + ds * SL + i] = acc[i];
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = ds + 16 * c;
+    if (ch < CH)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[tg * (DP + 1) + ch * 8 + e] = acc[c][e];
+  }
   if (ds == 0) rsx[tg] = sx;
   __syncthreads();
   float tot_sx = 0.f;

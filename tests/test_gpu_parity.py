@@ -193,11 +193,12 @@ def test_singular_rejected_and_select_withheld(ctx):
 
 
 @pytest.mark.parametrize("pstar", [0.9, 0.999, 1 - 1e-9])
-@pytest.mark.parametrize("n", [12, 3000])
-def test_near_singular_rows_match(ctx, pstar, n):
+@pytest.mark.parametrize("n,d", [(12, 8), (3000, 8), (3000, 96), (3000, 128), (1500, 256),
+                                 (70000, 128)])
+def test_near_singular_rows_match(ctx, pstar, n, d):
     """Rows whose arg-max holds most of the mass are accepted and match (the
-    arg-max term goes through the exact exclusion path above p* ~ 0.94)."""
-    d = 8
+    arg-max term goes through the exact exclusion path above p* ~ 0.94: one
+    16-byte chunk per lane for d <= 128, two at d = 256; a long head at 70000)."""
     L = math.log(pstar * (n - 1) / (1 - pstar))
     rng = np.random.default_rng(5)
     q = np.zeros((2, 1, d), np.float32); q[:, 0, 0] = 1.0
@@ -205,7 +206,7 @@ def test_near_singular_rows_match(ctx, pstar, n):
     k[0, n // 3, 0] = L * math.sqrt(d)
     v = rng.standard_normal((1, n, d)).astype(np.float32)
     q, k, v = wl.bf16_bits(q), wl.bf16_bits(k), wl.bf16_bits(v)
-    _full_check(ctx, q, k, v, 1, max(1, n // 4), f"p*={pstar} n={n}")
+    _full_check(ctx, q, k, v, 1, max(1, n // 4), f"p*={pstar} n={n} d={d}")
 
 
 def test_tied_maxima_across_splits(ctx):
