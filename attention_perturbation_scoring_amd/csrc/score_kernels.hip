@@ -623,7 +623,8 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
 // reproducible); a is summed by float4 column group with the splits
 // partitioned over SG thread groups.  Rows whose arg-max holds
 // probability above ~0.94 then get their arg-max term from the exact
-// exclusion sum, computed by the same workgroup.
+// exclusion sum, computed by the same workgroup from the other splits' sums
+// and one more pass over the arg-max split's tokens.
 constexpr int kMaxSplits = 1024;
 
 __device__ __forceinline__ float block_sum256(float x, float* red) {
@@ -651,12 +652,31 @@ __device__ __forceinline__ int block_min256(int x, int* red) {
   return min(min(red[0], red[1]), min(red[2], red[3]));
 }
 
+// Sum over the 16 lanes of a DPP row, left in every lane of the row, with
+// VALU moves only: partners lane ^ 1 and lane ^ 2 (quad permutations), then
+// the mirrored lane in the half row and in the row.  After each step all
+// lanes of a quad (then of a half row) hold the same bits, so the mirrored
+// partner gives what the xor partner would, and the sum is the same in every
+// lane and equal to the xor butterfly's.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xb1, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4e, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xf, 0xf, false));
+  return x;
+}
+
 // abar = sum_{j != j*} e_j v_j / sum_{j != j*} e_j over the keys row r sees,
 // then the arg-max token's contribution p*^2 ||abar - v_j*||^2 (algebraically
 // equal to the closed form, without the cancellation in a - v_j* as p* -> 1).
-// 16 token groups x 16 d-slices per workgroup.
+// The first pass partitions the tokens among its splits, so every split but
+// the arg-max's (sstar) already holds its part of both sums free of j*: the
+// caller passes them combined (ao: this thread's column, Sxo), and only the
+// tokens of split sstar are streamed again here, j* left out.  16 token
+// groups x 16 d-slices per workgroup.
 template <int DP>
-__device__ float exclusion_term(const ScoreArgs& a, int g, int r, int jst, float m2, float S,
+__device__ float exclusion_term(const ScoreArgs& a, int g, int r, int jst, int sstar, float m2,
+                                float S, float ao, float Sxo,
                                 float* red /* [16][DP+1] */, float* rsx /* [16] */, float* tmp) {
   // 16 lanes per token: lane ds holds the 16-byte chunks ds, ds + 16, ... of
   // the row (8 bf16 each); 16 tokens at a time per workgroup, and each lane
@@ -681,18 +701,25 @@ __device__ float exclusion_term(const ScoreArgs& a, int g, int r, int jst, float
       qv[c][e] = dd < d ? bf2f(qrow[dd]) : 0.f;
       acc[c][e] = 0.f;
     }
+  // the split's tokens, in the order of its tiles: i -> token; the row sees
+  // tokens below jlim (the causal bound, and the end of the split or head)
+  const SplitTiles sp(a.n, sstar, a.splits, a.split_len);
+  const int64_t ntok = (int64_t)sp.ntiles * kTile, jlim = min(sp.jend, P + 1);
   float sx = 0.f;
-  for (int64_t j0 = tg; j0 <= P; j0 += 16 * U) {
+  for (int64_t i0 = tg; i0 < ntok; i0 += 16 * U) {
     u32x4 kx[U][NCH], vx[U][NCH];
+    int64_t jj[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t j = j0 + 16 * u;
+      const int64_t i = i0 + 16 * u;
+      const int64_t j = i < ntok ? sp.start((int)(i / kTile)) + i % kTile : jlim;
+      jj[u] = j;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const int ch = ds + 16 * c;
         kx[u][c] = u32x4{0u, 0u, 0u, 0u};
         vx[u][c] = u32x4{0u, 0u, 0u, 0u};
-        if (j <= P && ch * 8 < d) {   // d is a multiple of 8: chunks are whole
+        if (j < jlim && ch * 8 < d) {   // d is a multiple of 8: chunks are whole
           kx[u][c] = *reinterpret_cast<const u32x4*>(kg + j * d + ch * 8);
           vx[u][c] = *reinterpret_cast<const u32x4*>(vg + j * d + ch * 8);
         }
@@ -700,17 +727,14 @@ __device__ float exclusion_term(const ScoreArgs& a, int g, int r, int jst, float
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t j = j0 + 16 * u;
+      const int64_t j = jj[u];
       float dot = 0.f;
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
         for (int e = 0; e < 8; ++e) dot += qv[c][e] * elem(kx[u][c], e);
-      dot += __shfl_xor(dot, 1, 16);
-      dot += __shfl_xor(dot, 2, 16);
-      dot += __shfl_xor(dot, 4, 16);
-      dot += __shfl_xor(dot, 8, 16);
-      const float p = (j > P || j == jst) ? 0.f : ex2(dot * a.scale_log2 - m2);
+      dot = row16_sum(dot);
+      const float p = (j >= jlim || j == jst) ? 0.f : ex2(dot * a.scale_log2 - m2);
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
@@ -728,12 +752,12 @@ __device__ float exclusion_term(const ScoreArgs& a, int g, int r, int jst, float
   }
   if (ds == 0) rsx[tg] = sx;
   __syncthreads();
-  float tot_sx = 0.f;
+  float tot_sx = Sxo;
 #pragma unroll
   for (int k = 0; k < 16; ++k) tot_sx += rsx[k];
   float dist = 0.f;
   if (tid < d) {
-    float t = 0.f;
+    float t = ao;
     for (int k = 0; k < 16; ++k) t += red[k * (DP + 1) + tid];
     const float df = t / tot_sx - bf2f(vg[(size_t)jst * d + tid]);
     dist = df * df;
@@ -912,7 +936,38 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
   const bool singular = !nonfin && !(Sx > 0x1p-53f);
   const bool fix = !nonfin && !singular && Sx < kFixupThreshold;
   float cstar = (nonfin || singular) ? 0.f : dist / (Sx * Sx);
-  if (fix) cstar = exclusion_term<DP>(a, g, rg_row, jst, M, Sf, red, rsx, tmp);
+  if (fix) {
+    // sum_s f_s a_s over every split but the arg-max's (red4 was last read
+    // before the barrier above)
+    // (PF loads in flight per thread: all issued before any is used)
+    float4 acx = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (sum_lane) {
+      for (int s0 = sg; s0 < S; s0 += SG * PF) {
+        float4 x[PF];
+#pragma unroll
+        for (int k = 0; k < PF; ++k) {
+          const int s = s0 + SG * k;
+          x[k] = (s < S && s != sstar) ? *reinterpret_cast<const float4*>(pa + (size_t)s * kRows * DP)
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int k = 0; k < PF; ++k) {
+          const int s = s0 + SG * k;
+          const float f = (s < S && s != sstar) ? sm_f[s] : 0.f;
+          acx.x += x[k].x * f; acx.y += x[k].y * f; acx.z += x[k].z * f; acx.w += x[k].w * f;
+        }
+      }
+      red4[sg * CG + cg] = acx;
+    }
+    __syncthreads();
+    float ao = 0.f;
+    if (tid < DP) {
+      const float* rr = reinterpret_cast<const float*>(red4);
+#pragma unroll
+      for (int k = 0; k < SG; ++k) ao += rr[k * DP + tid];
+    }
+    cstar = exclusion_term<DP>(a, g, rg_row, jst, sstar, M, Sf, ao, Sxo, red, rsx, tmp);
+  }
   if (tid == 0) {
     a.rs.m2[ro] = M;
     a.rs.S[ro] = Sf;

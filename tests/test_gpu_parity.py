@@ -209,6 +209,25 @@ def test_near_singular_rows_match(ctx, pstar, n, d):
     _full_check(ctx, q, k, v, 1, max(1, n // 4), f"p*={pstar} n={n} d={d}")
 
 
+def test_near_singular_heads_of_every_kind(ctx):
+    """Four KV heads, four row groups each (G = 16, w = 8), every row peaked on
+    one key placed differently per head: the first tile (p* = 0.999), inside
+    the window so that rows t < 3 do not see it (p* = 0.95 for the rest), mid
+    head below the fixup threshold (p* = 0.5), and the ragged last tile
+    (p* = 1 - 1e-7).  Only the split holding the arg-max is streamed again for
+    the fixed rows; the result must still be the exact exclusion."""
+    Hq, Hkv, d, w, n = 64, 4, 128, 8, 20011
+    rng = np.random.default_rng(17)
+    q = np.zeros((Hq, w, d), np.float32); q[:, :, 0] = 1.0
+    k = np.zeros((Hkv, n, d), np.float32); k[:, :, 1:] = rng.standard_normal((Hkv, n, d - 1))
+    v = rng.standard_normal((Hkv, n, d)).astype(np.float32)
+    for g, (pstar, j) in enumerate([(0.999, 7), (0.95, n - w + 3), (0.5, n // 2),
+                                    (1 - 1e-7, n - 10)]):
+        k[g, j, 0] = math.log(pstar * (n - 1) / (1 - pstar)) * math.sqrt(d)
+    q, k, v = wl.bf16_bits(q), wl.bf16_bits(k), wl.bf16_bits(v)
+    _full_check(ctx, q, k, v, 7, n // 4, "peaked heads G=16 w=8 n=20011")
+
+
 def test_tied_maxima_across_splits(ctx):
     """Three copies of the dominant key (each holding ~30 % of every row's
     mass) in tiles that the first pass gives to different splits, the lowest
