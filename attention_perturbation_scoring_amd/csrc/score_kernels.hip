@@ -617,7 +617,7 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
 }
 
 // ----------------------------------------------------------------- merge --
-// One workgroup per (KV head, row).  Every split's statistics and the first
+// One workgroup per (KV head, window row).  Every split's statistics and the first
 // partial sums of a are fetched in one round trip; the maximum and its split
 // come from one packed reduction; every reduction has a fixed order (bitwise
 // reproducible); a is summed by float4 column group with the splits
@@ -796,19 +796,27 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
   __shared__ float tmp[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   // virtual head hv = (KV head g, row group); r is the row within the group and
-  // rg_row the window query row within the KV head
-  const int hv = blockIdx.x / kRows, r = blockIdx.x % kRows;
+  // rg_row the window query row within the KV head.  A group has RB =
+  // min(32, M) workgroups: with fewer than 32 window rows per KV head, the
+  // workgroup of row r also zeroes the padded rows r + RB, r + 2 RB, ... of
+  // its group, which have no window row to merge.
+  const int RB = min(kRows, a.M);
+  const int hv = blockIdx.x / RB, r = blockIdx.x % RB;
   const int g = hv / a.R, rg_row = kRows * (hv % a.R) + r;
   const size_t ro = (size_t)hv * kRows + r;
-  if (rg_row >= a.M) {  // padded rows: zero operands so pass 2's MFMA rows stay inert
+  auto zero_row = [&](size_t rz) {   // padded rows: zero operands so pass 2's MFMA rows stay inert
     for (int dd = tid; dd < DP; dd += kThreads) {
-      a.rs.a_hi[ro * DP + dd] = 0;
-      a.rs.a_lo[ro * DP + dd] = 0;
+      a.rs.a_hi[rz * DP + dd] = 0;
+      a.rs.a_lo[rz * DP + dd] = 0;
     }
     if (tid == 0) {
-      a.rs.m2[ro] = 0.f; a.rs.lse2[ro] = INFINITY; a.rs.S[ro] = 1.f; a.rs.an2[ro] = 0.f;
-      a.rs.cstar[ro] = 0.f; a.rs.jstar[ro] = -1; a.rs.fix[ro] = 0;
+      a.rs.m2[rz] = 0.f; a.rs.lse2[rz] = INFINITY; a.rs.S[rz] = 1.f; a.rs.an2[rz] = 0.f;
+      a.rs.cstar[rz] = 0.f; a.rs.jstar[rz] = -1; a.rs.fix[rz] = 0;
     }
+  };
+  for (int rp = r + RB; rp < kRows; rp += RB) zero_row((size_t)hv * kRows + rp);
+  if (rg_row >= a.M) {   // the last group's rows past M (M > 32 only)
+    zero_row(ro);
     return;
   }
   const int S = a.splits;
@@ -1621,7 +1629,7 @@ static hipError_t launch_score_dp(void* ctx, const ScoreArgs& a, hipStream_t s) 
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   prof_begin(ctx, "merge", s);
-  hipLaunchKernelGGL(merge_kernel<DP>, dim3(a.Hkv * a.R * kRows), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(merge_kernel<DP>, dim3(a.Hkv * a.R * (a.M < kRows ? a.M : kRows)), dim3(kThreads), 0, s, a);
   prof_end(ctx, "merge", s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
