@@ -101,6 +101,57 @@ def time_layer_select(ctx, scores, Hkv, n, budget, stream, args):
     return 1e3 * tot / max(cnt // 2, 1)
 
 
+def plant_peaked_key(cfg, inp, pstar=0.9999):
+    """The layer's K with one key per KV head set so that every window row of
+    the head puts probability ~pstar on it: for head g, the least-squares (here
+    exact, G*w < d) solution b of Q_g b = ln(pstar (n-1) / (1-pstar)) sqrt(d),
+    rounded to bf16, at a token every window row sees.  Rows whose arg-max
+    holds more than ~0.94 take the exact exclusion fixup.  Returns the bf16
+    bits of K and the planted token."""
+    import math
+    import numpy as np
+    from attention_perturbation_scoring_amd import workload as wl
+    G, d, n, w = cfg.Hq // cfg.Hkv, cfg.d, cfg.n, cfg.w
+    q = wl.bf16_to_f32(inp["q"]).astype(np.float64)
+    k = inp["k"].copy()
+    jp = min(5000, n - w - 1)
+    logit = math.log(pstar * (n - 1) / (1.0 - pstar)) * math.sqrt(d)
+    for g in range(cfg.Hkv):
+        Q = q[g * G:(g + 1) * G].reshape(-1, d)
+        b, *_ = np.linalg.lstsq(Q, np.full(Q.shape[0], logit), rcond=None)
+        k[g, jp] = wl.bf16_bits(b.astype(np.float32))
+    return k, jp
+
+
+def time_peaked_rows(ctx, cfg, inp, dev, v_dev, scores, stream):
+    """Per-kernel HIP-event times of dropkv_score on the layer with a peaked
+    key planted in every KV head (every window row takes the fixup)."""
+    import torch
+    from attention_perturbation_scoring_amd import dropkv
+    k, jp = plant_peaked_key(cfg, inp)
+    qd, kd = dev(inp["q"]), dev(k)
+    Hq, Hkv, d, n, w, pool = cfg.Hq, cfg.Hkv, cfg.d, cfg.n, cfg.w, cfg.pool
+    ctx.score(qd, kd, v_dev, n, w, Hq, Hkv, d, pool, scores, stream)
+    status = ctx.sync(stream)
+    if status != dropkv.OK:
+        raise SystemExit(f"peaked rows: device status {dropkv.strerror(status)}")
+    ctx.profile(True)
+    ctx.profile_reset()
+    for _ in range(3):
+        ctx.score(qd, kd, v_dev, n, w, Hq, Hkv, d, pool, scores, stream)
+    torch.cuda.synchronize()
+    us = {}
+    for name in ("pass1", "merge", "pass2"):
+        tot, cnt = ctx.profile_read(name)
+        if cnt:
+            us[name] = round(1e3 * tot / cnt, 2)
+    ctx.profile(False)
+    ctx.check(stream)
+    return {"what": "dropkv_score with every window row's arg-max planted at p* > 0.94 "
+                    "(exact exclusion fixup on every row)",
+            "planted_token": jp, "kernel_us": us}
+
+
 def host_cpu() -> str:
     """The host's CPU model and logical CPU count, for the baseline's description."""
     model = "unknown CPU"
@@ -286,6 +337,12 @@ def run(args):
     if L == 1:
         layer_select_us = time_layer_select(ctx, scores, Hkv, n, budget, stream, args)
 
+    # ---- the same layer with every window row peaked (the exclusion fixup) ----
+    peaked_rows = None
+    if L == 1:
+        log("[bench] peaked rows")
+        peaked_rows = time_peaked_rows(ctx, cfg, inp, dev, copies[0][2], scores, stream)
+
     # ---- per-call distribution with the caches flushed before every call ----
     # Streaming 1 GiB through the caches evicts the 4 MB L2s and the 256 MB
     # last-level cache, so each call starts cold.  A read flush leaves clean
@@ -384,6 +441,7 @@ def run(args):
         "profiled_ms_per_step": prof_wall * 1e3 / args.steps,
         "attention_mode": attention_mode,
         "layer_select_us": layer_select_us,
+        "peaked_rows": peaked_rows,
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:

@@ -67,3 +67,28 @@ def test_traffic_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     # kernel's name must not be mistaken for pass 1's
     assert t["kernels"]["pass1"]["bytes_per_launch"] == pytest.approx((2 * 1100 + 20) * 1024)
     assert t["kernels"]["attn_pass1"]["bytes_per_launch"] == pytest.approx((2 * 50 + 5) * 1024)
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama4k"])
+def test_planted_key_peaks_every_window_row(name):
+    """The peaked-rows measurement's input: in every KV head the planted token
+    is every window row's arg-max, at p* above the 0.94 fixup threshold."""
+    import math
+    import numpy as np
+    from attention_perturbation_scoring_amd import workload as wl
+    cfg = wl.CONFIGS[name]
+    inp = wl.make_layer(cfg, cfg.seed)
+    k, jp = bench.plant_peaked_key(cfg, inp)
+    q = wl.bf16_to_f32(inp["q"]).astype(np.float64)
+    kf = wl.bf16_to_f32(k).astype(np.float64)
+    G, d, n, w = cfg.Hq // cfg.Hkv, cfg.d, cfg.n, cfg.w
+    for h in range(cfg.Hq):
+        logits = q[h] @ kf[h // G].T / math.sqrt(d)      # [w][n]
+        for t in range(w):
+            row = logits[t, : n - w + t + 1]             # the keys window query t sees
+            p = np.exp(row - row.max())
+            p /= p.sum()
+            assert int(np.argmax(p)) == jp and p[jp] > 0.95, (name, h, t, p[jp])
+    # only the planted token changed
+    diff = np.argwhere(k != inp["k"])
+    assert set(diff[:, 1].tolist()) <= {jp}
