@@ -16,8 +16,10 @@
 
 namespace dropkv {
 
-// Selection is exact integer arithmetic on order-preserving keys.  When a
-// team of ceil(n / 16384) workgroups per head fits on the device at once, one
+// Selection is exact integer arithmetic on order-preserving keys.  A head of
+// at most 16384 tokens is one workgroup (select_solo): the three radix rounds,
+// the ties and the ordered emission all stay in LDS.  When a larger head's
+// team of ceil(n / 16384) workgroups fits on the device at once, one
 // kernel does everything with each workgroup's keys held in registers: a 12-bit
 // histogram round over the team (device-scope adds, then a per-head barrier)
 // finds the bin holding the k-th smallest key; the team then exchanges that
@@ -741,6 +743,104 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
   }
 }
 
+// A head that fits one workgroup (n <= kFusedBlock): select_fused's steps for a
+// team of one, with every histogram in LDS, so no device-scope traffic, no
+// barrier beyond the workgroup's and no shared scratch (the fused kernel's
+// counters are left as they are).
+__global__ __launch_bounds__(kFusedThreads) void select_solo(SelArgs a) {
+  constexpr int NW = kFusedThreads / 64;
+  __shared__ uint32_t h[kBins1];
+  __shared__ uint32_t sh[NW];
+  __shared__ uint32_t s_bin, s_below;
+  const bool stop = latched(a.latch);   // tested once the keys have been requested
+  const int g = blockIdx.x, tid = threadIdx.x;
+
+  // this thread's kFusedPer consecutive tokens, as order keys (0 past the end)
+  const float* sg = a.scores + (size_t)g * a.n;
+  const int64_t base = (int64_t)tid * kFusedPer;
+  const int nv = (int)max((int64_t)0, min((int64_t)kFusedPer, a.n - base));
+  uint32_t key[kFusedPer];
+  if (nv == kFusedPer && (((size_t)g * a.n + base) & 3) == 0) {   // 16-byte aligned run
+#pragma unroll
+    for (int q = 0; q < kFusedPer / 4; ++q) {
+      const float4 x = *reinterpret_cast<const float4*>(sg + base + 4 * q);
+      key[4 * q + 0] = order_key(x.x);
+      key[4 * q + 1] = order_key(x.y);
+      key[4 * q + 2] = order_key(x.z);
+      key[4 * q + 3] = order_key(x.w);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kFusedPer; ++i) key[i] = i < nv ? order_key(sg[base + i]) : 0u;
+  }
+  if (stop) return;   // nothing has been written yet
+
+  // the k-th smallest key T, digits of 12, 10 and 10 bits; the slots past the
+  // end hold key 0 and rank first, so the rank sought moves up by their number
+  const uint32_t pad = (uint32_t)kFusedBlock - (uint32_t)a.n;
+  uint32_t prefix = 0u, mask = 0u;
+  uint32_t krem = (uint32_t)(a.n - a.budget) + pad;
+#pragma unroll
+  for (int r = 0; r < 3; ++r) {
+    const int shift = r == 0 ? 20 : (r == 1 ? 10 : 0);
+    const int nb = r == 0 ? kBins1 : 1024;
+    for (int i = tid; i < nb; i += kFusedThreads) h[i] = 0u;
+    __syncthreads();
+    // the slots past the end count once, while the prefix still admits key 0;
+    // real keys add once per run of one bin (pooling makes plateaus), so
+    // neither piles same-address LDS atomics onto one bin
+    if (tid == 0 && prefix == 0u && pad) atomicAdd(&h[0], pad);
+    uint32_t run = 0u, rbin = 0u;
+#pragma unroll
+    for (int i = 0; i < kFusedPer; ++i) {
+      const uint32_t bin = (key[i] >> shift) & (uint32_t)(nb - 1);
+      const bool in = i < nv && (key[i] & mask) == prefix;
+      if (in && run && bin == rbin) {
+        ++run;
+      } else if (in) {
+        if (run) atomicAdd(&h[rbin], run);
+        rbin = bin;
+        run = 1u;
+      }
+    }
+    if (run) atomicAdd(&h[rbin], run);
+    __syncthreads();
+    find_bin<NW>(h, nb, krem, &s_bin, &s_below, sh);
+    prefix |= s_bin << shift;
+    mask |= (uint32_t)(nb - 1) << shift;
+    krem -= s_below;
+    __syncthreads();
+  }
+  const uint32_t T = prefix, need = krem;   // need >= 1 of the keys equal to T are evicted
+
+  // ordered emission (thread order is index order): the first `need` ties go
+  uint32_t gt = 0u, nt = 0u;
+#pragma unroll
+  for (int i = 0; i < kFusedPer; ++i) {
+    gt += key[i] > T ? 1u : 0u;
+    nt += key[i] == T ? 1u : 0u;
+  }
+  uint32_t tot;   // both counts are below 2^16 per head: scan them packed
+  const uint32_t pre = block_exscan<NW>(gt | (nt << 16), &tot, sh);
+  const uint32_t gt_pre = pre & 0xffffu, tie_pre = pre >> 16;
+  uint32_t rank = tie_pre, keepbits = 0u;
+#pragma unroll
+  for (int i = 0; i < kFusedPer; ++i) {
+    const bool tie = key[i] == T;
+    const bool keepit = key[i] > T || (tie && rank >= need);
+    rank += tie ? 1u : 0u;
+    keepbits |= keepit ? 1u << i : 0u;
+  }
+  uint32_t pos = gt_pre + (tie_pre > need ? tie_pre - need : 0u);
+  int32_t* kg = a.keep + (size_t)g * a.budget;
+  while (keepbits) {   // one store per kept token, in index order
+    const int i = __builtin_ctz(keepbits);
+    keepbits &= keepbits - 1u;
+    if (pos < (uint32_t)a.budget) kg[pos] = (int32_t)(base + i);
+    ++pos;
+  }
+}
+
 __global__ __launch_bounds__(256) void select_all_kernel(int32_t* keep, int64_t n, int64_t total,
                                                          const uint32_t* latch) {
   if (latched(latch)) return;
@@ -886,6 +986,11 @@ hipError_t launch_select(void* ctx, const float* scores, int Hkv, int64_t n, int
   a.sc = sc;
   prof_begin(ctx, "select", s);
   const int64_t team = (n + kFusedBlock - 1) / kFusedBlock;
+  if (team == 1) {   // one workgroup per head: no team, no co-residency needed
+    hipLaunchKernelGGL(select_solo, dim3(Hkv), dim3(kFusedThreads), 0, s, a);
+    prof_end(ctx, "select", s);
+    return hipGetLastError();
+  }
   if (team <= kFusedThreads && (int64_t)Hkv * team <= fused_capacity()) {
     SelArgs f = a;
     f.nblk = (int)team;

@@ -109,7 +109,9 @@ def test_llama_configs(ctx, name):
 def test_select_exact_on_oracle_scores(ctx):
     """dropkv_select on the oracle's (fp32-rounded) scores gives the oracle's keep list."""
     rng = np.random.default_rng(3)
-    for n, Hkv in ((1, 1), (50, 3), (4097, 2), (70000, 2)):
+    # one-workgroup heads (n <= 16384, the last two at and just below the
+    # limit) and a team of five (70000)
+    for n, Hkv in ((1, 1), (50, 3), (4097, 2), (16384, 2), (16383, 3), (70000, 2)):
         s = rng.integers(0, 40, size=(Hkv, n)).astype(np.float32)      # heavy ties
         s[:, : n // 3] = rng.random((Hkv, n // 3)).astype(np.float32)
         s[:, -min(4, n):] = np.inf
@@ -131,10 +133,12 @@ def test_select_exact_on_oracle_scores(ctx):
             np.testing.assert_array_equal(got, want, err_msg=f"n={n} budget={budget}")
 
 
+@pytest.mark.parametrize("n", [20000, 5000])
 @pytest.mark.parametrize("kind", ["all_zero", "all_equal", "two_values", "negatives"])
-def test_select_heavy_ties_and_signs(ctx, kind):
-    """Threshold bins holding more than the candidate buffer, and negative keys."""
-    n, Hkv = 20000, 2
+def test_select_heavy_ties_and_signs(ctx, kind, n):
+    """Threshold bins holding more than the candidate buffer, and negative keys;
+    a team of two workgroups (20000) and one workgroup (5000) per head."""
+    Hkv = 2
     rng = np.random.default_rng(11)
     if kind == "all_zero":
         s = np.zeros((Hkv, n), np.float32)
@@ -147,18 +151,19 @@ def test_select_heavy_ties_and_signs(ctx, kind):
         s[0, :50] = -0.0
     s[:, -8:] = np.inf
     sd = torch.from_numpy(s).cuda()
-    for budget in (8, 100, 9999, 19999):
+    for budget in (8, 100, n // 2 - 1, n - 1):
         keep = torch.full((Hkv, budget), -9, dtype=torch.int32, device="cuda")
         ctx.select(sd, Hkv, n, budget, keep)
         assert ctx.sync() == dropkv.OK
         np.testing.assert_array_equal(keep.cpu().numpy(), orc.select(s.astype(np.float64), budget),
-                                      err_msg=f"{kind} budget={budget}")
+                                      err_msg=f"{kind} n={n} budget={budget}")
 
 
 def test_select_multi_launch_path(ctx):
-    """More blocks of 4096 tokens than the device holds at once (4096 > 256 CUs x
-    at most 10): selection runs as four launches instead of one, same result."""
-    Hkv, n = 2048, 8192
+    """Heads of two workgroups each, more workgroups than the device holds at
+    once (2800 > 256 CUs x at most 10): selection runs as the multi-launch path
+    instead of one launch, same result."""
+    Hkv, n = 1400, 16500
     rng = np.random.default_rng(21)
     s = rng.integers(0, 300, size=(Hkv, n)).astype(np.float32)
     s[:, : n // 2] += rng.random((Hkv, n // 2)).astype(np.float32)
