@@ -162,6 +162,13 @@ constexpr int kTargetWG2 = DROPKV_P2_TARGET;   // pass-2 workgroups aimed for ov
 // through the exact exclusion kernel instead of the fp32 output a.
 constexpr float kFixupThreshold = 0.0625f;
 
+// Pass 2 takes ||a - v||^2 from the expansion ||a||^2 - 2 a.v + ||v||^2 unless
+// that value is below this fraction of ||a||^2 + ||v||^2: there the expansion's
+// rounding (a split into two bf16 parts, fp32 sums: about 3e-5 of ||a||^2 +
+// ||v||^2 at worst) could exceed 1e-3 of the result, and the distance is summed
+// directly instead, as ||(a - v_j*) + (v_j* - v)||^2.
+constexpr float kCancelFrac = 0.0625f;
+
 // Per-row (window query) state produced by the merge, consumed by pass 2.
 struct RowState {
   float* m2;      // [Hkv][32] running max of the logits, log2 units
@@ -173,6 +180,8 @@ struct RowState {
   int* fix;       // [Hkv][32] 1 if the arg-max term needs the exclusion kernel
   u16* a_hi;      // [Hkv][32][DP] bf16 high part of a
   u16* a_lo;      // [Hkv][32][DP] bf16 remainder a - a_hi
+  float* ares;    // [Hkv][32][DP] a - v_j* in fp32: from the exact exclusion sum for
+                  // rows whose arg-max holds p* > ~0.94, else from a (zero past d)
 };
 
 struct Partials {

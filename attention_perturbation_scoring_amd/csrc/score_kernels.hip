@@ -674,9 +674,12 @@ __device__ __forceinline__ float row16_sum(float x) {
 // caller passes them combined (ao: this thread's column, Sxo), and only the
 // tokens of split sstar are streamed again here, j* left out.  16 token
 // groups x 16 d-slices per workgroup.
+// It also overwrites the row's a - v_j* (ares_row, d values) with the exact
+// (1 - p*) (abar - v_j*), 1 - p* = Sx / S, which pass 2 uses for tokens whose
+// value row lies close to a.
 template <int DP>
 __device__ float exclusion_term(const ScoreArgs& a, int g, int r, int jst, int sstar, float m2,
-                                float S, float ao, float Sxo,
+                                float S, float Sx, float ao, float Sxo, float* ares_row,
                                 float* red /* [16][DP+1] */, float* rsx /* [16] */, float* tmp) {
   // 16 lanes per token: lane ds holds the 16-byte chunks ds, ds + 16, ... of
   // the row (8 bf16 each); 16 tokens at a time per workgroup, and each lane
@@ -761,6 +764,7 @@ __device__ float exclusion_term(const ScoreArgs& a, int g, int r, int jst, int s
     for (int k = 0; k < 16; ++k) t += red[k * (DP + 1) + tid];
     const float df = t / tot_sx - bf2f(vg[(size_t)jst * d + tid]);
     dist = df * df;
+    ares_row[tid] = (Sx / S) * df;
   }
   dist = block_sum256(dist, tmp);
   const float pstar = 1.f / S;
@@ -808,6 +812,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
     for (int dd = tid; dd < DP; dd += kThreads) {
       a.rs.a_hi[rz * DP + dd] = 0;
       a.rs.a_lo[rz * DP + dd] = 0;
+      a.rs.ares[rz * DP + dd] = 0.f;
     }
     if (tid == 0) {
       a.rs.m2[rz] = 0.f; a.rs.lse2[rz] = INFINITY; a.rs.S[rz] = 1.f; a.rs.an2[rz] = 0.f;
@@ -924,6 +929,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
     const __bf16 lo = (__bf16)(avv - (float)hi);
     a.rs.a_hi[ro * DP + tid] = __builtin_bit_cast(u16, hi);
     a.rs.a_lo[ro * DP + tid] = __builtin_bit_cast(u16, lo);
+    // a - v_j* (zero past d); rows that take the exclusion sum below overwrite it
+    a.rs.ares[ro * DP + tid] = avv - vstar;
     // row r of head g is window query (g * G + r / w, r % w): [Hq][w][d] order
     if (a.out_a && tid < a.d) a.out_a[((size_t)g * a.M + rg_row) * a.d + tid] = avv;
     if (tid < a.d && jst >= 0) {
@@ -974,7 +981,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
 #pragma unroll
       for (int k = 0; k < SG; ++k) ao += rr[k * DP + tid];
     }
-    cstar = exclusion_term<DP>(a, g, rg_row, jst, sstar, M, Sf, ao, Sxo, red, rsx, tmp);
+    cstar = exclusion_term<DP>(a, g, rg_row, jst, sstar, M, Sf, Sx, ao, Sxo, a.rs.ares + ro * DP, red,
+                               rsx, tmp);
   }
   if (tid == 0) {
     a.rs.m2[ro] = M;
@@ -1016,6 +1024,49 @@ constexpr size_t pass2_lds_base(int R) {
 template <int DP>
 constexpr size_t pass2_lds_bytes(int R) {
   return pass2_lds_base<DP>(R) + (pass2_vlds<DP>() ? (size_t)kWaves * kRows * RowLayout<DP>::ROWB : 0);
+}
+
+// ||a - v||^2 summed directly for one (row, token): the row's a is held as its
+// arg-max token's value row c = v_j* (bf16, from the cache) plus the fp32
+// difference ares = a - v_j*, so a - v = ares + (c - v), where c - v of two bf16
+// values is exact in fp32.  Used where the expansion could have cancelled
+// (value rows near a, e.g. copies of a dominant token's value row): a rare
+// path.  `vchunk(c)` gives the token's value columns 8c .. 8c + 7; ares and c
+// come from the row state and the cache (L2-resident), four chunks' loads in
+// flight at a time.
+template <int DP, typename VChunk>
+__device__ __forceinline__ float direct_dist(const float* __restrict__ ares,
+                                             const u16* __restrict__ crow, int d, VChunk vchunk) {
+  constexpr int CH = DP / 8, U = 4;
+  float s = 0.f;
+#pragma unroll 1
+  for (int c0 = 0; c0 < CH; c0 += U) {
+    u32x4 cx[U];
+    float4 r0[U], r1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = min(c0 + u, CH - 1);
+      cx[u] = *reinterpret_cast<const u32x4*>(crow + 8 * min(c, d / 8 - 1));
+      r0[u] = *reinterpret_cast<const float4*>(ares + 8 * c);
+      r1[u] = *reinterpret_cast<const float4*>(ares + 8 * c + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u;
+      if (c >= CH || 8 * c >= d) break;
+      const bf16x8 vx = vchunk(c);
+      const u32x4 cw = cx[u];
+      const float rv[8] = {r0[u].x, r0[u].y, r0[u].z, r0[u].w, r1[u].x, r1[u].y, r1[u].z, r1[u].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = cw[e >> 1];
+        const float ce = __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+        const float x = rv[e] + (ce - (float)vx[e]);
+        s = fmaf(x, x, s);
+      }
+    }
+  }
+  return s;
 }
 
 // NB8: 8-row blocks of the row group that can hold window rows (rows >= M have
@@ -1155,6 +1206,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
 #pragma unroll
       for (int v = 4 * NB8; v < 16; ++v) cc[v] = 0.f;
       float ovf = 0.f;   // becomes NaN if an expansion term overflowed fp32
+      uint32_t near = 0u;   // elements whose distance is summed directly (bit v)
 #pragma unroll
       for (int q4 = 0; q4 < NB8; ++q4) {
         // this lane's rows 8*q4 + 4*hh + 0..3 of the group
@@ -1167,9 +1219,14 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
           const int v = 4 * q4 + i;
           const float p = ex2(sacc[v] * a.scale_log2 - lv[i]);
           const float odds = p * __builtin_amdgcn_rcpf(1.f - p);
+          const float o2 = odds * odds;
           const float d0 = nv[i] - 2.f * av[v] + vn2;
           ovf = fmaf(d0, 0.f, ovf);
-          cc[v] = odds * odds * fmaxf(d0, 0.f);
+          // the expansion is kept where it cannot have cancelled (or where the
+          // contribution is zero anyway); the rest get o2 now, the distance later
+          const bool cancel = o2 > 0.f && d0 < kCancelFrac * (nv[i] + vn2);
+          near |= cancel ? 1u << v : 0u;
+          cc[v] = cancel ? o2 : o2 * fmaxf(d0, 0.f);
         }
       }
       if (tok_ok && !(ovf == 0.f)) flags |= LATCH_RANGE;
@@ -1179,7 +1236,9 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
         for (int v = 0; v < 16; ++v) {
           const int rv = kRows * rg + 8 * (v >> 2) + 4 * hh + (v & 3);   // row within the head
           const int lim = rv < a.M ? (int)(n - a.w + (rv % a.w)) : -1;
-          cc[v] = (tok_ok && itok <= lim) ? cc[v] : 0.f;
+          const bool ok = tok_ok && itok <= lim;
+          cc[v] = ok ? cc[v] : 0.f;
+          near &= ok ? ~0u : ~(1u << v);
         }
       }
       // the arg-max token of a row takes the value computed by the merge instead
@@ -1197,6 +1256,38 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
 #pragma unroll
           for (int v = 0; v < 16; ++v)
             if (v == vr) cc[v] = cs;
+          near &= ~(1u << vr);
+        }
+      }
+      if (__builtin_expect(__any(near != 0u), 0)) {
+        // value rows close to a (other than the arg-max's own): the exact
+        // distance for each such element
+        const size_t ro0 = ((size_t)g * R + rg) * kRows;
+        while (near) {
+          const int v = __builtin_ctz(near);
+          near &= near - 1u;
+          const int rho = 8 * (v >> 2) + 4 * hh + (v & 3);   // row within the group
+          const int js = js_s[rg * kRows + rho];
+          // (a row without an arg-max is a rejected input: nothing to read)
+          float dist = 0.f;
+          if (js >= 0) {
+            const float* ar = a.rs.ares + (ro0 + rho) * DP;
+            const u16* cr = vg + (size_t)js * d;
+            if constexpr (pass2_vlds<DP>()) {
+              // this token's value row is still in the wave's LDS slot
+              const unsigned char* vslot =
+                  smem_raw + pass2_lds_base<DP>(R) + (size_t)wid * kRows * L::ROWB;
+              dist = direct_dist<DP>(ar, cr, d, [&](int c) { return lds8<DP>(vslot, r, c); });
+            } else {
+              const u16* vrow = vg + (size_t)tok * d;
+              dist = direct_dist<DP>(ar, cr, d, [&](int c) {
+                return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vrow + 8 * c));
+              });
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            if (u == v) cc[u] *= dist;
         }
       }
       float sum = 0.f;
@@ -1590,7 +1681,7 @@ size_t score_scratch_bytes(int Hkv, int splits, int DP) {
   const size_t prow = (size_t)Hkv * splits * kRows;
   const size_t rrow = (size_t)Hkv * kRows;
   return align256(prow * 4) * 5 + align256(prow * DP * 4) + align256(rrow * 4) * 7 +
-         align256(rrow * DP * 2) * 2;
+         align256(rrow * DP * 2) * 2 + align256(rrow * DP * 4);
 }
 
 void carve_scratch(void* base, int Hkv, int splits, int DP, Partials* p, RowState* rs) {
@@ -1613,6 +1704,7 @@ void carve_scratch(void* base, int Hkv, int splits, int DP, Partials* p, RowStat
   rs->fix = (int*)take(rrow * 4);
   rs->a_hi = (u16*)take(rrow * DP * 2);
   rs->a_lo = (u16*)take(rrow * DP * 2);
+  rs->ares = (float*)take(rrow * DP * 4);
 }
 
 template <int DP, bool FULLD>

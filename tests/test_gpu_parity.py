@@ -236,6 +236,70 @@ def test_near_singular_heads_of_every_kind(ctx):
     np.testing.assert_array_equal(s.view(np.uint32), again[1].view(np.uint32))
 
 
+def _peaked_with_copies(seed, Hq, Hkv, d, n, w, pstar, jstar, copies, near=(), near_scale=1e-2):
+    """Every window row puts probability pstar on key jstar (logit gap from its
+    key's first channel); the value rows at `copies` are exact copies of
+    v_jstar (identical tokens have identical value rows) and those at `near`
+    are v_jstar plus near_scale * N(0, 1) before the bf16 cast."""
+    rng = np.random.default_rng(seed)
+    q = np.zeros((Hq, w, d), np.float32); q[:, :, 0] = 1.0
+    k = np.zeros((Hkv, n, d), np.float32); k[:, :, 1:] = rng.standard_normal((Hkv, n, d - 1))
+    k[:, jstar, 0] = math.log(pstar * (n - 1) / (1 - pstar)) * math.sqrt(d)
+    v = rng.standard_normal((Hkv, n, d)).astype(np.float32)
+    v = wl.bf16_to_f32(wl.bf16_bits(v))
+    for j in copies:
+        v[:, j] = v[:, jstar]
+    for j in near:
+        v[:, j] = v[:, jstar] + near_scale * rng.standard_normal((Hkv, d)).astype(np.float32)
+    return wl.bf16_bits(q), wl.bf16_bits(k), wl.bf16_bits(v)
+
+
+@pytest.mark.parametrize("pstar", [0.99, 0.999, 0.9999])
+@pytest.mark.parametrize("d", [96, 128, 256])
+def test_value_rows_copying_the_argmax(ctx, pstar, d):
+    """Tokens whose value row copies the dominant token's, one of them inside
+    the window, and near copies: for them a - v is tiny next to ||a|| and ||v||,
+    the expansion ||a||^2 - 2 a.v + ||v||^2 would cancel, and the distance must
+    come out of the exact difference (notes, "Core equation": Delta_j =
+    p_j/(1 - p_j) (a - v_j) for every token)."""
+    n, w = 3000, 4
+    js = n // 3
+    copies = (js + 17, n // 2 + 5, n - 2)      # n - 2 lies in the window (w = 4)
+    near = (js - 40, 2 * n // 3)
+    q, k, v = _peaked_with_copies(31 + d, 2, 1, d, n, w, pstar, js, copies, near)
+    got = _full_check(ctx, q, k, v, 1, n // 4, f"copies of v* p*={pstar} d={d}")
+    assert got is not None
+    s, want, _, _ = got
+    # the copies score far below their neighbours and match one by one
+    for j in copies[:2] + near:
+        assert abs(s[0, j] - want[0, j]) <= 2e-3 * want[0, j] + H.FLT_MIN, j
+
+
+def test_value_rows_copying_the_argmax_llama_shape(ctx):
+    """The same at the headline head geometry (G = 4, w = 8: 32 rows), a long head
+    over several second-pass chunks, copies of v* in three chunks and pooling."""
+    n, w, d = 20011, 8, 128
+    js = 4100
+    q, k, v = _peaked_with_copies(77, 32, 8, d, n, w, 0.999, js, (5, js + 1, 9000, n - 5),
+                                  (12000,))
+    _full_check(ctx, q, k, v, 7, n // 20, "copies of v*, 32 rows, n=20011")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_value_rows_with_common_offset(ctx, d):
+    """Every value row is a shared offset plus a small per-token part
+    (V = 4 mu + 0.05 N(0, 1)): ||a - v_j|| is small against ||a|| and ||v_j|| for
+    every token at once, so every distance takes the direct sum."""
+    Hq, Hkv, n, w = 8, 2, 3000, 4
+    rng = np.random.default_rng(90 + d)
+    q = rng.standard_normal((Hq, w, d), dtype=np.float32)
+    k = rng.standard_normal((Hkv, n, d), dtype=np.float32)
+    mu = rng.standard_normal((Hkv, 1, d), dtype=np.float32)
+    v = (4.0 * mu + 0.05 * rng.standard_normal((Hkv, n, d))).astype(np.float32)
+    q, k, v = wl.bf16_bits(q), wl.bf16_bits(k), wl.bf16_bits(v)
+    _full_check(ctx, q, k, v, 5, n // 10, f"common value offset d={d}")
+
+
 def test_tied_maxima_across_splits(ctx):
     """Three copies of the dominant key (each holding ~30 % of every row's
     mass) in tiles that the first pass gives to different splits, the lowest
