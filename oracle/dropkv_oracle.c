@@ -156,41 +156,63 @@ int oracle_raw_scores(const uint16_t *q, const uint16_t *k, const uint16_t *v, i
     for (int64_t i = 0; i < (int64_t)hkv * n * d; ++i)
         if (!bf16_is_finite(k[i]) || !bf16_is_finite(v[i])) return ORC_ENONFINITE;
 
-    int status = ORC_OK;
+    /* Work is spread over the window rows (h, t) of every KV head: each row
+     * writes its contributions to a buffer of its own, and each head's rows are
+     * then added in (h, t) order -- the order a single thread walking the rows
+     * would add them in, so the result does not depend on the thread count. */
     if (nthreads < 1) nthreads = 1;
-#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
-    for (int g = 0; g < hkv; ++g) {
-        double *K = malloc(sizeof(double) * (size_t)n * d);
-        double *V = malloc(sizeof(double) * (size_t)n * d);
-        double *l = malloc(sizeof(double) * (size_t)n);
-        double *a = malloc(sizeof(double) * (size_t)d);
-        double *abar = malloc(sizeof(double) * (size_t)d);
-        double *qq = malloc(sizeof(double) * (size_t)d);
-        double *rg = raw + (size_t)g * n;
-        int local = ORC_OK;
-        if (!K || !V || !l || !a || !abar || !qq) local = ORC_ENOMEM;
-        if (local == ORC_OK) {
+    const int M = G * w;                      /* window rows per KV head */
+    const int64_t units = (int64_t)hkv * M;
+    double *Kd = malloc(sizeof(double) * (size_t)hkv * n * d);
+    double *Vd = malloc(sizeof(double) * (size_t)hkv * n * d);
+    double *rows = malloc(sizeof(double) * (size_t)units * n);
+    int status = (Kd && Vd && rows) ? ORC_OK : ORC_ENOMEM;
+    if (status == ORC_OK) {
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+        for (int g = 0; g < hkv; ++g)
             for (int64_t i = 0; i < n * d; ++i) {
-                K[i] = bf16_to_double(k[(size_t)g * n * d + i]);
-                V[i] = bf16_to_double(v[(size_t)g * n * d + i]);
+                Kd[(size_t)g * n * d + i] = bf16_to_double(k[(size_t)g * n * d + i]);
+                Vd[(size_t)g * n * d + i] = bf16_to_double(v[(size_t)g * n * d + i]);
             }
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+        for (int64_t u = 0; u < units; ++u) {
+            const int g = (int)(u / M), row = (int)(u % M);
+            const int h = g * G + row / w, t = row % w;
+            double *l = malloc(sizeof(double) * (size_t)n);
+            double *a = malloc(sizeof(double) * (size_t)d);
+            double *abar = malloc(sizeof(double) * (size_t)d);
+            double *qq = malloc(sizeof(double) * (size_t)d);
+            double *ru = rows + (size_t)u * n;
+            int local = ORC_OK;
+            if (!l || !a || !abar || !qq) local = ORC_ENOMEM;
+            if (local == ORC_OK) {
+                for (int64_t j = 0; j < n; ++j) ru[j] = 0.0;
+                for (int i = 0; i < d; ++i) qq[i] = bf16_to_double(q[((size_t)h * w + t) * d + i]);
+                const int64_t P = n - w + t; /* last key this query sees */
+                local = score_one_row(qq, Kd + (size_t)g * n * d, Vd + (size_t)g * n * d, P, d, l,
+                                      a, abar, ru);
+            }
+            free(l); free(a); free(abar); free(qq);
+            if (local != ORC_OK) {
+#pragma omp critical
+                { if (local > status) status = local; }
+            }
+        }
+    }
+    if (status == ORC_OK) {
+        /* raw[g][j] = (1/G) * sum over the group's rows in (h, t) order */
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+        for (int g = 0; g < hkv; ++g) {
+            double *rg = raw + (size_t)g * n;
             for (int64_t j = 0; j < n; ++j) rg[j] = 0.0;
-            for (int h = g * G; h < (g + 1) * G && local == ORC_OK; ++h) {
-                for (int t = 0; t < w && local == ORC_OK; ++t) {
-                    for (int i = 0; i < d; ++i)
-                        qq[i] = bf16_to_double(q[((size_t)h * w + t) * d + i]);
-                    const int64_t P = n - w + t; /* last key this query sees */
-                    local = score_one_row(qq, K, V, P, d, l, a, abar, rg);
-                }
+            for (int row = 0; row < M; ++row) {
+                const double *ru = rows + ((size_t)g * M + row) * n;
+                for (int64_t j = 0; j < n; ++j) rg[j] += ru[j];
             }
             for (int64_t j = 0; j < n; ++j) rg[j] /= (double)G;
         }
-        free(K); free(V); free(l); free(a); free(abar); free(qq);
-        if (local != ORC_OK) {
-#pragma omp critical
-            { if (local > status) status = local; }
-        }
     }
+    free(Kd); free(Vd); free(rows);
     return status;
 }
 

@@ -18,8 +18,8 @@ MUTANTS = {
     "one_minus_p_sign": ("(S - l[j]) / S;", "(S + l[j]) / S;"),
     "causal_off_by_one": ("const int64_t P = n - w + t; /* last key", "const int64_t P = n - w + t - 1; /* last key"),
     "no_head_mean": ("rg[j] /= (double)G;", "rg[j] /= 1.0;"),
-    "strided_head_groups": ("for (int h = g * G; h < (g + 1) * G && local == ORC_OK; ++h) {",
-                            "for (int h = g; h < hq && local == ORC_OK; h += hkv) {"),
+    "strided_head_groups": ("const int h = g * G + row / w, t = row % w;",
+                            "const int h = g + (row / w) * hkv, t = row % w;"),
     "argmax_form_unsquared_p": ("c = pj * pj * dist2;", "c = pj * dist2;"),
     "residual_sign_abar": ("const double r = abar[i] - V[j * d + i];", "const double r = abar[i] + V[j * d + i];"),
     "no_sqrt_d": ("l[j] = s * inv_sqrt_d;\n    }\n    /* maximum", "l[j] = s;\n    }\n    /* maximum"),

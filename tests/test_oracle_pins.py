@@ -306,3 +306,16 @@ def test_tiny_golden_fixture_reproduces():
     np.testing.assert_allclose(raw, np.array(g["raw"]), rtol=1e-14)
     scores = orc.pool_protect(raw, cfg.w, cfg.pool)
     np.testing.assert_array_equal(orc.select(scores, cfg.budget), np.array(g["keep"], dtype=np.int32))
+
+
+def test_thread_count_does_not_change_a_bit():
+    """The oracle spreads a call over the window rows of every KV head and adds
+    each head's rows in a fixed order: the scores are bitwise the same on one
+    thread and on several."""
+    rng = np.random.default_rng(8)
+    q = wl.bf16_bits(rng.standard_normal((8, 3, 16), dtype=np.float32))
+    k = wl.bf16_bits(rng.standard_normal((2, 300, 16), dtype=np.float32))
+    v = wl.bf16_bits(rng.standard_normal((2, 300, 16), dtype=np.float32))
+    one = orc.score(q, k, v, 5, nthreads=1)
+    for t in (2, 3, 7):
+        assert np.array_equal(one.view(np.uint64), orc.score(q, k, v, 5, nthreads=t).view(np.uint64))
