@@ -36,14 +36,19 @@ def _gpu_attention(ctx, q, k, pool, budget=None):
     Hq, w, d = q.shape
     Hkv, n, _ = k.shape
     qd, kd = H.to_dev(q), H.to_dev(k)
-    scores = torch.full((Hkv, n), -7.0, dtype=torch.float32, device="cuda")
+    gs = H.Guarded((Hkv, n), torch.float32, -7.0)
+    scores = gs.t
     ctx.score_attention(qd, kd, n, w, Hq, Hkv, d, pool, scores)
-    keep = None
+    keep = gk = None
     if budget:
-        keep = torch.full((Hkv, budget), -5, dtype=torch.int32, device="cuda")
+        gk = H.Guarded((Hkv, budget), torch.int32, -5)
+        keep = gk.t
         ctx.select(scores, Hkv, n, budget, keep)
     st = ctx.sync()
     torch.cuda.synchronize()
+    gs.check("scores")
+    if gk is not None:
+        gk.check("keep")
     return st, scores.cpu().numpy(), (keep.cpu().numpy() if keep is not None else None)
 
 

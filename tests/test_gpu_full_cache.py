@@ -4,9 +4,13 @@ heads, d = 96, n = 131072, about 48 GiB of K/V) through the C ABI.
 Every head: the window is +inf, the rest finite and non-negative; keep lists
 are ascending, in range and hold the window; every kept score is >= every
 evicted one, ties evicted oldest first; the packed cache is the kept rows bit
-for bit.  Sampled heads: every score and the eviction set against the float64
-oracle on host copies of the same bytes (2e-3 bar, band at the threshold).
+for bit; and every score and eviction set of all 1024 heads against the float64
+oracle on host copies of the same bytes (2e-3 bar, band at the threshold), one
+layer (1.6 GB of K/V) at a time.
 """
+import concurrent.futures as cf
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -27,16 +31,17 @@ def test_phi3_full_cache():
     HQ, HK = L * Hq, L * Hkv
     print("[case] phi3full: drawing the cache on the device", flush=True)
     q, k, v = wd.make_cache(cfg)
-    scores = torch.empty((HK, n), dtype=torch.float32, device="cuda")
-    keep = torch.empty((HK, b), dtype=torch.int32, device="cuda")
-    ko = torch.empty((HK, b, d), dtype=torch.int16, device="cuda")
-    vo = torch.empty((HK, b, d), dtype=torch.int16, device="cuda")
+    outs = dict(scores=H.Guarded((HK, n), torch.float32), keep=H.Guarded((HK, b), torch.int32),
+                k_out=H.Guarded((HK, b, d), torch.int16), v_out=H.Guarded((HK, b, d), torch.int16))
+    scores, keep, ko, vo = (outs[x].t for x in ("scores", "keep", "k_out", "v_out"))
     with dropkv.Context(0) as ctx:
         print("[case] phi3full: score + select + compact", flush=True)
         ctx.score(q, k, v, n, w, HQ, HK, d, pool, scores)
         ctx.select(scores, HK, n, b, keep)
         ctx.compact(k, v, HK, n, d, keep, b, ko, vo)
         assert ctx.sync() == dropkv.OK
+    for name, g in outs.items():
+        g.check(name)
 
     # every head: protection, finiteness, keep structure
     assert bool(torch.isinf(scores[:, n - w:]).all())
@@ -60,15 +65,23 @@ def test_phi3_full_cache():
     rows = kl[:, :, None].expand(HK, b, d)
     assert bool((torch.gather(k, 1, rows) == ko).all()) and bool((torch.gather(v, 1, rows) == vo).all())
 
-    # sampled heads against the oracle
-    for layer, head in ((0, 0), (13, 7), (31, 31)):
-        hk = layer * Hkv + head           # G = 1: query head hk belongs to KV head hk
-        print(f"[case] phi3full: oracle on layer {layer} head {head}", flush=True)
-        qh = q[hk:hk + 1].cpu().numpy().view(np.uint16)
-        kh = k[hk:hk + 1].cpu().numpy().view(np.uint16)
-        vh = v[hk:hk + 1].cpu().numpy().view(np.uint16)
-        want = orc.score(qh, kh, vh, pool)
-        got = scores[hk:hk + 1].cpu().numpy()
-        H.assert_scores_close(got, want, where=f"layer {layer} head {head}")
-        H.assert_keep_sets_match(keep[hk:hk + 1].cpu().numpy(), orc.select(want, b), want, b,
-                                 where=f"layer {layer} head {head}")
+    # every head against the oracle, one layer at a time on host copies of the
+    # same bytes (the oracle runs the layer's heads on all host threads)
+    threads = min(orc.default_threads(), 16)   # one GPU's share of the host
+    scores_h = scores.cpu().numpy()
+    keep_h = keep.cpu().numpy()
+    for layer in range(L):
+        t0 = time.perf_counter()
+        lo, hi = layer * Hkv, (layer + 1) * Hkv      # G = 1: query heads = KV heads
+        qh = q[lo:hi].cpu().numpy().view(np.uint16)
+        kh = k[lo:hi].cpu().numpy().view(np.uint16)
+        vh = v[lo:hi].cpu().numpy().view(np.uint16)
+        want = orc.score(qh, kh, vh, pool, nthreads=threads)
+        del kh, vh
+        H.assert_scores_close(scores_h[lo:hi], want, where=f"layer {layer}")
+        with cf.ThreadPoolExecutor(threads) as ex:   # the oracle's selection, one head per call
+            keep_o = np.concatenate(list(ex.map(lambda g: orc.select(want[g:g + 1], b),
+                                                range(Hkv))))
+        H.assert_keep_sets_match(keep_h[lo:hi], keep_o, want, b, where=f"layer {layer}")
+        print(f"[case] phi3full: layer {layer} matches the oracle on all {Hkv} heads "
+              f"({time.perf_counter() - t0:.1f} s)", flush=True)

@@ -25,10 +25,13 @@ def ctx():
 def _layer_select(ctx, s, budget):
     Hkv, n = s.shape
     sd = torch.from_numpy(np.ascontiguousarray(s, dtype=np.float32)).cuda()
-    keep = torch.full((max(budget, 1),), -9, dtype=torch.int32, device="cuda")
-    counts = torch.full((Hkv,), -9, dtype=torch.int32, device="cuda")
+    gk = H.Guarded((max(budget, 1),), torch.int32, -9)
+    gc = H.Guarded((Hkv,), torch.int32, -9)
+    keep, counts = gk.t, gc.t
     ctx.select_layer(sd, Hkv, n, budget, keep, counts)
     st = ctx.sync()
+    gk.check("keep")
+    gc.check("counts")
     return st, keep.cpu().numpy()[:budget], counts.cpu().numpy()
 
 
@@ -74,15 +77,16 @@ def test_full_path_llama32k(ctx):
     Hkv, n, d = cfg.Hkv, cfg.n, cfg.d
     budget = Hkv * cfg.budget
     qd, kd, vd = H.to_dev(q), H.to_dev(k), H.to_dev(v)
-    scores = torch.empty((Hkv, n), dtype=torch.float32, device="cuda")
-    keep = torch.empty((budget,), dtype=torch.int32, device="cuda")
-    counts = torch.empty((Hkv,), dtype=torch.int32, device="cuda")
-    ko = torch.empty((budget, d), dtype=torch.int16, device="cuda")
-    vo = torch.empty((budget, d), dtype=torch.int16, device="cuda")
+    outs = dict(scores=H.Guarded((Hkv, n), torch.float32), keep=H.Guarded((budget,), torch.int32),
+                counts=H.Guarded((Hkv,), torch.int32), k_out=H.Guarded((budget, d), torch.int16),
+                v_out=H.Guarded((budget, d), torch.int16))
+    scores, keep, counts, ko, vo = (outs[x].t for x in ("scores", "keep", "counts", "k_out", "v_out"))
     ctx.score(qd, kd, vd, n, cfg.w, cfg.Hq, Hkv, d, cfg.pool, scores)
     ctx.select_layer(scores, Hkv, n, budget, keep, counts)
     ctx.compact(kd, vd, 1, Hkv * n, d, keep, budget, ko, vo)
     assert ctx.sync() == dropkv.OK
+    for name, g in outs.items():
+        g.check(name)
     want = orc.score(q, k, v, cfg.pool)
     kg, cg = keep.cpu().numpy(), counts.cpu().numpy()
     assert cg.sum() == budget and np.all(cg >= cfg.w)

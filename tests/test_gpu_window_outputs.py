@@ -37,13 +37,15 @@ def _run(ctx, q, k, v, pool):
     Hq, w, d = q.shape
     Hkv, n, _ = k.shape
     qd, kd, vd = H.to_dev(q), H.to_dev(k), H.to_dev(v)
-    s1 = torch.empty((Hkv, n), dtype=torch.float32, device="cuda")
-    s2 = torch.empty_like(s1)
-    oa = torch.full((Hq, w, d), 7.0, dtype=torch.float32, device="cuda")
-    ol = torch.full((Hq, w), 7.0, dtype=torch.float32, device="cuda")
+    outs = dict(s1=H.Guarded((Hkv, n), torch.float32), s2=H.Guarded((Hkv, n), torch.float32),
+                out_a=H.Guarded((Hq, w, d), torch.float32, 7.0),
+                out_lse=H.Guarded((Hq, w), torch.float32, 7.0))
+    s1, s2, oa, ol = (outs[x].t for x in ("s1", "s2", "out_a", "out_lse"))
     ctx.score(qd, kd, vd, n, w, Hq, Hkv, d, pool, s1)
     ctx.score_ex(qd, kd, vd, n, w, Hq, Hkv, d, pool, s2, oa, ol)
     st = ctx.sync()
+    for name, g in outs.items():
+        g.check(name)
     return st, s1.cpu().numpy(), s2.cpu().numpy(), oa.cpu().numpy(), ol.cpu().numpy()
 
 
