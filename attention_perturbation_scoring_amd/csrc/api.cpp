@@ -31,6 +31,7 @@ struct dropkv_ctx {
     size_t bytes = 0;
     int hkv = 0;                   // head count the zeroed prefix was laid out for
   } sel[2];
+  int64_t sel_wait = kSelectWait;  // team-barrier polls before a selection workgroup goes alone
   uint32_t* latch = nullptr;       // device word
   uint32_t* latch_host = nullptr;  // pinned read-back
   bool prof = false;
@@ -131,6 +132,22 @@ int dropkv_destroy(dropkv_ctx* c) {
   if (c->latch) (void)hipFree(c->latch);
   if (c->latch_host) (void)hipHostFree(c->latch_host);
   delete c;
+  return DROPKV_OK;
+}
+
+int dropkv_scratch_bytes(int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int32_t d,
+                         int64_t* score_bytes, int64_t* select_bytes) {
+  if (!score_bytes || !select_bytes) return DROPKV_EINVAL;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || n < 1 || n >= (int64_t(1) << 31) || w < 1 || w > n ||
+      d < 8 || d % 8 != 0 || d > 256)
+    return DROPKV_EINVAL;
+  const int M = (Hq / Hkv) * w;
+  if ((int64_t)M > (int64_t)kRows * kMaxRowGroups) return DROPKV_EINVAL;
+  const int DP = (d + 31) / 32 * 32, R = (M + kRows - 1) / kRows;
+  int64_t len = 0;
+  const int splits = plan_splits(n, Hkv * R, &len, kTargetWG1);
+  *score_bytes = (int64_t)score_scratch_bytes(Hkv * R, splits, DP);
+  *select_bytes = (int64_t)select_scratch_bytes(Hkv, n);
   return DROPKV_OK;
 }
 
@@ -264,7 +281,7 @@ int dropkv_select(dropkv_ctx* c, const float* scores, int32_t Hkv, int64_t n, in
   SelScratch sc{};
   const int rc = sel_prepare(c, c->sel[0], Hkv, n, s, &sc);
   if (rc != DROPKV_OK) return rc;
-  return to_status(launch_select(c, scores, Hkv, n, budget, keep, c->latch, sc, s));
+  return to_status(launch_select(c, scores, Hkv, n, budget, keep, c->latch, sc, c->sel_wait, s));
 }
 
 int dropkv_select_layer(dropkv_ctx* c, const float* scores, int32_t Hkv, int64_t n,
@@ -282,7 +299,7 @@ int dropkv_select_layer(dropkv_ctx* c, const float* scores, int32_t Hkv, int64_t
     SelScratch sc{};
     const int rc = sel_prepare(c, c->sel[1], 1, total, s, &sc);
     if (rc != DROPKV_OK) return rc;
-    const hipError_t e = launch_select(c, scores, 1, total, budget, keep, c->latch, sc, s);
+    const hipError_t e = launch_select(c, scores, 1, total, budget, keep, c->latch, sc, c->sel_wait, s);
     if (e != hipSuccess) return to_status(e);
   }
   return to_status(launch_layer_counts(c, keep, budget, n, Hkv, counts, c->latch, s));
@@ -326,11 +343,6 @@ int dropkv_sync(dropkv_ctx* c, void* stream) {
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return to_status(e);
   }
-  if (bits & LATCH_TIMEOUT) {
-    // a selection gave up inside its barriers: its scratch counters are stale
-    c->sel[0].hkv = c->sel[1].hkv = 0;
-    return DROPKV_EDEVICE;
-  }
   if (bits & LATCH_NONFINITE) return DROPKV_ENONFINITE;
   if (bits & LATCH_SINGULAR) return DROPKV_ESINGULAR;
   if (bits & LATCH_RANGE) return DROPKV_ERANGE;
@@ -348,6 +360,12 @@ const char* dropkv_strerror(int code) {
     case DROPKV_ENOMEM: return "out of device memory";
     default: return "unknown status";
   }
+}
+
+int dropkv_set_select_wait(dropkv_ctx* c, int64_t polls) {
+  if (!c) return DROPKV_EINVAL;
+  c->sel_wait = polls < 0 ? -1 : polls;
+  return DROPKV_OK;
 }
 
 int dropkv_profile_enable(dropkv_ctx* c, int on) {

@@ -72,8 +72,11 @@ enum : uint32_t {
   LATCH_NONFINITE = 1u,
   LATCH_SINGULAR = 2u,
   LATCH_RANGE = 4u,
-  LATCH_TIMEOUT = 8u,   // a workgroup barrier of the single-launch selection gave up waiting
 };
+
+// Polls a workgroup of the single-launch selection makes at a team barrier
+// before it finishes its share alone (about 10-20 ms on MI355X).
+constexpr int64_t kSelectWait = 16384;
 
 constexpr int kRows = 32;        // window-query rows of one row group (one MFMA tile)
 constexpr int kMaxRowGroups = 4; // G*w <= 128 rows per KV head
@@ -246,7 +249,8 @@ void prof_end(void* ctx, const char* name, hipStream_t s);
 
 hipError_t launch_score(void* ctx, const ScoreArgs& a, hipStream_t s);
 hipError_t launch_select(void* ctx, const float* scores, int Hkv, int64_t n, int64_t budget,
-                         int32_t* keep, uint32_t* latch, const SelScratch& sc, hipStream_t s);
+                         int32_t* keep, uint32_t* latch, const SelScratch& sc, int64_t wait,
+                         hipStream_t s);
 hipError_t launch_layer_counts(void* ctx, const int32_t* keep, int64_t budget, int64_t n, int Hkv,
                                int32_t* counts, uint32_t* latch, hipStream_t s);
 hipError_t launch_compact(void* ctx, const u16* k, const u16* v, int Hkv, int64_t n, int d,

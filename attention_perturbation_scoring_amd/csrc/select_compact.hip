@@ -80,6 +80,8 @@ struct SelArgs {
   int nblk;                 // blocks of kSelBlock tokens per head
   const uint32_t* latch;
   SelScratch sc;
+  int64_t wait;             // single-launch path: polls at a team barrier before a
+                            // workgroup finishes its share alone (< 0: at once)
 };
 
 __device__ __forceinline__ bool latched(const uint32_t* latch) {
@@ -372,13 +374,11 @@ __global__ __launch_bounds__(kSelThreads) void select_s4(SelArgs a) {
 // adds land on one bin); 16 keys per thread (8 workgroups per head at 128K
 // tokens) load the keys sooner than 32 and measured fastest on MI355X
 // (23 vs 28 us over 8 heads of 128K tokens; 8 or 12 keys: 25 us).
-// Cooperative launch (guaranteed co-residency) costs more per call than an
-// ordinary one; the ordinary launch relies on the team fitting an idle device
-// and on the barriers' bounded wait otherwise.
-#ifndef DROPKV_SEL_COOP
-#define DROPKV_SEL_COOP 0
-#endif
-
+// The launch is an ordinary one: a cooperative launch (guaranteed
+// co-residency) measured 16 us slower per call on MI355X.  A team member that
+// waits too long at a team barrier (its teammates not resident, e.g. on a
+// device shared with other work) does not fail: it finishes its share alone
+// from the scores in memory (select_alone), which gives the same keep entries.
 #ifndef DROPKV_SEL_THREADS
 #define DROPKV_SEL_THREADS 1024
 #endif
@@ -392,7 +392,6 @@ static_assert(kFusedBlock < 65536, "per-member counts are scanned packed in 16 b
 static_assert(kFusedThreads >= 256 && kFusedThreads <= 1024 && kFusedPer % 4 == 0, "team shape");
 constexpr int kFusedBins = kBins1 + 2 * 1024;            // per-head histograms of the three rounds
 constexpr int kFusedCand = 8192;                         // threshold-bin keys a team exchanges
-constexpr uint32_t kSpinLimit = 1u << 20;                // about a second of polling before giving up
 
 __device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -404,20 +403,21 @@ __device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
 // before it arrives.  With PLAIN, the workgroup also published ordinary stores:
 // every wave waits until its stores reach L2, then one release fence writes L2
 // back before the arrival, and one acquire fence follows the wait.
-// Returns false, for every thread of the workgroup, if the wait gave up.
+// Returns false, for every thread of the workgroup, if the wait gave up after
+// `wait` polls.
 template <bool PLAIN = false>
-__device__ bool team_barrier(uint32_t* bar, uint32_t target, int* s_ok) {
+__device__ bool team_barrier(uint32_t* bar, uint32_t target, int64_t wait, int* s_ok) {
   if (PLAIN) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
     if (PLAIN) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const uint32_t o = __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("s_waitcnt vmcnt(0)" ::"v"(o) : "memory");
-    uint32_t spins = 0u;
+    int64_t spins = 0;
     int ok = 1;
     while (load_agent(bar) < target) {
+      if (++spins > wait) { ok = 0; break; }
       __builtin_amdgcn_s_sleep(2);
-      if (++spins > kSpinLimit) { ok = 0; break; }
     }
     if (PLAIN) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     *s_ok = ok;
@@ -462,9 +462,9 @@ __device__ void find_bin_agent(const uint32_t* hist, uint32_t krem, uint32_t* s_
 // In the first round every key matches (mask = 0).
 template <int NB, bool FIRST>
 __device__ bool radix_round(const uint32_t (&key)[kFusedPer], int shift, uint32_t* h,
-                            uint32_t* gh, uint32_t* bar, uint32_t target, uint32_t& prefix,
-                            uint32_t& mask, uint32_t& krem, uint32_t* sh, uint32_t* s_bin,
-                            uint32_t* s_below, uint32_t* s_count, int* s_ok) {
+                            uint32_t* gh, uint32_t* bar, uint32_t target, int64_t wait,
+                            uint32_t& prefix, uint32_t& mask, uint32_t& krem, uint32_t* sh,
+                            uint32_t* s_bin, uint32_t* s_below, uint32_t* s_count, int* s_ok) {
   constexpr int NW = kFusedThreads / 64;
   constexpr int PER = NB / kFusedThreads;
   const int tid = threadIdx.x;
@@ -501,7 +501,7 @@ __device__ bool radix_round(const uint32_t (&key)[kFusedPer], int shift, uint32_
 #pragma unroll
   for (int i = 0; i < PER; ++i) sink |= old[i];
   asm volatile("s_waitcnt vmcnt(0)" ::"v"(sink) : "memory");
-  if (!team_barrier(bar, target, s_ok)) return false;
+  if (!team_barrier(bar, target, wait, s_ok)) return false;
   find_bin_agent<NW, NB>(gh, krem, s_bin, s_below, s_count, sh);
   prefix |= *s_bin << shift;
   mask |= (uint32_t)(NB - 1) << shift;
@@ -512,6 +512,51 @@ __device__ bool radix_round(const uint32_t (&key)[kFusedPer], int shift, uint32_
 
 __device__ __forceinline__ uint64_t load_agent64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A team member that stopped waiting for its team: the head's threshold key T
+// and the number `need` of keys equal to T that are evicted, from every score
+// of the head (three radix rounds over the keys in memory, histograms in LDS),
+// and the counts of keys above T and equal to T in the tokens before this
+// member.  Exactly what the team computes together, so the member's keep
+// entries are the same either way.  Whole workgroup.
+__device__ void select_alone(const SelArgs& a, int g, int b, uint32_t* h, uint32_t* sh,
+                             uint32_t* s_bin, uint32_t* s_below, uint32_t& T, uint32_t& need,
+                             uint32_t& gt_before, uint32_t& ties_before) {
+  constexpr int NW = kFusedThreads / 64;
+  const int tid = threadIdx.x;
+  const float* sg = a.scores + (size_t)g * a.n;
+  uint32_t prefix = 0u, mask = 0u, krem = (uint32_t)(a.n - a.budget);
+  for (int r = 0; r < 3; ++r) {
+    const int shift = r == 0 ? 20 : (r == 1 ? 10 : 0);
+    const int nb = r == 0 ? kBins1 : 1024;
+    for (int i = tid; i < nb; i += kFusedThreads) h[i] = 0u;
+    __syncthreads();
+    for (int64_t j = tid; j < a.n; j += kFusedThreads) {
+      const uint32_t k = order_key(sg[j]);
+      if ((k & mask) == prefix) atomicAdd(&h[(k >> shift) & (uint32_t)(nb - 1)], 1u);
+    }
+    __syncthreads();
+    find_bin<NW>(h, nb, krem, s_bin, s_below, sh);
+    prefix |= *s_bin << shift;
+    mask |= (uint32_t)(nb - 1) << shift;
+    krem -= *s_below;
+    __syncthreads();
+  }
+  T = prefix;
+  need = krem;
+  const int64_t before = min(a.n, (int64_t)b * kFusedBlock);
+  uint32_t gt = 0u, nt = 0u;
+  for (int64_t j = tid; j < before; j += kFusedThreads) {
+    const uint32_t k = order_key(sg[j]);
+    gt += k > T ? 1u : 0u;
+    nt += k == T ? 1u : 0u;
+  }
+  uint32_t tg, tt;   // (a member's 16384 tokens fit 16 bits, a head's prefix may not)
+  (void)block_exscan<NW>(gt, &tg, sh);
+  (void)block_exscan<NW>(nt, &tt, sh);
+  gt_before = tg;
+  ties_before = tt;
 }
 
 // Slots past the end of the head hold key 0, below every key a float maps to
@@ -559,154 +604,147 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
   const uint32_t pad = nblk * (uint32_t)kFusedBlock - (uint32_t)a.n;
   if (stop) return;   // nothing has been written yet
 
+  // T is the k-th smallest key; `need` (>= 1) of the keys equal to T are
+  // evicted; the members before b hold gt_before keys above T and ties_before
+  // keys equal to T
+  uint32_t T = 0u, need = 0u, gt_before = 0u, ties_before = 0u;
+  bool alone = a.wait < 0;
   // round 1: the 12-bit bin b1 holding the k-th smallest key, and its size
   uint32_t prefix = 0u, mask = 0u, krem = (uint32_t)(a.n - a.budget) + pad;
-  if (!radix_round<kBins1, true>(key, 20, h, fh, bar, nblk, prefix, mask, krem, sh, &s_bin,
-                                 &s_below, &s_count, &s_ok)) {
-    if (tid == 0) atomicOr((uint32_t*)a.latch, LATCH_TIMEOUT);
-    return;
+  if (!alone)
+    alone = !radix_round<kBins1, true>(key, 20, h, fh, bar, nblk, a.wait, prefix, mask, krem, sh,
+                                       &s_bin, &s_below, &s_count, &s_ok);
+  if (!alone) {
+    const uint32_t c1 = s_count;   // the same in every member: read from one histogram
+    const uint32_t b1 = prefix >> 20;
+    if (c1 <= (uint32_t)kFusedCand) {
+      // Exchange the bin's keys (tagged with the member) and each member's count
+      // of keys above the bin; then every member finishes alone.
+      uint32_t mine = 0u, gt1 = 0u;
+#pragma unroll
+      for (int i = 0; i < kFusedPer; ++i) {
+        const uint32_t bin = key[i] >> 20;
+        mine += bin == b1 ? 1u : 0u;
+        gt1 += bin > b1 ? 1u : 0u;
+      }
+      uint32_t tot;   // both counts are below 2^16 per member: scan them packed
+      const uint32_t off = block_exscan<NW>(mine | (gt1 << 16), &tot, sh) & 0xffffu;
+      if (tid == 0) {
+        const uint32_t o = __hip_atomic_exchange(blk_gt + b, tot >> 16, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t mt = tot & 0xffffu;
+        s_base = mt ? __hip_atomic_fetch_add(a.sc.cand_cnt + g, mt, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT)
+                    : 0u;
+        asm volatile("s_waitcnt vmcnt(0)" ::"v"(o) : "memory");
+      }
+      __syncthreads();
+      uint64_t* cand = a.sc.fcand + (size_t)g * kFusedCand;
+      uint32_t pos = s_base + off;
+      // ordinary stores (one device-scope atomic per key would serialise at the
+      // memory side), published by the fences of the barrier
+#pragma unroll
+      for (int i = 0; i < kFusedPer; ++i)
+        if ((key[i] >> 20) == b1) {
+          if (pos < (uint32_t)kFusedCand) cand[pos] = (uint64_t)key[i] | ((uint64_t)b << 32);
+          ++pos;
+        }
+      alone = !team_barrier<true>(bar, 2 * nblk, a.wait, &s_ok);
+      if (!alone) {
+        // every candidate and count load in flight at once (c1 <= kFusedCand)
+        constexpr int CU = kFusedCand / kFusedThreads;
+        uint64_t cv[CU];
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
+          const uint32_t i = (uint32_t)tid + (uint32_t)(u * kFusedThreads);
+          cv[u] = i < c1 ? load_agent64(cand + i) : 0u;
+        }
+        const uint32_t gv = (uint32_t)tid < nblk ? load_agent(blk_gt + tid) : 0u;
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
+          const uint32_t i = (uint32_t)tid + (uint32_t)(u * kFusedThreads);
+          if (i < c1) {
+            ck[i] = (uint32_t)cv[u];
+            cw[i] = (uint16_t)(cv[u] >> 32);
+          }
+        }
+        if ((uint32_t)tid < nblk) {
+          gtc[tid] = gv;
+          tiec[tid] = 0u;
+        }
+        __syncthreads();
+        // the exact k-th smallest key: two 10-bit digits below the bin, in LDS
+        for (int shift = 10; shift >= 0; shift -= 10) {
+          for (int i = tid; i < 1024; i += kFusedThreads) h[i] = 0u;
+          __syncthreads();
+          for (uint32_t i = tid; i < c1; i += kFusedThreads) {
+            const uint32_t k = ck[i];
+            if ((k & mask) == prefix) atomicAdd(&h[(k >> shift) & 1023u], 1u);
+          }
+          __syncthreads();
+          find_bin<NW>(h, 1024, krem, &s_bin, &s_below, sh);
+          prefix |= s_bin << shift;
+          mask |= 1023u << shift;
+          krem -= s_below;
+          __syncthreads();
+        }
+        T = prefix;
+        need = krem;
+        for (uint32_t i = tid; i < c1; i += kFusedThreads) {
+          const uint32_t k = ck[i];
+          if (k > T) atomicAdd(&gtc[cw[i]], 1u);
+          else if (k == T) atomicAdd(&tiec[cw[i]], 1u);
+        }
+        __syncthreads();
+      }
+    } else {
+      // Too many keys share the bin: two more histogram rounds over the team,
+      // then an exchange of each member's counts above and equal to T.
+      bool ok = radix_round<1024, false>(key, 10, h, fh + kBins1, bar, 2 * nblk, a.wait, prefix,
+                                         mask, krem, sh, &s_bin, &s_below, &s_count, &s_ok);
+      ok = ok && radix_round<1024, false>(key, 0, h, fh + kBins1 + 1024, bar, 3 * nblk, a.wait,
+                                          prefix, mask, krem, sh, &s_bin, &s_below, &s_count,
+                                          &s_ok);
+      if (ok) {
+        T = prefix;
+        need = krem;
+        uint32_t gt = 0u, nt = 0u;
+#pragma unroll
+        for (int i = 0; i < kFusedPer; ++i) {
+          gt += key[i] > T ? 1u : 0u;
+          nt += key[i] == T ? 1u : 0u;
+        }
+        uint32_t tot;
+        (void)block_exscan<NW>(gt | (nt << 16), &tot, sh);
+        if (tid == 0) {
+          const uint32_t o1 = __hip_atomic_exchange(blk_gt + b, tot & 0xffffu, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+          const uint32_t o2 = __hip_atomic_exchange(blk_tie + b, tot >> 16, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+          asm volatile("s_waitcnt vmcnt(0)" ::"v"(o1), "v"(o2) : "memory");
+        }
+        ok = team_barrier(bar, 4 * nblk, a.wait, &s_ok);
+        if (ok) {
+          for (uint32_t i = tid; i < nblk; i += kFusedThreads) {
+            gtc[i] = load_agent(blk_gt + i);
+            tiec[i] = load_agent(blk_tie + i);
+          }
+          __syncthreads();
+        }
+      }
+      alone = !ok;
+    }
+    if (!alone)
+      for (int bb = 0; bb < b; ++bb) {
+        gt_before += gtc[bb];
+        ties_before += tiec[bb];
+      }
   }
-  const uint32_t c1 = s_count;   // the same in every member: read from one histogram
-  const uint32_t b1 = prefix >> 20;
-  uint32_t T, need;
-  if (c1 <= (uint32_t)kFusedCand) {
-    // Exchange the bin's keys (tagged with the member) and each member's count
-    // of keys above the bin; then every member finishes alone.
-    uint32_t mine = 0u, gt1 = 0u;
-#pragma unroll
-    for (int i = 0; i < kFusedPer; ++i) {
-      const uint32_t bin = key[i] >> 20;
-      mine += bin == b1 ? 1u : 0u;
-      gt1 += bin > b1 ? 1u : 0u;
-    }
-    uint32_t tot;   // both counts are below 2^16 per member: scan them packed
-    const uint32_t off = block_exscan<NW>(mine | (gt1 << 16), &tot, sh) & 0xffffu;
-    if (tid == 0) {
-      const uint32_t o = __hip_atomic_exchange(blk_gt + b, tot >> 16, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t mt = tot & 0xffffu;
-      s_base = mt ? __hip_atomic_fetch_add(a.sc.cand_cnt + g, mt, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT)
-                  : 0u;
-      asm volatile("s_waitcnt vmcnt(0)" ::"v"(o) : "memory");
-    }
-    __syncthreads();
-    uint64_t* cand = a.sc.fcand + (size_t)g * kFusedCand;
-    uint32_t pos = s_base + off;
-    // ordinary stores (one device-scope atomic per key would serialise at the
-    // memory side), published by the fences of the barrier
-#pragma unroll
-    for (int i = 0; i < kFusedPer; ++i)
-      if ((key[i] >> 20) == b1) {
-        if (pos < (uint32_t)kFusedCand) cand[pos] = (uint64_t)key[i] | ((uint64_t)b << 32);
-        ++pos;
-      }
-    if (!team_barrier<true>(bar, 2 * nblk, &s_ok)) {
-      if (tid == 0) atomicOr((uint32_t*)a.latch, LATCH_TIMEOUT);
-      return;
-    }
-    // every candidate and count load in flight at once (c1 <= kFusedCand)
-    constexpr int CU = kFusedCand / kFusedThreads;
-    uint64_t cv[CU];
-#pragma unroll
-    for (int u = 0; u < CU; ++u) {
-      const uint32_t i = (uint32_t)tid + (uint32_t)(u * kFusedThreads);
-      cv[u] = i < c1 ? load_agent64(cand + i) : 0u;
-    }
-    const uint32_t gv = (uint32_t)tid < nblk ? load_agent(blk_gt + tid) : 0u;
-#pragma unroll
-    for (int u = 0; u < CU; ++u) {
-      const uint32_t i = (uint32_t)tid + (uint32_t)(u * kFusedThreads);
-      if (i < c1) {
-        ck[i] = (uint32_t)cv[u];
-        cw[i] = (uint16_t)(cv[u] >> 32);
-      }
-    }
-    if ((uint32_t)tid < nblk) {
-      gtc[tid] = gv;
-      tiec[tid] = 0u;
-    }
-    __syncthreads();
-    // the exact k-th smallest key: two 10-bit digits below the bin, in LDS
-    for (int shift = 10; shift >= 0; shift -= 10) {
-      for (int i = tid; i < 1024; i += kFusedThreads) h[i] = 0u;
-      __syncthreads();
-      for (uint32_t i = tid; i < c1; i += kFusedThreads) {
-        const uint32_t k = ck[i];
-        if ((k & mask) == prefix) atomicAdd(&h[(k >> shift) & 1023u], 1u);
-      }
-      __syncthreads();
-      find_bin<NW>(h, 1024, krem, &s_bin, &s_below, sh);
-      prefix |= s_bin << shift;
-      mask |= 1023u << shift;
-      krem -= s_below;
-      __syncthreads();
-    }
-    T = prefix;
-    need = krem;
-    for (uint32_t i = tid; i < c1; i += kFusedThreads) {
-      const uint32_t k = ck[i];
-      if (k > T) atomicAdd(&gtc[cw[i]], 1u);
-      else if (k == T) atomicAdd(&tiec[cw[i]], 1u);
-    }
-    __syncthreads();
-  } else {
-    // Too many keys share the bin: two more histogram rounds over the team,
-    // then an exchange of each member's counts above and equal to T.
-    bool ok = radix_round<1024, false>(key, 10, h, fh + kBins1, bar, 2 * nblk, prefix, mask, krem,
-                                       sh, &s_bin, &s_below, &s_count, &s_ok);
-    ok = ok && radix_round<1024, false>(key, 0, h, fh + kBins1 + 1024, bar, 3 * nblk, prefix,
-                                        mask, krem, sh, &s_bin, &s_below, &s_count, &s_ok);
-    if (!ok) {
-      if (tid == 0) atomicOr((uint32_t*)a.latch, LATCH_TIMEOUT);
-      return;
-    }
-    T = prefix;
-    need = krem;
-    uint32_t gt = 0u, nt = 0u;
-#pragma unroll
-    for (int i = 0; i < kFusedPer; ++i) {
-      gt += key[i] > T ? 1u : 0u;
-      nt += key[i] == T ? 1u : 0u;
-    }
-    uint32_t tot;
-    (void)block_exscan<NW>(gt | (nt << 16), &tot, sh);
-    if (tid == 0) {
-      const uint32_t o1 = __hip_atomic_exchange(blk_gt + b, tot & 0xffffu, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t o2 = __hip_atomic_exchange(blk_tie + b, tot >> 16, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-      asm volatile("s_waitcnt vmcnt(0)" ::"v"(o1), "v"(o2) : "memory");
-    }
-    if (!team_barrier(bar, 4 * nblk, &s_ok)) {
-      if (tid == 0) atomicOr((uint32_t*)a.latch, LATCH_TIMEOUT);
-      return;
-    }
-    for (uint32_t i = tid; i < nblk; i += kFusedThreads) {
-      gtc[i] = load_agent(blk_gt + i);
-      tiec[i] = load_agent(blk_tie + i);
-    }
-    __syncthreads();
-  }
-  // T is the k-th smallest key; `need` (>= 1) of the keys equal to T are evicted.
+  if (alone)   // the teammates did not all arrive in time: the same answer alone
+    select_alone(a, g, b, h, sh, &s_bin, &s_below, T, need, gt_before, ties_before);
+
   // Evicted ties are the oldest, so the members before b evict min(need, their
   // ties) of them and b evicts what remains of `need`, up to its own ties.
-  uint32_t gt_before = 0u, ties_before = 0u;
-  for (int bb = 0; bb < b; ++bb) {
-    gt_before += gtc[bb];
-    ties_before += tiec[bb];
-  }
-  const uint32_t ev_before = min(need, ties_before);
-  const uint32_t ev = min(tiec[b], need - ev_before);
-  const uint32_t keep_before = gt_before + ties_before - ev_before;
-
-  // The whole team is past its last barrier, so nobody reads the histograms or
-  // the candidate count again: clear this member's share of the histograms.
-  for (int i = b * kFusedThreads + tid; i < kFusedBins; i += (int)nblk * kFusedThreads) fh[i] = 0u;
-
-  // ordered emission (thread order is index order within the member): the
-  // threads before this one hold gt_pre keys above T and tie_pre ties, of which
-  // the first `ev` of the member are evicted
   uint32_t gt = 0u, nt = 0u;
 #pragma unroll
   for (int i = 0; i < kFusedPer; ++i) {
@@ -715,6 +753,13 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
   }
   uint32_t tot;
   const uint32_t pre = block_exscan<NW>(gt | (nt << 16), &tot, sh);
+  const uint32_t ev_before = min(need, ties_before);
+  const uint32_t ev = min(tot >> 16, need - ev_before);
+  const uint32_t keep_before = gt_before + ties_before - ev_before;
+
+  // ordered emission (thread order is index order within the member): the
+  // threads before this one hold gt_pre keys above T and tie_pre ties, of which
+  // the first `ev` of the member are evicted
   const uint32_t gt_pre = pre & 0xffffu, tie_pre = pre >> 16;
   uint32_t rank = tie_pre, keepbits = 0u;
 #pragma unroll
@@ -726,7 +771,8 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
   }
   uint32_t pos = keep_before + gt_pre + (tie_pre > ev ? tie_pre - ev : 0u);
   // count this member out (its reply arrives while the keep list is written);
-  // the last member of the team resets the counters
+  // the last member of the team -- every other member is past its last read of
+  // the team's scratch -- leaves the histograms and counters zeroed
   uint32_t done_before = 0u;
   if (tid == 0) done_before = atomicAdd(a.sc.done + g, 1u);
   int32_t* kg = a.keep + (size_t)g * a.budget;
@@ -736,10 +782,15 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
     if (pos < (uint32_t)a.budget) kg[pos] = (int32_t)(base + i);
     ++pos;
   }
-  if (tid == 0 && done_before == nblk - 1u) {
-    __hip_atomic_store(bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(a.sc.cand_cnt + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(a.sc.done + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) s_ok = done_before == nblk - 1u;
+  __syncthreads();
+  if (s_ok) {
+    for (int i = tid; i < kFusedBins; i += kFusedThreads) fh[i] = 0u;
+    if (tid == 0) {
+      __hip_atomic_store(bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.sc.cand_cnt + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.sc.done + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -968,7 +1019,8 @@ static int64_t fused_capacity() {
 }
 
 hipError_t launch_select(void* ctx, const float* scores, int Hkv, int64_t n, int64_t budget,
-                         int32_t* keep, uint32_t* latch, const SelScratch& sc, hipStream_t s) {
+                         int32_t* keep, uint32_t* latch, const SelScratch& sc, int64_t wait,
+                         hipStream_t s) {
   if (budget == n) {
     const int64_t total = (int64_t)Hkv * n;
     int64_t blocks = (total + 255) / 256;
@@ -984,6 +1036,7 @@ hipError_t launch_select(void* ctx, const float* scores, int Hkv, int64_t n, int
   a.nblk = (int)((n + kSelBlock - 1) / kSelBlock);
   a.latch = latch;
   a.sc = sc;
+  a.wait = wait;
   prof_begin(ctx, "select", s);
   const int64_t team = (n + kFusedBlock - 1) / kFusedBlock;
   if (team == 1) {   // one workgroup per head: no team, no co-residency needed
@@ -997,10 +1050,7 @@ hipError_t launch_select(void* ctx, const float* scores, int Hkv, int64_t n, int
     void* args[] = {&f};
     const dim3 fgrid((unsigned)((int64_t)Hkv * team)), fblock(kFusedThreads);
     const hipError_t e =
-        DROPKV_SEL_COOP
-            ? hipLaunchCooperativeKernel(reinterpret_cast<const void*>(select_fused), fgrid, fblock,
-                                         args, 0, s)
-            : hipLaunchKernel(reinterpret_cast<const void*>(select_fused), fgrid, fblock, args, 0, s);
+        hipLaunchKernel(reinterpret_cast<const void*>(select_fused), fgrid, fblock, args, 0, s);
     if (e == hipSuccess) {
       prof_end(ctx, "select", s);
       return hipSuccess;

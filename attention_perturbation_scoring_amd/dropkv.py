@@ -49,11 +49,14 @@ def lib():
             "dropkv_select_layer": [P, P, i32, i64, i64, P, P, P],
             "dropkv_compact": [P, P, P, i32, i64, i32, P, i64, P, P, P],
             "dropkv_sync": [P, P],
+            "dropkv_set_select_wait": [P, i64],
             "dropkv_profile_enable": [P, ctypes.c_int],
             "dropkv_profile_reset": [P],
             "dropkv_profile_read": [P, ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_int64)],
             "dropkv_plan_splits": [i64, i32, ctypes.POINTER(i32)],
+            "dropkv_scratch_bytes": [i64, i32, i32, i32, i32, ctypes.POINTER(i64),
+                                     ctypes.POINTER(i64)],
             "dropkv_stream_read": [P, P, i64, P],
         }
         for name, args in sig.items():
@@ -102,6 +105,14 @@ def plan_splits(n: int, Hkv: int) -> int:
     s = ctypes.c_int32(0)
     _check(lib().dropkv_plan_splits(n, Hkv, ctypes.byref(s)), "dropkv_plan_splits")
     return s.value
+
+
+def scratch_bytes(n: int, w: int, Hq: int, Hkv: int, d: int):
+    """(score scratch, select scratch) in bytes that a context holds for these sizes."""
+    a, b = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(lib().dropkv_scratch_bytes(n, w, Hq, Hkv, d, ctypes.byref(a), ctypes.byref(b)),
+           "dropkv_scratch_bytes")
+    return a.value, b.value
 
 
 class Context:
@@ -165,6 +176,10 @@ class Context:
         nbytes = buf.numel() * buf.element_size() if nbytes is None else nbytes
         _check(lib().dropkv_stream_read(self._h, _ptr(buf), nbytes, _stream(stream)),
                "dropkv_stream_read")
+
+    def set_select_wait(self, polls: int):
+        """Team-barrier polls before a selection workgroup finishes its share alone."""
+        _check(lib().dropkv_set_select_wait(self._h, polls), "dropkv_set_select_wait")
 
     def sync(self, stream=None) -> int:
         """Wait for the stream; return (and clear) the latched device status."""

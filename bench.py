@@ -152,6 +152,18 @@ def time_peaked_rows(ctx, cfg, inp, dev, v_dev, scores, stream):
             "planted_token": jp, "kernel_us": us}
 
 
+def scratch_report(n, w, Hq, Hkv, d):
+    """Device scratch the library holds for one call of these sizes, beside the
+    pages' figures for the same question (n = 128K: ~17 MB for the fused Triton
+    scorer against ~9 GB for the naive PyTorch one)."""
+    from attention_perturbation_scoring_amd import dropkv
+    sb, selb = dropkv.scratch_bytes(n, w, Hq, Hkv, d)
+    return {"score": sb, "select": selb, "total": sb + selb,
+            "what": "context scratch of dropkv_score (split partial states, per-row state) "
+                    "and dropkv_select (histograms, candidates, per-block counts); no "
+                    "attention weights or distances are materialised"}
+
+
 def host_cpu() -> str:
     """The host's CPU model and logical CPU count, for the baseline's description."""
     model = "unknown CPU"
@@ -166,31 +178,38 @@ def host_cpu() -> str:
     return f"{model}, nproc {os.cpu_count()}"
 
 
+def host_threads() -> int:
+    """Threads for the oracle: the CPUs this process may run on, at most 16 (one
+    GPU's share of the host)."""
+    from oracle import oracle as orc
+    return min(orc.default_threads(), 16)
+
+
 def cpu_baseline(cfg, inp, dev_inputs):
-    """Time the float64 oracle (score + select) on the host: the full layer of a
-    single-layer workload; for a multi-layer cache, the first KV heads of
-    layer 0 (one per thread), projected to the whole cache.  One thread per KV
-    head, the oracle's parallel unit."""
+    """Time the float64 oracle (score + select) on the host, on every host
+    thread (the oracle spreads a call over all window rows of all KV heads):
+    the full layer of a single-layer workload; for a multi-layer cache, the
+    first KV heads of layer 0, projected to the whole cache."""
     import numpy as np
     from oracle import oracle as orc
+    threads = host_threads()
     if cfg.layers > 1:
         q, k, v = dev_inputs
         G = cfg.Hq // cfg.Hkv
-        heads = min(cfg.Hkv, orc.default_threads())
+        heads = min(cfg.Hkv, threads)
         qs = q[: heads * G].cpu().numpy().view(np.uint16)
         ks = k[:heads].cpu().numpy().view(np.uint16)
         vs = v[:heads].cpu().numpy().view(np.uint16)
         t0 = time.perf_counter()
-        s = orc.score(qs, ks, vs, cfg.pool, nthreads=heads)
+        s = orc.score(qs, ks, vs, cfg.pool, nthreads=threads)
         orc.select(s, cfg.budget)
         dt = time.perf_counter() - t0
         whole = dt * (cfg.layers * cfg.Hkv) / heads
-        return {"value": cfg.layers * cfg.n / whole, "unit": "tokens/s", "cores": heads,
+        return {"value": cfg.layers * cfg.n / whole, "unit": "tokens/s", "cores": threads,
                 "kind": "oracle",
                 "sample": f"{heads} KV heads of layer 0 of {cfg.name} (n={cfg.n}), float64 score + "
-                          f"select in {dt:.2f} s on {heads} threads ({host_cpu()}), projected "
+                          f"select in {dt:.2f} s on {threads} threads ({host_cpu()}), projected "
                           f"to all {cfg.layers * cfg.Hkv} heads"}
-    threads = min(cfg.Hkv, orc.default_threads())
     t0 = time.perf_counter()
     s = orc.score(inp["q"], inp["k"], inp["v"], cfg.pool, nthreads=threads)
     orc.select(s, cfg.budget)
@@ -205,8 +224,8 @@ def cpu_baseline(cfg, inp, dev_inputs):
             "value_one_thread": cfg.n / dt1,
             "sample": f"full {cfg.name} layer (all {cfg.Hkv} KV heads, n={cfg.n}); "
                       f"float64 score + select, {dt:.2f} s wall on {threads} threads "
-                      f"(one per KV head; {host_cpu()}); one thread: KV head 0 alone, "
-                      f"{dt1 / cfg.Hkv:.2f} s, scaled to the layer"}
+                      f"(spread over the layer's {cfg.Hq * cfg.w} window rows; {host_cpu()}); "
+                      f"one thread: KV head 0 alone, {dt1 / cfg.Hkv:.2f} s, scaled to the layer"}
 
 
 def run(args):
@@ -443,6 +462,7 @@ def run(args):
         "layer_select_us": layer_select_us,
         "peaked_rows": peaked_rows,
         "kernel_source_hash": kernel_source_hash(),
+        "scratch_bytes": scratch_report(n, w, Hq, Hkv, d),
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the float64 oracle on the host")

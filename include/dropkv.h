@@ -138,9 +138,14 @@ int dropkv_score_attention(dropkv_ctx *ctx, const uint16_t *q_win, const uint16_
  *   budget < 0 or budget > n.  (dropkv_score's protected window survives any
  *   budget >= w.)
  * If the context has a latched device error, nothing is written.
- * When Hkv * ceil(n / 16384) workgroups of 1024 threads fit on the device at
- * once, this is one launch whose workgroups wait for each other (bounded: see
- * dropkv_sync); otherwise four launches.  Both give the same result.
+ * A head of at most 16384 tokens is one workgroup.  Larger heads: when
+ * Hkv * ceil(n / 16384) workgroups of 1024 threads fit on the device at once,
+ * one launch whose workgroups (a team per head) exchange histograms and
+ * candidates; a workgroup whose teammates have not all arrived at an exchange
+ * after dropkv_set_select_wait polls (e.g. on a device shared with other work)
+ * finishes its share alone from the scores in memory, which is slower but
+ * gives the same keep entries -- the call never fails for lack of
+ * co-residency.  Otherwise four launches.  All paths give the same result.
  */
 int dropkv_select(dropkv_ctx *ctx, const float *scores, int32_t Hkv, int64_t n, int64_t budget,
                   int32_t *keep, void *stream);
@@ -177,11 +182,17 @@ int dropkv_compact(dropkv_ctx *ctx, const uint16_t *k, const uint16_t *v, int32_
                    uint16_t *v_out, void *stream);
 
 /* Wait for `stream`, then return and clear the latched device condition
- * (EDEVICE before ENONFINITE before ESINGULAR before ERANGE), or DROPKV_OK.
- * EDEVICE here means a selection's workgroups stopped waiting for each other
- * (about a second without progress, e.g. a device shared with other work); its
- * keep list is unspecified and the next dropkv_select resets its scratch. */
+ * (ENONFINITE before ESINGULAR before ERANGE), or DROPKV_OK; EDEVICE if the
+ * HIP runtime reports an error. */
 int dropkv_sync(dropkv_ctx *ctx, void *stream);
+
+/* Polls a workgroup of the single-launch selection makes at a team exchange
+ * before it finishes its share alone (see dropkv_select).  Default 16384
+ * (about 10-20 ms); 0 stops waiting at the first poll that finds a teammate
+ * missing; a negative value makes every workgroup go alone at once (no
+ * exchange at all).  The result is the same for every value.  EINVAL if ctx is
+ * NULL. */
+int dropkv_set_select_wait(dropkv_ctx *ctx, int64_t polls);
 
 /* Static string naming a status code. */
 const char *dropkv_strerror(int code);
@@ -207,6 +218,15 @@ int dropkv_profile_read(dropkv_ctx *ctx, const char *name, double *total_ms, int
  * multiple of 16, else EINVAL.  Asynchronous on `stream`.
  */
 int dropkv_stream_read(dropkv_ctx *ctx, const void *p, int64_t bytes, void *stream);
+
+/* Device scratch (bytes) the context holds for these sizes: *score_bytes for
+ * dropkv_score (split partial states and per-query state; independent of n
+ * beyond the split count, which the device's size fixes), *select_bytes for
+ * dropkv_select over [Hkv][n] scores.  Nothing of size O(n * d) -- no attention
+ * weights or distances -- is ever allocated.  EINVAL as for dropkv_score's
+ * shape checks, or a NULL output pointer. */
+int dropkv_scratch_bytes(int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int32_t d,
+                         int64_t *score_bytes, int64_t *select_bytes);
 
 /* Launch geometry dropkv_score would use for these sizes (for tests/diagnostics):
  * number of sequence splits of the first pass. */

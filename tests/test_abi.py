@@ -49,6 +49,13 @@ def test_host_only_entry_points():
     assert L.dropkv_score(None, None, None, None, 10, 1, 1, 1, 8, 1, None, None) == dropkv.EINVAL
     assert L.dropkv_sync(None, None) == dropkv.EINVAL
     assert L.dropkv_stream_read(None, None, 16, None) == dropkv.EINVAL
+    # scratch at the headline shape: 64 splits x 32 rows x (d + 5) floats per KV
+    # head plus per-row state -- megabytes, nothing of size n * d
+    sb, selb = dropkv.scratch_bytes(131072, 8, 32, 8, 128)
+    assert 8 * 64 * 32 * (128 + 5) * 4 <= sb < 12 * 2**20
+    assert 0 < selb < 4 * 2**20
+    with pytest.raises(dropkv.DropKVError):
+        dropkv.scratch_bytes(100, 8, 3, 2, 128)     # Hq % Hkv != 0
 
 
 def test_binding_has_no_fallback(monkeypatch, tmp_path):

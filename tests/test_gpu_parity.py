@@ -177,6 +177,49 @@ def test_select_multi_launch_path(ctx):
                                       err_msg=f"budget={budget}")
 
 
+@pytest.mark.parametrize("wait", [-1, 0])
+def test_select_when_teammates_do_not_arrive(ctx, wait):
+    """A selection workgroup that stops waiting for its team finishes its share
+    alone from the scores in memory: with every workgroup going alone (-1), or
+    each going alone as soon as one poll finds a teammate missing (0; a mix
+    of both paths), the keep lists equal the oracle's.  Heads of one to
+    nine workgroups, heavy ties, a threshold bin larger than the candidate
+    exchange, and the layer-wide selection."""
+    rng = np.random.default_rng(40 + wait)
+    try:
+        ctx.set_select_wait(wait)
+        for n, Hkv in ((20000, 3), (70000, 2), (131072, 8)):
+            s = rng.integers(0, 50, size=(Hkv, n)).astype(np.float32)
+            s[:, : n // 3] = rng.random((Hkv, n // 3)).astype(np.float32)
+            s[:, -8:] = np.inf
+            s[-1, : n // 2] = 2.5                                       # one huge threshold bin
+            sd = torch.from_numpy(s).cuda()
+            for budget in (8, n // 20, n // 2, n - 1):
+                g = H.Guarded((Hkv, budget), torch.int32, -9)
+                ctx.select(sd, Hkv, n, budget, g.t)
+                assert ctx.sync() == dropkv.OK
+                g.check("keep")
+                np.testing.assert_array_equal(g.t.cpu().numpy(),
+                                              orc.select(s.astype(np.float64), budget),
+                                              err_msg=f"wait={wait} n={n} budget={budget}")
+            total = Hkv * n
+            gk = H.Guarded((total // 10,), torch.int32, -9)
+            gc = H.Guarded((Hkv,), torch.int32, -9)
+            ctx.select_layer(sd, Hkv, n, total // 10, gk.t, gc.t)
+            assert ctx.sync() == dropkv.OK
+            wk, wc = orc.select_layer(s.astype(np.float64), total // 10)
+            np.testing.assert_array_equal(gk.t.cpu().numpy(), wk)
+            np.testing.assert_array_equal(gc.t.cpu().numpy(), wc)
+    finally:
+        ctx.set_select_wait(16384)
+    # the default afterwards: the team path, same answers
+    s = rng.random((8, 131072)).astype(np.float32)
+    keep = torch.empty((8, 6553), dtype=torch.int32, device="cuda")
+    ctx.select(torch.from_numpy(s).cuda(), 8, 131072, 6553, keep)
+    assert ctx.sync() == dropkv.OK
+    np.testing.assert_array_equal(keep.cpu().numpy(), orc.select(s.astype(np.float64), 6553))
+
+
 def test_singular_rejected_and_select_withheld(ctx):
     n, d = 40, 8
     q = np.zeros((1, 1, d), np.float32); q[0, 0, 0] = 1.0
