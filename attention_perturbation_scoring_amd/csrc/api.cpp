@@ -15,6 +15,13 @@
 
 using namespace dropkv;
 
+// Scratch of dropkv_score_noalloc, for callers that cannot allocate: one copy
+// per device, resident while the library is loaded.  Host code never uses the
+// array's name as an address: its device address is read once per device with
+// hipGetSymbolAddress (at dropkv_create) and used from then on.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 struct ProfRec {
   std::string name;
   hipEvent_t start, stop;
@@ -32,6 +39,7 @@ struct dropkv_ctx {
     int hkv = 0;                   // head count the zeroed prefix was laid out for
   } sel[2];
   int64_t sel_wait = kSelectWait;  // team-barrier polls before a selection workgroup goes alone
+  void* noalloc_scratch = nullptr; // device address of this device's `scratch` array
   uint32_t* latch = nullptr;       // device word
   uint32_t* latch_host = nullptr;  // pinned read-back
   bool prof = false;
@@ -66,6 +74,23 @@ hipEvent_t get_event(dropkv_ctx* c) {
   hipEvent_t e = nullptr;
   if (hipEventCreate(&e) != hipSuccess) return nullptr;
   return e;
+}
+
+// Device address of the no-allocation scratch array on `device` (the current
+// device), looked up once per device.
+void* noalloc_scratch_ptr(int device) {
+  static std::mutex mu;
+  static void* ptr[64];
+  static bool known[64];
+  if (device < 0 || device >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!known[device]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptr[device] = p;
+    known[device] = true;
+  }
+  return ptr[device];
 }
 
 int to_status(hipError_t e) {
@@ -111,8 +136,13 @@ int dropkv_create(dropkv_ctx** out, int device) {
   // complete before any call, whatever stream it uses
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e == hipSuccess) e = hipHostMalloc(&c->latch_host, sizeof(uint32_t));
+  if (e == hipSuccess) {
+    c->noalloc_scratch = noalloc_scratch_ptr(device);
+    if (!c->noalloc_scratch) e = hipErrorInvalidSymbol;
+  }
   if (e != hipSuccess) {
     if (c->latch) (void)hipFree(c->latch);
+    if (c->latch_host) (void)hipHostFree(c->latch_host);
     delete c;
     return to_status(e);
   }
@@ -160,11 +190,13 @@ int dropkv_plan_splits(int64_t n, int32_t Hkv, int32_t* splits) {
 
 namespace {
 
-// Shared by both scoring entry points: checks, launch geometry, scratch.
+// Shared by the scoring entry points: checks, launch geometry, scratch (the
+// context's, grown on demand, or -- noalloc -- the static per-device array, with
+// no allocation and no profiling events).
 int score_common(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
                  const uint16_t* v_cache, bool attention_only, int64_t n, int32_t w, int32_t Hq,
                  int32_t Hkv, int32_t d, int32_t pool, float* scores, float* out_a,
-                 float* out_lse, void* stream) {
+                 float* out_lse, void* stream, bool noalloc = false) {
   if (!c) return DROPKV_EINVAL;
   if (!aligned16(q_win) || !aligned16(k_cache) || !aligned16(scores)) return DROPKV_EINVAL;
   if ((out_a && !aligned16(out_a)) || (out_lse && !aligned16(out_lse))) return DROPKV_EINVAL;
@@ -194,6 +226,12 @@ int score_common(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
   a.out_a = out_a;
   a.out_lse = out_lse;
   const size_t need = score_scratch_bytes(Hkv * a.R, a.splits, a.DP);
+  if (noalloc) {
+    if (need > kNoAllocScratchBytes) return DROPKV_ESCRATCH;
+    if (!c->noalloc_scratch) return DROPKV_EDEVICE;
+    carve_scratch(c->noalloc_scratch, Hkv * a.R, a.splits, a.DP, &a.part, &a.rs);
+    return to_status(launch_score(nullptr, a, s));
+  }
   if (need > c->scratch_bytes) {
     if (c->scratch) {
       (void)hipStreamSynchronize(s);
@@ -226,6 +264,15 @@ int dropkv_score_ex(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cach
   return score_common(c, q_win, k_cache, v_cache, false, n, w, Hq, Hkv, d, pool, scores, out_a,
                       out_lse, stream);
 }
+
+int dropkv_score_noalloc(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
+                         const uint16_t* v_cache, int64_t n, int32_t w, int32_t Hq, int32_t Hkv,
+                         int32_t d, int32_t pool, float* scores, void* stream) {
+  return score_common(c, q_win, k_cache, v_cache, false, n, w, Hq, Hkv, d, pool, scores, nullptr,
+                      nullptr, stream, true);
+}
+
+int64_t dropkv_noalloc_scratch_bytes(void) { return (int64_t)kNoAllocScratchBytes; }
 
 int dropkv_score_attention(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
                            int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int32_t d, int32_t pool,
@@ -358,6 +405,7 @@ const char* dropkv_strerror(int code) {
     case DROPKV_ERANGE: return "value out of range";
     case DROPKV_EDEVICE: return "HIP runtime error";
     case DROPKV_ENOMEM: return "out of device memory";
+    case DROPKV_ESCRATCH: return "needs more scratch than the no-allocation entry point holds";
     default: return "unknown status";
   }
 }

@@ -16,7 +16,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdropkv.so")
 
-OK, EINVAL, ESINGULAR, ENONFINITE, ERANGE, EDEVICE, ENOMEM = range(7)
+OK, EINVAL, ESINGULAR, ENONFINITE, ERANGE, EDEVICE, ENOMEM, ESCRATCH = range(8)
 KERNELS = ("pass1", "merge", "pass2", "select", "compact", "attn_pass1", "attn_pass2",
            "stream_read")
 
@@ -45,6 +45,7 @@ def lib():
             "dropkv_score": [P, P, P, P, i64, i32, i32, i32, i32, i32, P, P],
             "dropkv_score_attention": [P, P, P, i64, i32, i32, i32, i32, i32, P, P],
             "dropkv_score_ex": [P, P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P],
+            "dropkv_score_noalloc": [P, P, P, P, i64, i32, i32, i32, i32, i32, P, P],
             "dropkv_select": [P, P, i32, i64, i64, P, P],
             "dropkv_select_layer": [P, P, i32, i64, i64, P, P, P],
             "dropkv_compact": [P, P, P, i32, i64, i32, P, i64, P, P, P],
@@ -63,6 +64,8 @@ def lib():
             f = getattr(L, name)
             f.argtypes = args
             f.restype = ctypes.c_int
+        L.dropkv_noalloc_scratch_bytes.argtypes = []
+        L.dropkv_noalloc_scratch_bytes.restype = ctypes.c_int64
         L.dropkv_strerror.argtypes = [ctypes.c_int]
         L.dropkv_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -147,6 +150,11 @@ class Context:
     def score(self, q_win, k_cache, v_cache, n, w, Hq, Hkv, d, pool, scores, stream=None):
         _check(lib().dropkv_score(self._h, _ptr(q_win), _ptr(k_cache), _ptr(v_cache), n, w, Hq,
                                   Hkv, d, pool, _ptr(scores), _stream(stream)), "dropkv_score")
+
+    def score_noalloc(self, q_win, k_cache, v_cache, n, w, Hq, Hkv, d, pool, scores, stream=None):
+        _check(lib().dropkv_score_noalloc(self._h, _ptr(q_win), _ptr(k_cache), _ptr(v_cache), n, w,
+                                          Hq, Hkv, d, pool, _ptr(scores), _stream(stream)),
+               "dropkv_score_noalloc")
 
     def score_ex(self, q_win, k_cache, v_cache, n, w, Hq, Hkv, d, pool, scores, out_a=None,
                  out_lse=None, stream=None):

@@ -58,7 +58,9 @@ enum {
     DROPKV_ENONFINITE = 3, /* a non-finite input element */
     DROPKV_ERANGE = 4,     /* a score beyond FLT_MAX, or a keep index outside [0, n) */
     DROPKV_EDEVICE = 5,    /* a HIP runtime error */
-    DROPKV_ENOMEM = 6      /* scratch allocation failed */
+    DROPKV_ENOMEM = 6,     /* scratch allocation failed */
+    DROPKV_ESCRATCH = 7    /* dropkv_score_noalloc: the call needs more scratch than its
+                              static buffer holds */
 };
 
 typedef struct dropkv_ctx dropkv_ctx;
@@ -92,6 +94,30 @@ int dropkv_destroy(dropkv_ctx *ctx);
 int dropkv_score(dropkv_ctx *ctx, const uint16_t *q_win, const uint16_t *k_cache,
                  const uint16_t *v_cache, int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int32_t d,
                  int32_t pool, float *scores, void *stream);
+
+/*
+ * dropkv_score for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same kernels and the same results, bit for bit, as dropkv_score, but the
+ * split partial states and per-query state live in a static device array of
+ * dropkv_noalloc_scratch_bytes() bytes (16 MiB: the headline Llama-shaped
+ * layer, Hkv = 8, d = 128, w = 8, G = 4, needs 9 MB) instead of the context's
+ * scratch.  The call allocates nothing (no hipMalloc, no events; the context
+ * must exist, and dropkv_create is where the array's device address is read).
+ * Every call on one device shares that device's array and it keeps the last
+ * call's contents; nothing in it needs clearing between calls.  Calls that may
+ * overlap in time on one device -- any two streams without ordering, even with
+ * different contexts -- race on the array and must not be issued.
+ * ESCRATCH (synchronously, nothing launched) if dropkv_scratch_bytes reports a
+ * score scratch above dropkv_noalloc_scratch_bytes() for these sizes.  All
+ * other arguments, checks and latched conditions as for dropkv_score.
+ */
+int dropkv_score_noalloc(dropkv_ctx *ctx, const uint16_t *q_win, const uint16_t *k_cache,
+                         const uint16_t *v_cache, int64_t n, int32_t w, int32_t Hq, int32_t Hkv,
+                         int32_t d, int32_t pool, float *scores, void *stream);
+
+/* Size in bytes of dropkv_score_noalloc's static scratch array. */
+int64_t dropkv_noalloc_scratch_bytes(void);
 
 /*
  * dropkv_score, also handing back what the first pass computes anyway for the

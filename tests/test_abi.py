@@ -14,7 +14,8 @@ HEADER = os.path.join(ROOT, "include", "dropkv.h")
 
 def declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(dropkv_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char \*)\s*(dropkv_\w+)\s*\(", text,
+                                 re.M)))
 
 
 def test_header_declares_the_path():
@@ -49,6 +50,9 @@ def test_host_only_entry_points():
     assert L.dropkv_score(None, None, None, None, 10, 1, 1, 1, 8, 1, None, None) == dropkv.EINVAL
     assert L.dropkv_sync(None, None) == dropkv.EINVAL
     assert L.dropkv_stream_read(None, None, 16, None) == dropkv.EINVAL
+    assert L.dropkv_score_noalloc(None, None, None, None, 10, 1, 1, 1, 8, 1, None, None) == dropkv.EINVAL
+    assert L.dropkv_noalloc_scratch_bytes() == 16 << 20
+    assert dropkv.strerror(dropkv.ESCRATCH).startswith("needs more scratch")
     # scratch at the headline shape: 64 splits x 32 rows x (d + 5) floats per KV
     # head plus per-row state -- megabytes, nothing of size n * d
     sb, selb = dropkv.scratch_bytes(131072, 8, 32, 8, 128)
