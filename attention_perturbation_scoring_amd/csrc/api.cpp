@@ -40,6 +40,7 @@ struct dropkv_ctx {
   } sel[2];
   int64_t sel_wait = kSelectWait;  // team-barrier polls before a selection workgroup goes alone
   void* noalloc_scratch = nullptr; // device address of this device's `scratch` array
+  int score_hv = 0, score_splits = 0, score_dp = 0, score_xh = 0;   // layout of `scratch` (counters zeroed for it)
   uint32_t* latch = nullptr;       // device word
   uint32_t* latch_host = nullptr;  // pinned read-back
   bool prof = false;
@@ -176,7 +177,8 @@ int dropkv_scratch_bytes(int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int32_t 
   const int DP = (d + 31) / 32 * 32, R = (M + kRows - 1) / kRows;
   int64_t len = 0;
   const int splits = plan_splits(n, Hkv * R, &len, kTargetWG1);
-  *score_bytes = (int64_t)score_scratch_bytes(Hkv * R, splits, DP);
+  const int xh = plan_helpers(n, Hkv * R, splits);
+  *score_bytes = (int64_t)score_scratch_bytes(Hkv * R, splits, DP, xh);
   *select_bytes = (int64_t)select_scratch_bytes(Hkv, n);
   return DROPKV_OK;
 }
@@ -225,13 +227,19 @@ int score_common(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
   a.latch = c->latch;
   a.out_a = out_a;
   a.out_lse = out_lse;
-  const size_t need = score_scratch_bytes(Hkv * a.R, a.splits, a.DP);
+  a.xh = plan_helpers(n, Hkv * a.R, a.splits);
+  const size_t need = score_scratch_bytes(Hkv * a.R, a.splits, a.DP, a.xh);
   if (noalloc) {
+    // the array starts zeroed and every call leaves its counters zeroed
     if (need > kNoAllocScratchBytes) return DROPKV_ESCRATCH;
     if (!c->noalloc_scratch) return DROPKV_EDEVICE;
-    carve_scratch(c->noalloc_scratch, Hkv * a.R, a.splits, a.DP, &a.part, &a.rs);
+    carve_scratch(c->noalloc_scratch, Hkv * a.R, a.splits, a.DP, a.xh, &a.part, &a.rs, &a.ex);
     return to_status(launch_score(nullptr, a, s));
   }
+  // a layout change moves the merge's arrival counters: zero them (in stream
+  // order) whenever the scratch or its layout changes; every call leaves them zeroed
+  const bool relayout = need > c->scratch_bytes || Hkv * a.R != c->score_hv ||
+                        a.splits != c->score_splits || a.DP != c->score_dp || a.xh != c->score_xh;
   if (need > c->scratch_bytes) {
     if (c->scratch) {
       (void)hipStreamSynchronize(s);
@@ -244,7 +252,13 @@ int score_common(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
     if (e != hipSuccess) { c->scratch = nullptr; return DROPKV_ENOMEM; }
     c->scratch_bytes = need;
   }
-  carve_scratch(c->scratch, Hkv * a.R, a.splits, a.DP, &a.part, &a.rs);
+  carve_scratch(c->scratch, Hkv * a.R, a.splits, a.DP, a.xh, &a.part, &a.rs, &a.ex);
+  if (!attention_only && relayout) {
+    // the merge's arrival counters and head flags (adjacent in the carve)
+    const hipError_t e = launch_zero(a.ex.cnt, (size_t)(a.ex.head + Hkv * a.R) - (size_t)a.ex.cnt, s);
+    if (e != hipSuccess) return to_status(e);
+    c->score_hv = Hkv * a.R; c->score_splits = a.splits; c->score_dp = a.DP; c->score_xh = a.xh;
+  }
   return to_status(attention_only ? launch_score_attention(c, a, s) : launch_score(c, a, s));
 }
 

@@ -161,9 +161,12 @@ constexpr int kTargetWG1 =   // pass-1 workgroups aimed for
 #endif
 constexpr int kTargetWG2 = DROPKV_P2_TARGET;   // pass-2 workgroups aimed for over all heads
 
-// S_excl below this (argmax probability above ~0.94) routes the arg-max term
-// through the exact exclusion kernel instead of the fp32 output a.
+// A first-pass split whose S_excl is below this (its arg-max holds more than
+// ~0.94 of its mass) is flagged; a row whose winning split is flagged takes
+// its arg-max term and a - v_j* from the exact sum without the arg-max, which
+// the merge's helper workgroups recompute over that split's tokens.
 constexpr float kFixupThreshold = 0.0625f;
+constexpr int kMaxHelpers = 8;    // merge helper workgroups per (KV head, row group)
 
 // Pass 2 takes ||a - v||^2 from the expansion ||a||^2 - 2 a.v + ||v||^2 unless
 // that value is below this fraction of ||a||^2 + ||v||^2: there the expansion's
@@ -196,6 +199,20 @@ struct Partials {
   float* a;       // [Hkv][splits][32][DP] un-normalised output
 };
 
+// Scratch of the exact exclusion sums (see the merge): per virtual head, each
+// helper's partial sums over its share of the winning split's tokens, the row
+// workgroup's sum over the other splits, and per-row arrival counters (zero
+// between calls: the last arrival resets them).
+struct ExclScratch {
+  float* part;     // [Hv][xh][32][DP]  helper h: sum of e_j v_j over its tokens, j != j*
+  float* sx;       // [Hv][xh][32]      helper h: sum of e_j over the same tokens
+  float* ao;       // [Hv][32][DP]      sum over the other splits of f_s a_s
+  float* meta;     // [Hv][32][4]       S, S_excl, S over the other splits, j* (bits)
+  uint32_t* cnt;   // [Hv][32]          arrivals (xh helpers + the row's workgroup)
+  uint32_t* head;  // [Hv]              some split of the virtual head is flagged (set by
+                   //                   the first pass, cleared by the second)
+};
+
 struct ScoreArgs {
   const u16* q;
   const u16* k;
@@ -214,6 +231,8 @@ struct ScoreArgs {
   uint32_t* latch;
   float* out_a;     // optional [Hq][w][d] fp32: each window query's attention output
   float* out_lse;   // optional [Hq][w]: natural-log log-sum-exp of its visible logits
+  int xh;           // merge helper workgroups per virtual head
+  ExclScratch ex;
 };
 
 // Scratch of the selection kernels (owned by the context; hist1 and cand_cnt
@@ -257,9 +276,14 @@ hipError_t launch_compact(void* ctx, const u16* k, const u16* v, int Hkv, int64_
                           const int32_t* keep, int64_t budget, u16* k_out, u16* v_out,
                           uint32_t* latch, hipStream_t s);
 
-// Bytes of scratch the scoring pass needs for these sizes.
-size_t score_scratch_bytes(int Hkv, int splits, int DP);
-void carve_scratch(void* base, int Hkv, int splits, int DP, Partials* p, RowState* rs);
+// Bytes of scratch the scoring pass needs for these sizes (Hkv counts virtual
+// heads: KV heads times row groups; xh merge helpers per virtual head).
+size_t score_scratch_bytes(int Hkv, int splits, int DP, int xh);
+void carve_scratch(void* base, int Hkv, int splits, int DP, int xh, Partials* p, RowState* rs,
+                   ExclScratch* ex);
+// Merge helpers per virtual head: enough to cut the winning split's tokens into
+// pieces of about eight tiles, at most kMaxHelpers and about 1024 over the call.
+int plan_helpers(int64_t n, int Hv, int splits);
 int plan_splits(int64_t n, int Hkv, int64_t* split_len, int target = kTargetWG1);
 hipError_t launch_score_attention(void* ctx, const ScoreArgs& a, hipStream_t s);
 bool score_fits(int DP, int R);

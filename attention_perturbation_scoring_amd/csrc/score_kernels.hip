@@ -198,8 +198,17 @@ __device__ __forceinline__ void load_k_tile(const u16* kg, int64_t tok, bool tok
 // the compiler does not order every later LDS access after it; the caller waits
 // explicitly (vector-memory counter) before reading the destination.
 __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
-               "s"(lds)
+  // the base is wave-uniform by contract; reading it from the first lane lets
+  // the compiler keep it in scalar registers whatever it can prove.  M0 is
+  // written here without a clobber (the compiler reserves it and rejects one);
+  // no compiler-generated code in these kernels reads M0.
+  // (readfirstlane returns int: each half goes through uint32_t, never sign-extended)
+  const uint64_t p = reinterpret_cast<uint64_t>(sbase);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  const uint64_t u = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"(reinterpret_cast<const void*>(u)), "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds))
                : "memory");
 }
 
@@ -604,7 +613,10 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
     a.part.S[pb + r] = Sf;
     a.part.Sx[pb + r] = Sxf;
     a.part.jstar[pb + r] = jbest;
-    a.part.bad[pb + r] = badf;
+    // bit 1: the split's arg-max holds all but S_excl / S < kFixupThreshold of its mass
+    const bool flagged = Mf > -INFINITY && Sxf < kFixupThreshold;
+    a.part.bad[pb + r] = badf | (flagged ? 2 : 0);
+    if (__any(flagged) && tid == 0) atomicOr(a.ex.head + hv, 1u);   // rare
   }
   const float* slabs = reinterpret_cast<const float*>(smem_raw);
   for (int i = tid; i < kRows * DP; i += NT) {   // the group's 32 rows (padding rows are ignored later)
@@ -621,10 +633,22 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
 // partial sums of a are fetched in one round trip; the maximum and its split
 // come from one packed reduction; every reduction has a fixed order (bitwise
 // reproducible); a is summed by float4 column group with the splits
-// partitioned over SG thread groups.  Rows whose arg-max holds
-// probability above ~0.94 then get their arg-max term from the exact
-// exclusion sum, computed by the same workgroup from the other splits' sums
-// and one more pass over the arg-max split's tokens.
+// partitioned over SG thread groups.
+//
+// Rows whose winning split is flagged (its arg-max holds more than ~0.94 of the
+// split's mass) take the arg-max term from the exact output over the other
+// tokens, abar = sum_{j != j*} e_j v_j / S_excl.  Every split but the winning
+// one already sums only tokens other than j* (the first pass partitions the
+// tokens), so only the winning split's tokens are summed again, j* left out.
+// That work is spread over xh helper workgroups per (KV head, row group): each
+// takes a slice of the winning split's tokens for every flagged row of the
+// group.  The row's workgroup and its helpers each count themselves in on a
+// per-row counter after writing their part; whichever arrives last adds the
+// parts in a fixed order and writes the arg-max term (no workgroup ever waits
+// for another).  The helpers take the lowest workgroup indices, so that in the
+// rare call that needs them their first loads reach memory ahead of the row
+// workgroups' (measured: peaked merge ~27 us against ~29 us with helpers
+// last); in the common call they read one flag and exit.
 constexpr int kMaxSplits = 1024;
 
 __device__ __forceinline__ float block_sum256(float x, float* red) {
@@ -634,141 +658,6 @@ __device__ __forceinline__ float block_sum256(float x, float* red) {
   if ((threadIdx.x & 63) == 0) red[wid] = x;
   __syncthreads();
   return red[0] + red[1] + red[2] + red[3];
-}
-__device__ __forceinline__ float block_max256(float x, float* red) {
-  x = wave_max(x);
-  const int wid = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wid] = x;
-  __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-}
-__device__ __forceinline__ int block_min256(int x, int* red) {
-  x = wave_min_i(x);
-  const int wid = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wid] = x;
-  __syncthreads();
-  return min(min(red[0], red[1]), min(red[2], red[3]));
-}
-
-// Sum over the 16 lanes of a DPP row, left in every lane of the row, with
-// VALU moves only: partners lane ^ 1 and lane ^ 2 (quad permutations), then
-// the mirrored lane in the half row and in the row.  After each step all
-// lanes of a quad (then of a half row) hold the same bits, so the mirrored
-// partner gives what the xor partner would, and the sum is the same in every
-// lane and equal to the xor butterfly's.
-__device__ __forceinline__ float row16_sum(float x) {
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xb1, 0xf, 0xf, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4e, 0xf, 0xf, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xf, 0xf, false));
-  return x;
-}
-
-// abar = sum_{j != j*} e_j v_j / sum_{j != j*} e_j over the keys row r sees,
-// then the arg-max token's contribution p*^2 ||abar - v_j*||^2 (algebraically
-// equal to the closed form, without the cancellation in a - v_j* as p* -> 1).
-// The first pass partitions the tokens among its splits, so every split but
-// the arg-max's (sstar) already holds its part of both sums free of j*: the
-// caller passes them combined (ao: this thread's column, Sxo), and only the
-// tokens of split sstar are streamed again here, j* left out.  16 token
-// groups x 16 d-slices per workgroup.
-// It also overwrites the row's a - v_j* (ares_row, d values) with the exact
-// (1 - p*) (abar - v_j*), 1 - p* = Sx / S, which pass 2 uses for tokens whose
-// value row lies close to a.
-template <int DP>
-__device__ float exclusion_term(const ScoreArgs& a, int g, int r, int jst, int sstar, float m2,
-                                float S, float Sx, float ao, float Sxo, float* ares_row,
-                                float* red /* [16][DP+1] */, float* rsx /* [16] */, float* tmp) {
-  // 16 lanes per token: lane ds holds the 16-byte chunks ds, ds + 16, ... of
-  // the row (8 bf16 each); 16 tokens at a time per workgroup, and each lane
-  // keeps U tokens' K and V chunks in flight (tokens visited in index order)
-  constexpr int CH = DP / 8, NCH = (CH + 15) / 16, U = 4;
-  const int tid = threadIdx.x, tg = tid >> 4, ds = tid & 15;
-  const int d = a.d;
-  const int64_t P = a.n - a.w + (r % a.w);
-  const u16* kg = a.k + (size_t)g * a.n * d;
-  const u16* vg = a.v + (size_t)g * a.n * d;
-  const u16* qrow = a.q + ((size_t)g * a.M + r) * d;
-  auto elem = [](const u32x4& x, int e) {   // bf16 element e of a 16-byte chunk, as float
-    const uint32_t w = x[e >> 1];
-    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
-  };
-  float qv[NCH][8], acc[NCH][8];
-#pragma unroll
-  for (int c = 0; c < NCH; ++c)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int dd = (ds + 16 * c) * 8 + e;
-      qv[c][e] = dd < d ? bf2f(qrow[dd]) : 0.f;
-      acc[c][e] = 0.f;
-    }
-  // the split's tokens, in the order of its tiles: i -> token; the row sees
-  // tokens below jlim (the causal bound, and the end of the split or head)
-  const SplitTiles sp(a.n, sstar, a.splits, a.split_len);
-  const int64_t ntok = (int64_t)sp.ntiles * kTile, jlim = min(sp.jend, P + 1);
-  float sx = 0.f;
-  for (int64_t i0 = tg; i0 < ntok; i0 += 16 * U) {
-    u32x4 kx[U][NCH], vx[U][NCH];
-    int64_t jj[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = i0 + 16 * u;
-      const int64_t j = i < ntok ? sp.start((int)(i / kTile)) + i % kTile : jlim;
-      jj[u] = j;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const int ch = ds + 16 * c;
-        kx[u][c] = u32x4{0u, 0u, 0u, 0u};
-        vx[u][c] = u32x4{0u, 0u, 0u, 0u};
-        if (j < jlim && ch * 8 < d) {   // d is a multiple of 8: chunks are whole
-          kx[u][c] = *reinterpret_cast<const u32x4*>(kg + j * d + ch * 8);
-          vx[u][c] = *reinterpret_cast<const u32x4*>(vg + j * d + ch * 8);
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t j = jj[u];
-      float dot = 0.f;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dot += qv[c][e] * elem(kx[u][c], e);
-      dot = row16_sum(dot);
-      const float p = (j >= jlim || j == jst) ? 0.f : ex2(dot * a.scale_log2 - m2);
-#pragma unroll
-      for (int c = 0; c < NCH; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[c][e] += p * elem(vx[u][c], e);
-      sx += p;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int ch = ds + 16 * c;
-    if (ch < CH)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) red[tg * (DP + 1) + ch * 8 + e] = acc[c][e];
-  }
-  if (ds == 0) rsx[tg] = sx;
-  __syncthreads();
-  float tot_sx = Sxo;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) tot_sx += rsx[k];
-  float dist = 0.f;
-  if (tid < d) {
-    float t = ao;
-    for (int k = 0; k < 16; ++k) t += red[k * (DP + 1) + tid];
-    const float df = t / tot_sx - bf2f(vg[(size_t)jst * d + tid]);
-    dist = df * df;
-    ares_row[tid] = (Sx / S) * df;
-  }
-  dist = block_sum256(dist, tmp);
-  const float pstar = 1.f / S;
-  return pstar * pstar * dist;
 }
 
 // Order-preserving uint32 image of a float for max-reductions; NaN and -0 map
@@ -782,30 +671,515 @@ __device__ __forceinline__ uint32_t max_key(float f) {
 __device__ __forceinline__ float from_max_key(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
+// (max key of m2, ~arg-max token): the largest m2, the lowest token on ties
+__device__ __forceinline__ uint64_t split_key(float m2, int j) {
+  return ((uint64_t)max_key(m2) << 32) | (uint32_t)~(uint32_t)j;
+}
+
+__device__ __forceinline__ uint32_t load_agent_u32(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// After this workgroup's writes: count it in on `cnt` (release, agent scope);
+// true, for every thread, if it was the last of `total` arrivals -- its
+// caller then reads the others' writes (acquire already done here).
+__device__ __forceinline__ bool arrive_last(uint32_t* cnt, uint32_t total, int* s_flag) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == total - 1u;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *s_flag = last ? 1 : 0;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// The last arrival for flagged rows rows[0..nl) (arg-max tokens js[0..nl)):
+// abar from the other splits' sum and the helpers' parts (added in helper
+// order), then a - v_j* = (S_excl / S)(abar - v_j*) and the arg-max term
+// p*^2 ||abar - v_j*||^2.  Every load is issued before the first result is
+// used, and every sum has a fixed order, so the result does not depend on which
+// workgroup arrived last.  Whole workgroup; dsq holds nl * DP / 4 floats, sxs
+// and rmeta nl entries; resets the rows' counters.
+template <int DP>
+__device__ void exclusion_combine(const ScoreArgs& a, int hv, const int* rows, const int* js, int nl,
+                                  float* dsq, float* sxs, float4* rmeta) {
+  constexpr int CG = DP / 4;   // float4 column groups of a row
+  // (row, column group) pairs per thread whose loads fly together: all of a
+  // 32-row group's at DP <= 128
+  constexpr int U = DP <= 128 ? (kRows * CG + kThreads - 1) / kThreads : 2;
+  constexpr bool kOneBatch = U * kThreads >= kRows * CG;
+  static_assert(CG % 8 == 0, "eight lanes share a row's distance");
+  const int tid = threadIdx.x;
+  const int g = hv / a.R;
+  // uniform bases; the per-lane offsets below fit 32 bits
+  const float* aob = a.ex.ao + (size_t)hv * kRows * DP;
+  const float* pbase = a.ex.part + (size_t)hv * a.xh * kRows * DP;   // helper h, row r: (h * 32 + r) * DP
+  const float* sxb = a.ex.sx + (size_t)hv * a.xh * kRows;
+  float* aresb = a.rs.ares + (size_t)hv * kRows * DP;
+  const u16* vb = a.v + (size_t)g * a.n * a.d;
+  // the rows' scalars (threads below nl) in the same round trip as the first pairs
+  float4 m = make_float4(0.f, 0.f, 0.f, 0.f);
+  float sxp[kMaxHelpers];
+#pragma unroll
+  for (int h = 0; h < kMaxHelpers; ++h) sxp[h] = 0.f;
+  if (tid < nl) {
+    const int row = rows[tid];
+    m = *reinterpret_cast<const float4*>(a.ex.meta + ((size_t)hv * kRows + row) * 4);   // S, S_excl, S other, -
+#pragma unroll
+    for (int h = 0; h < kMaxHelpers; ++h)
+      if (h < a.xh) sxp[h] = sxb[(uint32_t)(h * kRows + row)];
+  }
+  const int np = nl * CG;
+  float4 ao[U], pv[U][kMaxHelpers];
+  uint2 vv[U];
+  auto load_pairs = [&](int p0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + u * kThreads;
+      const bool in = p < np;
+      const int i = in ? p / CG : 0, cg = in ? p - (p / CG) * CG : 0, row = rows[i];
+      const bool col = in && 4 * cg < a.d;
+      const uint32_t off = (uint32_t)(row * DP + 4 * cg);
+      ao[u] = col ? *reinterpret_cast<const float4*>(aob + off) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int h = 0; h < kMaxHelpers; ++h)
+        pv[u][h] = (col && h < a.xh)
+                       ? *reinterpret_cast<const float4*>(pbase + (uint32_t)(h * kRows * DP) + off)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int jst = js[i];   // checked in range before a row is flagged; kept so here
+      vv[u] = (col && jst >= 0 && jst < a.n)
+                  ? *reinterpret_cast<const uint2*>(vb + (size_t)jst * a.d + 4 * cg)
+                  : make_uint2(0u, 0u);
+    }
+  };
+  auto publish_rows = [&]() {
+    if (tid < nl) {
+      float x = m.z;
+#pragma unroll
+      for (int h = 0; h < kMaxHelpers; ++h) x += sxp[h];
+      sxs[tid] = x;
+      rmeta[tid] = m;
+    }
+    __syncthreads();
+  };
+  auto finish_pairs = [&](int p0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + u * kThreads;
+      if (p >= np) continue;
+      const int i = p / CG, cg = p - i * CG;
+      float4 t = ao[u];
+#pragma unroll
+      for (int h = 0; h < kMaxHelpers; ++h) {
+        t.x += pv[u][h].x; t.y += pv[u][h].y; t.z += pv[u][h].z; t.w += pv[u][h].w;
+      }
+      const float sx = sxs[i];
+      const bool in = 4 * cg < a.d;   // columns past d are zero
+      const float d0 = in ? t.x / sx - __uint_as_float(vv[u].x << 16) : 0.f;
+      const float d1 = in ? t.y / sx - __uint_as_float(vv[u].x & 0xffff0000u) : 0.f;
+      const float d2 = in ? t.z / sx - __uint_as_float(vv[u].y << 16) : 0.f;
+      const float d3 = in ? t.w / sx - __uint_as_float(vv[u].y & 0xffff0000u) : 0.f;
+      const float k = rmeta[i].y / rmeta[i].x;   // S_excl / S
+      *reinterpret_cast<float4*>(aresb + (uint32_t)(rows[i] * DP + 4 * cg)) =
+          make_float4(k * d0, k * d1, k * d2, k * d3);
+      dsq[p] = (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
+    }
+  };
+  if constexpr (kOneBatch) {
+    load_pairs(tid);
+    publish_rows();
+    finish_pairs(tid);
+  } else {
+    const int nb = (np + U * kThreads - 1) / (U * kThreads);
+    for (int bt = 0; bt < nb; ++bt) {
+      load_pairs(bt * U * kThreads + tid);
+      if (bt == 0) publish_rows();
+      finish_pairs(bt * U * kThreads + tid);
+    }
+  }
+  __syncthreads();
+  // a row's squared distance: eight lanes over consecutive column groups, then a
+  // butterfly; lane 0 of the eight holds the fixed-order total
+  {
+    const int i = tid >> 3, k = tid & 7;
+    float x = 0.f;
+    if (i < nl)
+#pragma unroll
+      for (int c = 0; c < CG / 8; ++c) x += dsq[i * CG + k * (CG / 8) + c];
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 1);
+    if (k == 0 && i < nl) {
+      const size_t ro = (size_t)hv * kRows + rows[i];
+      const float pstar = 1.f / rmeta[i].x;
+      a.rs.cstar[ro] = pstar * pstar * x;
+      __hip_atomic_store(a.ex.cnt + ro, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+}
 
 template <int DP>
-__global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
+struct MergeRowLds {
+  float m2[kMaxSplits], S[kMaxSplits], Sx[kMaxSplits], f[kMaxSplits];
+  int j[kMaxSplits], bad[kMaxSplits];
+  float4 red4[kThreads];
+};
+// V tiles in flight per helper wave: two at DP <= 128, one above
+template <int DP>
+constexpr int help_tb() { return DP <= 128 ? 2 : 1; }
+template <int DP>
+struct MergeHelpLds {
+  // the group's Q rows, then help_tb V tile slots per wave (VLayout, as in the
+  // first pass); after the tiles, the slots hold two slabs of sums
+  unsigned char buf[(1 + kWaves * help_tb<DP>()) * kRows * RowLayout<DP>::ROWB];
+  float m2[kRows];
+  int js[kRows], sst[kRows], lim[kRows];
+  int act[kRows];                            // row flagged and in the split being summed
+  float sxw[kWaves][kRows];
+  int nlist, list[kRows];                    // distinct winning splits of flagged rows
+  static_assert(2 * (size_t)kRows * DP * 4 <= (size_t)kWaves * kRows * RowLayout<DP>::ROWB,
+                "two slabs fit the tile slots");
+  static_assert((size_t)kRows * DP <= sizeof(buf), "the combine's squares fit the tiles");
+};
+template <int DP>
+struct MergeCombineLds {
+  float dsq[kRows * DP / 4];
+};
+
+// A helper: the flagged rows of virtual head hv (from the same order-free
+// maximum as their row workgroups), then for each distinct winning split its
+// slice of the split's tokens, summed for every flagged row of that split.
+// The dependent steps are kept few: statistics and Q rows in one round trip,
+// a wave's tile loads (two tiles at DP <= 128: K into registers, V straight
+// into LDS) in the next, one arrival round trip for all rows, and two for the
+// combine.
+template <int DP>
+__device__ void merge_helper(const ScoreArgs& a, int hv, int h, MergeHelpLds<DP>& L, float* dsq,
+                             int* crows, int* cjs, float* csxs, float4* cmeta, int* s_flag) {
+  using RL = RowLayout<DP>;
+  const int tid = threadIdx.x;
+  const int g = hv / a.R, row0 = kRows * (hv % a.R);
+  const int S = a.splits;
+  const size_t base = (size_t)hv * S * kRows;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r = lane & 31;
+  // no split of this virtual head is flagged (the common case): nothing to do
+  if (load_agent_u32(a.ex.head + hv) == 0u) return;
+  // the group's query rows (zero past d and past M), loaded with the statistics
+  RowStage<DP> qst;
+  qst.load(a.q + ((size_t)g * a.M + row0) * a.d, min(kRows, a.M - row0), a.d, a.d);
+  // rows: 8 threads each, splits strided by 8; a batch of SB splits per thread
+  // loaded at once, and the winner found in registers
+  {
+    constexpr int SB = 8;
+    const int row = tid >> 3, k = tid & 7;
+    const bool rok = row0 + row < a.M;
+    const float* m2b = a.part.m2 + base;   // uniform bases, 32-bit offsets
+    const int* jb = a.part.jstar + base;
+    const int* bb = a.part.bad + base;
+    uint64_t best = 0u;
+    int bs = -1, bflag = 0;
+#pragma unroll 1
+    for (int s0 = k; s0 < S; s0 += 8 * SB) {
+      float mv[SB];
+      int jv[SB], bv[SB];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const int sp_ = s0 + 8 * u;
+        const bool ok = rok && sp_ < S;
+        const uint32_t o = (uint32_t)((ok ? sp_ : 0) * kRows + row);
+        mv[u] = ok ? m2b[o] : -INFINITY;
+        jv[u] = ok ? jb[o] : INT_MAX;
+        bv[u] = ok ? bb[o] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const uint64_t key = split_key(mv[u], jv[u]);
+        if (s0 + 8 * u < S && key > best) { best = key; bs = s0 + 8 * u; bflag = bv[u]; }
+      }
+    }
+    uint64_t gbest = best;
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)gbest, o);
+      const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(gbest >> 32), o);
+      const uint64_t ob = ((uint64_t)hi << 32) | lo;
+      gbest = gbest > ob ? gbest : ob;
+    }
+    const float M = from_max_key((uint32_t)(gbest >> 32));
+    const int jst = (int)~(uint32_t)gbest;
+    if (k == 0) {
+      L.sst[row] = -1;
+      L.m2[row] = M;
+      L.js[row] = jst;
+      L.act[row] = 0;
+      L.lim[row] = rok ? (int)(a.n - a.w + ((row0 + row) % a.w)) : -1;
+    }
+    __syncthreads();
+    // the lane holding the winning split (keys are distinct: tokens differ)
+    if (rok && M > -INFINITY && best == gbest && bs >= 0)
+      L.sst[row] = ((bflag & 2) && jst >= 0 && jst < a.n) ? bs : -1;
+    __syncthreads();
+  }
+  // the distinct winning splits of the flagged rows (any order: a row belongs
+  // to exactly one of them)
+  if (wid == 0) {
+    const int s = lane < kRows ? L.sst[lane] : -1;
+    bool first = s >= 0;
+#pragma unroll 1
+    for (int o = 0; o < kRows; ++o) {
+      const int so = __shfl(s, o);
+      if (o < lane && so == s) first = false;
+    }
+    const uint64_t fm = __ballot(first);
+    if (first) L.list[__popcll(fm & ((1ull << lane) - 1ull))] = s;
+    if (lane == 0) L.nlist = __popcll(fm);
+  }
+  __syncthreads();
+  if (L.nlist == 0) return;   // no flagged row: nothing to sum, nobody to meet
+
+  constexpr int NC = DP / 16, DB = DP / 32;
+  constexpr int TB = help_tb<DP>(), VI = VLayout<DP>::CHP / 2;   // VI: loads per V tile
+  unsigned char* qs = L.buf;
+  qst.store(qs);
+  unsigned char* vs0 = L.buf + (size_t)kRows * RL::ROWB * (1 + TB * wid);   // this wave's V slots
+  const u16* kg = a.k + (size_t)g * a.n * a.d;
+  const u16* vg = a.v + (size_t)g * a.n * a.d;
+  __syncthreads();
+  for (int li = 0; li < L.nlist; ++li) {
+    const int s0 = __builtin_amdgcn_readfirstlane(L.list[li]);
+    if (tid < kRows) L.act[tid] = L.sst[tid] == s0 ? 1 : 0;
+    __syncthreads();
+    const bool ract = L.act[r] != 0;
+    const float rm2 = L.m2[r];
+    const int rjs = L.js[r], rlim = L.lim[r];
+    const SplitTiles sp(a.n, s0, a.splits, a.split_len);
+    const int tph = (sp.ntiles + a.xh - 1) / a.xh;   // tiles per helper
+    const int t0 = h * tph, t1 = min(sp.ntiles, t0 + tph);
+    f32x16 acc[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
+    float sx = 0.f;
+    // each wave walks its tiles as in the first pass, TB at a time with every
+    // load issued first (K tiles into registers, then V tiles straight into
+    // the wave's slots); e_j = 2^(l_j - m2) with the row's own maximum, zero
+    // for the arg-max, for keys past the row's causal limit and past the
+    // split, and for rows not summed here
+    for (int tb = t0 + wid; tb < t1; tb += TB * kWaves) {
+      const int nu = (TB > 1 && tb + kWaves < t1) ? 2 : 1;   // tiles this pass (wave-uniform)
+      // lane-derived addresses are recomputed every tile from an opaque copy of
+      // the lane index (as in the first pass), not held in registers across the loop
+      int lx = lane;
+      asm volatile("" : "+v"(lx));
+      const int rx = lx & 31, hx = lx >> 5;
+      // every load first: K tiles into registers (the second into kB), then the
+      // V tiles straight into the wave's slots
+      bf16x8 kA[NC], kB[NC];
+      {
+        const int64_t j0 = sp.start(tb);
+        load_k_tile<NC, false>(kg, j0 + rx, j0 + rx < sp.jend, j0 + kTile > sp.jend, hx, a.d, kA);
+      }
+      if (nu > 1) {
+        const int64_t j1 = sp.start(tb + kWaves);
+        load_k_tile<NC, false>(kg, j1 + rx, j1 + rx < sp.jend, j1 + kTile > sp.jend, hx, a.d, kB);
+      }
+      dma_v_tile<DP>(vg, sp.start(tb), sp.jend, a.d, vs0, lx);
+      if (nu > 1) dma_v_tile<DP>(vg, sp.start(tb + kWaves), sp.jend, a.d, vs0 + kRows * RL::ROWB, lx);
+      // one copy of the tile's code, run nu times (the helper path runs once per
+      // call: its code is cold in the instruction cache, so it is kept short)
+#pragma unroll 1
+      for (int u = 0; u < nu; ++u) {
+        const int64_t j0 = sp.start(tb + u * kWaves);
+        unsigned char* vs = vs0 + (size_t)u * kRows * RL::ROWB;
+        int ly = lane;
+        asm volatile("" : "+v"(ly));
+        const int ry = ly & 31, hy = ly >> 5;
+        f32x16 st;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) st[v] = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) st = mfma32(kA[c], lds8<DP>(qs, ry, 2 * c + hy), st);
+        // offsets within the tile: valid below `end` (the split's end and the
+        // row's causal limit), and not the arg-max's (`skip`, -1 when elsewhere)
+        const int end = ract ? (int)max(min(min(sp.jend - j0, (int64_t)rlim - j0 + 1), (int64_t)kTile),
+                                        (int64_t)0)
+                             : 0;
+        const int skip = (rjs >= j0 && rjs < j0 + kTile) ? (int)(rjs - j0) : -1;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int off = 8 * (v >> 2) + 4 * hy + (v & 3);
+          const bool ok = off < end && off != skip;
+          st[v] = ok ? ex2(st[v] * a.scale_log2 - rm2) : 0.f;
+          sx += st[v];
+        }
+        bf16x8 ph[2], pl[2];
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = st[8 * kc + e];
+            const __bf16 hi = (__bf16)x;
+            ph[kc][e] = hi;
+            pl[kc][e] = (__bf16)(x - (float)hi);
+          }
+        // this tile's V has landed once at most the next tile's V loads are pending
+        if (u + 1 < nu) wait_vmem_below<VI>();
+        else wait_vmem_below<0>();
+        wave_sync_lds();
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          const int gsub = (ly >> 4) & 1, e4 = (ly >> 2) & 3, q = ly & 3;
+          bf16x8 va[DB];
+#pragma unroll
+          for (int b = 0; b < DB; ++b) {
+            s16x4 part[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const int row = 16 * kc + 8 * half + 4 * hy + e4;
+              const int chunk = 4 * b + 2 * gsub + (q >> 1);
+              part[half] = lds_read_tr16(vs + VLayout<DP>::off(row, chunk) + 8 * (q & 1));
+            }
+            va[b] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3,
+                                                                       4, 5, 6, 7));
+          }
+#pragma unroll
+          for (int b = 0; b < DB; ++b) acc[b] = mfma32(va[b], ph[kc], acc[b]);
+#pragma unroll
+          for (int b = 0; b < DB; ++b) acc[b] = mfma32(va[b], pl[kc], acc[b]);
+        }
+        wave_sync_lds();
+        if (u + 1 < nu) {
+#pragma unroll
+          for (int c = 0; c < NC; ++c) kA[c] = kB[c];
+        }
+      }
+    }
+    sx += __shfl_xor(sx, 32);
+    // the waves' sums over the tile slots: waves 0 and 1 store slabs 0 and 1,
+    // waves 2 and 3 add into them, then slab 0 + slab 1: a fixed order.  Rows are padded to DP + 1 floats where two such slabs fit
+    // the slots (the 32 rows one store touches then fall in distinct banks, and
+    // every store is a constant offset from the row); otherwise columns are
+    // XOR-ed with the row within their 32-column block.
+    constexpr bool kPadSlab = 2 * kRows * (DP + 1) * 4 <= TB * kWaves * kRows * RL::ROWB;
+    constexpr int SP = kPadSlab ? DP + 1 : DP;
+    static_assert(2 * kRows * SP * 4 <= TB * kWaves * kRows * RL::ROWB, "two slabs fit the slots");
+    __syncthreads();   // every wave is done with its slots
+    int lz = lane;
+    asm volatile("" : "+v"(lz));
+    const int rz = lz & 31, hz = lz >> 5;
+    float* slab = reinterpret_cast<float*>(L.buf + (size_t)kRows * RL::ROWB);
+    float* mine = slab + (size_t)(wid & 1) * kRows * SP + rz * SP;
+    if (hz == 0) L.sxw[wid][rz] = sx;
+    if (wid < 2) {
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int c = 32 * b + 8 * (v >> 2) + 4 * hz + (v & 3);
+          mine[kPadSlab ? c : (c ^ rz)] = acc[b][v];
+        }
+    }
+    __syncthreads();
+    if (wid >= 2) {
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int c = 32 * b + 8 * (v >> 2) + 4 * hz + (v & 3);
+          mine[kPadSlab ? c : (c ^ rz)] += acc[b][v];
+        }
+    }
+    __syncthreads();
+    // this helper's part for the split's rows
+    const size_t hb = ((size_t)hv * a.xh + h) * kRows;
+#pragma unroll 1
+    for (int i = tid; i < kRows * DP; i += kThreads) {
+      const int row = i / DP, dd = i - row * DP;
+      const int o = row * SP + (kPadSlab ? dd : (dd ^ (row & 31)));
+      if (L.act[row]) a.ex.part[(hb + row) * DP + dd] = slab[o] + slab[kRows * SP + o];
+    }
+    if (tid < kRows && L.act[tid]) {
+      float x = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) x += L.sxw[w][tid];
+      a.ex.sx[hb + tid] = x;
+    }
+    __syncthreads();
+  }
+  // count in on every flagged row at once (one lane per row), then combine
+  // those this helper finished last
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (wid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    bool last = false;
+    if (lane < kRows && L.sst[lane] >= 0) {
+      const uint32_t old = __hip_atomic_fetch_add(a.ex.cnt + (size_t)hv * kRows + lane, 1u,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = old == (uint32_t)a.xh;   // xh helpers + the row's workgroup
+    }
+    const uint64_t lm = __ballot(last);
+    if (lm) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (last) {
+      const int at = __popcll(lm & ((1ull << lane) - 1ull));
+      crows[at] = lane;
+      cjs[at] = L.js[lane];
+    }
+    if (lane == 0) *s_flag = __popcll(lm);
+  }
+  __syncthreads();
+  const int nl = *s_flag;
+  if (nl) exclusion_combine<DP>(a, hv, crows, cjs, nl, dsq, csxs, cmeta);   // dsq overlays the slots
+}
+
+template <int DP>
+__global__ __launch_bounds__(kThreads, (DP <= 128 ? 2 : 1)) void merge_kernel(ScoreArgs a) {
   constexpr int CG = DP / 4;              // float4 column groups of a row of a
   constexpr int SG = kThreads / CG;       // split groups summing a
   constexpr int PF = 8;                   // a loads per thread issued before the weights exist
-  __shared__ float sm_m2[kMaxSplits], sm_S[kMaxSplits], sm_Sx[kMaxSplits], sm_f[kMaxSplits];
-  __shared__ int sm_j[kMaxSplits];
-  __shared__ float4 red4[SG * CG];
+  // one LDS region for the role of the workgroup; the combine's squares reuse
+  // it once the row workgroup's arrays or the helper's tiles are done with
+  __shared__ __align__(16) union {
+    MergeRowLds<DP> r;
+    MergeHelpLds<DP> h;
+    MergeCombineLds<DP> c;
+  } lds;
+  __shared__ int crows[kRows], cjs[kRows];
+  __shared__ float csxs[kRows];
+  __shared__ float4 cmeta[kRows];
   __shared__ uint64_t rk[kWaves];
-  __shared__ int s_star;
+  __shared__ int s_star, s_flag;
   __shared__ float rf[3][kWaves];
   __shared__ uint32_t ro_[2][kWaves];
-  __shared__ float red[16 * (DP + 1)];
-  __shared__ float rsx[16];
   __shared__ float tmp[kWaves];
+  float* sm_m2 = lds.r.m2;
+  float* sm_S = lds.r.S;
+  float* sm_Sx = lds.r.Sx;
+  float* sm_f = lds.r.f;
+  int* sm_j = lds.r.j;
+  int* sm_bad = lds.r.bad;
+  float4* red4 = lds.r.red4;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   // virtual head hv = (KV head g, row group); r is the row within the group and
   // rg_row the window query row within the KV head.  A group has RB =
   // min(32, M) workgroups: with fewer than 32 window rows per KV head, the
   // workgroup of row r also zeroes the padded rows r + RB, r + 2 RB, ... of
-  // its group, which have no window row to merge.
+  // its group, which have no window row to merge.  The helpers come first.
   const int RB = min(kRows, a.M);
-  const int hv = blockIdx.x / RB, r = blockIdx.x % RB;
+  const int nhelp = a.Hkv * a.R * a.xh;
+  if ((int)blockIdx.x < nhelp) {
+    const int hb = blockIdx.x;
+    merge_helper<DP>(a, hb / a.xh, hb % a.xh, lds.h, lds.c.dsq, crows, cjs, csxs, cmeta, &s_flag);
+    return;
+  }
+  const int bx = blockIdx.x - nhelp;
+  const int hv = bx / RB, r = bx % RB;
   const int g = hv / a.R, rg_row = kRows * (hv % a.R) + r;
   const size_t ro = (size_t)hv * kRows + r;
   auto zero_row = [&](size_t rz) {   // padded rows: zero operands so pass 2's MFMA rows stay inert
@@ -839,7 +1213,6 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
     av[k] = (sum_lane && s < S) ? *reinterpret_cast<const float4*>(pa + (size_t)s * kRows * DP)
                                 : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  // (max key of m2, ~arg-max token): the largest m2, the lowest token on ties
   uint64_t best = 0u;
   uint32_t badl = 0u;
   for (int s = tid; s < S; s += kThreads) {
@@ -849,8 +1222,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
     sm_S[s] = a.part.S[o];
     sm_Sx[s] = a.part.Sx[o];
     sm_j[s] = a.part.jstar[o];
-    badl |= a.part.bad[o] ? 1u : 0u;
-    const uint64_t k = ((uint64_t)max_key(ms) << 32) | (uint32_t)~(uint32_t)sm_j[s];
+    const int bd = a.part.bad[o];
+    sm_bad[s] = bd;
+    badl |= (bd & 1) ? 1u : 0u;
+    const uint64_t k = split_key(ms, sm_j[s]);
     best = best > k ? best : k;
   }
   best = wave_max_u64(best);
@@ -860,19 +1235,24 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
   for (int w = 0; w < kWaves; ++w) best = best > rk[w] ? best : rk[w];
   const float M = from_max_key((uint32_t)(best >> 32));
   const bool have = M > -INFINITY;
-  // the split holding the winning token (tokens are distinct across splits)
-  if (tid == 0) s_star = -1;
+  // the split holding the winning token (tokens are distinct across splits),
+  // and whether it is flagged
+  if (tid == 0) { s_star = -1; s_flag = 0; }
   __syncthreads();
   if (have)
     for (int s = tid; s < S; s += kThreads)
-      if (sm_m2[s] > -INFINITY && ((((uint64_t)max_key(sm_m2[s]) << 32) |
-                                    (uint32_t)~(uint32_t)sm_j[s]) == best))
+      if (sm_m2[s] > -INFINITY && split_key(sm_m2[s], sm_j[s]) == best) {
         s_star = s;
+        s_flag = (sm_bad[s] & 2) ? 1 : 0;
+      }
   __syncthreads();
   const int sstar = have ? s_star : -1;
   int jst = (sstar >= 0) ? sm_j[sstar] : -1;
   uint32_t bad = 0u;
   if (jst < 0 || jst >= a.n) { jst = -1; bad = 1u; }
+  // the row takes the exact arg-max term (helpers sum the winning split again);
+  // decided exactly as the helpers decide it
+  const bool fix = sstar >= 0 && jst >= 0 && s_flag != 0;
   // the arg-max token's value row, needed at the end
   const float vstar = (tid < a.d && jst >= 0) ? bf2f(a.v[((size_t)g * a.n + jst) * a.d + tid]) : 0.f;
 
@@ -896,19 +1276,24 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
   for (int w = 0; w < kWaves; ++w) { Sf += rf[0][w]; Sxo += rf[1][w]; bad |= ro_[0][w]; }
   const float Sx = have ? sm_Sx[sstar] + Sxo : 0.f;
 
-  // a = sum_s f_s a_s / S: each thread sums its column group over its splits
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  // a = sum_s f_s a_s / S, and for a flagged row also the sum without the
+  // arg-max's split: each thread sums its column group over its splits
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f), acx = acc;
   if (sum_lane) {
 #pragma unroll
     for (int k = 0; k < PF; ++k) {
       const int s = sg + SG * k;
       const float f = s < S ? sm_f[s] : 0.f;
+      const float fx = s != sstar ? f : 0.f;
       acc.x += av[k].x * f; acc.y += av[k].y * f; acc.z += av[k].z * f; acc.w += av[k].w * f;
+      acx.x += av[k].x * fx; acx.y += av[k].y * fx; acx.z += av[k].z * fx; acx.w += av[k].w * fx;
     }
     for (int s = sg + SG * PF; s < S; s += SG) {
       const float4 x = *reinterpret_cast<const float4*>(pa + (size_t)s * kRows * DP);
       const float f = sm_f[s];
+      const float fx = s != sstar ? f : 0.f;
       acc.x += x.x * f; acc.y += x.y * f; acc.z += x.z * f; acc.w += x.w * f;
+      acx.x += x.x * fx; acx.y += x.y * fx; acx.z += x.z * fx; acx.w += x.w * fx;
     }
     red4[sg * CG + cg] = acc;
   }
@@ -929,8 +1314,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
     const __bf16 lo = (__bf16)(avv - (float)hi);
     a.rs.a_hi[ro * DP + tid] = __builtin_bit_cast(u16, hi);
     a.rs.a_lo[ro * DP + tid] = __builtin_bit_cast(u16, lo);
-    // a - v_j* (zero past d); rows that take the exclusion sum below overwrite it
-    a.rs.ares[ro * DP + tid] = avv - vstar;
+    // a - v_j* (zero past d); a flagged row's comes from the exact sum instead
+    if (!fix) a.rs.ares[ro * DP + tid] = avv - vstar;
     // row r of head g is window query (g * G + r / w, r % w): [Hq][w][d] order
     if (a.out_a && tid < a.d) a.out_a[((size_t)g * a.M + rg_row) * a.d + tid] = avv;
     if (tid < a.d && jst >= 0) {
@@ -946,44 +1331,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
   an2 = 0.f; dist = 0.f; nonfin = 0u;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) { an2 += rf[2][w]; dist += tmp[w]; nonfin |= ro_[1][w]; }
-  __syncthreads();   // tmp is reused by the exclusion sum
   nonfin |= bad | (!(Sf <= FLT_MAX) ? 1u : 0u) | (!have ? 1u : 0u);
   const bool singular = !nonfin && !(Sx > 0x1p-53f);
-  const bool fix = !nonfin && !singular && Sx < kFixupThreshold;
-  float cstar = (nonfin || singular) ? 0.f : dist / (Sx * Sx);
-  if (fix) {
-    // sum_s f_s a_s over every split but the arg-max's (red4 was last read
-    // before the barrier above)
-    // (PF loads in flight per thread: all issued before any is used)
-    float4 acx = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (sum_lane) {
-      for (int s0 = sg; s0 < S; s0 += SG * PF) {
-        float4 x[PF];
-#pragma unroll
-        for (int k = 0; k < PF; ++k) {
-          const int s = s0 + SG * k;
-          x[k] = (s < S && s != sstar) ? *reinterpret_cast<const float4*>(pa + (size_t)s * kRows * DP)
-                                       : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int k = 0; k < PF; ++k) {
-          const int s = s0 + SG * k;
-          const float f = (s < S && s != sstar) ? sm_f[s] : 0.f;
-          acx.x += x[k].x * f; acx.y += x[k].y * f; acx.z += x[k].z * f; acx.w += x[k].w * f;
-        }
-      }
-      red4[sg * CG + cg] = acx;
-    }
-    __syncthreads();
-    float ao = 0.f;
-    if (tid < DP) {
-      const float* rr = reinterpret_cast<const float*>(red4);
-#pragma unroll
-      for (int k = 0; k < SG; ++k) ao += rr[k * DP + tid];
-    }
-    cstar = exclusion_term<DP>(a, g, rg_row, jst, sstar, M, Sf, Sx, ao, Sxo, a.rs.ares + ro * DP, red,
-                               rsx, tmp);
-  }
   if (tid == 0) {
     a.rs.m2[ro] = M;
     a.rs.S[ro] = Sf;
@@ -992,9 +1341,30 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(ScoreArgs a) {
     a.rs.an2[ro] = an2;
     a.rs.jstar[ro] = jst;
     a.rs.fix[ro] = fix ? 1 : 0;
-    a.rs.cstar[ro] = cstar;
+    if (!fix) a.rs.cstar[ro] = (nonfin || singular) ? 0.f : dist / (Sx * Sx);
     const uint32_t bits = (nonfin ? LATCH_NONFINITE : 0u) | (singular ? LATCH_SINGULAR : 0u);
     if (bits) atomicOr(a.latch, bits);
+  }
+  if (!fix) return;
+  // the other splits' part of the exact sum, then count in with the helpers
+  __syncthreads();   // red4 is reused
+  if (sum_lane) red4[sg * CG + cg] = acx;
+  __syncthreads();
+  if (tid < DP) {
+    const float* rr = reinterpret_cast<const float*>(red4);
+    float ao = 0.f;
+#pragma unroll
+    for (int k = 0; k < SG; ++k) ao += rr[k * DP + tid];
+    a.ex.ao[ro * DP + tid] = ao;
+  }
+  if (tid == 0) {
+    float* meta = a.ex.meta + ro * 4;
+    meta[0] = Sf; meta[1] = Sx; meta[2] = Sxo; meta[3] = __int_as_float(jst);
+  }
+  if (arrive_last(a.ex.cnt + ro, (uint32_t)a.xh + 1u, &s_flag)) {
+    if (tid == 0) { crows[0] = r; cjs[0] = jst; }
+    __syncthreads();
+    exclusion_combine<DP>(a, hv, crows, cjs, 1, lds.c.dsq, csxs, cmeta);
   }
 }
 
@@ -1126,7 +1496,9 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
   }
   const float invG = 1.f / (float)a.G;
   uint32_t flags = 0;
-  __syncthreads();
+  // the merge has read this KV head's flags: clear them for the next call
+  if (ch == 0 && tid < R) a.ex.head[(size_t)g * R + tid] = 0u;
+  __syncthreads();   // the staged rows and their state, for every wave
 
   auto issue = [&](int t, bf16x8 (&kk)[NC], bf16x8 (&vv)[NC]) {
     const int64_t t0 = e0 + (int64_t)t * kTile;
@@ -1677,14 +2049,17 @@ int plan_chunks2(int64_t n, int Hkv, int64_t* chunk_len, int target) {
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-size_t score_scratch_bytes(int Hkv, int splits, int DP) {
+size_t score_scratch_bytes(int Hkv, int splits, int DP, int xh) {
   const size_t prow = (size_t)Hkv * splits * kRows;
   const size_t rrow = (size_t)Hkv * kRows;
   return align256(prow * 4) * 5 + align256(prow * DP * 4) + align256(rrow * 4) * 7 +
-         align256(rrow * DP * 2) * 2 + align256(rrow * DP * 4);
+         align256(rrow * DP * 2) * 2 + align256(rrow * DP * 4) +
+         align256(rrow * xh * DP * 4) + align256(rrow * xh * 4) + align256(rrow * DP * 4) +
+         align256(rrow * 4 * 4) + align256(rrow * 4) + align256((size_t)Hkv * 4);
 }
 
-void carve_scratch(void* base, int Hkv, int splits, int DP, Partials* p, RowState* rs) {
+void carve_scratch(void* base, int Hkv, int splits, int DP, int xh, Partials* p, RowState* rs,
+                   ExclScratch* ex) {
   char* c = static_cast<char*>(base);
   const size_t prow = (size_t)Hkv * splits * kRows;
   const size_t rrow = (size_t)Hkv * kRows;
@@ -1705,6 +2080,22 @@ void carve_scratch(void* base, int Hkv, int splits, int DP, Partials* p, RowStat
   rs->a_hi = (u16*)take(rrow * DP * 2);
   rs->a_lo = (u16*)take(rrow * DP * 2);
   rs->ares = (float*)take(rrow * DP * 4);
+  ex->part = (float*)take(rrow * xh * DP * 4);
+  ex->sx = (float*)take(rrow * xh * 4);
+  ex->ao = (float*)take(rrow * DP * 4);
+  ex->meta = (float*)take(rrow * 4 * 4);
+  ex->cnt = (uint32_t*)take(rrow * 4);
+  ex->head = (uint32_t*)take((size_t)Hkv * 4);   // right after cnt: one zeroed range
+}
+
+int plan_helpers(int64_t n, int Hv, int splits) {
+  const int64_t tiles = ((n + kTile - 1) / kTile + splits - 1) / splits;   // per split
+  int64_t xh = (tiles + 7) / 8;   // two tiles per wave of a helper
+  const int64_t cap = 1024 / Hv;
+  if (xh > cap) xh = cap;
+  if (xh > kMaxHelpers) xh = kMaxHelpers;
+  if (xh < 1) xh = 1;
+  return (int)xh;
 }
 
 template <int DP, bool FULLD>
@@ -1721,7 +2112,10 @@ static hipError_t launch_score_dp(void* ctx, const ScoreArgs& a, hipStream_t s) 
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   prof_begin(ctx, "merge", s);
-  hipLaunchKernelGGL(merge_kernel<DP>, dim3(a.Hkv * a.R * (a.M < kRows ? a.M : kRows)), dim3(kThreads), 0, s, a);
+  // xh helpers per (KV head, row group), then the row workgroups
+  hipLaunchKernelGGL(merge_kernel<DP>,
+                     dim3(a.Hkv * a.R * ((a.M < kRows ? a.M : kRows) + a.xh)), dim3(kThreads), 0, s,
+                     a);
   prof_end(ctx, "merge", s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

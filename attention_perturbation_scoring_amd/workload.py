@@ -20,6 +20,11 @@ values are synthetic:
 * "sink" workloads then add to keys 0..3 of every KV head the least-norm vector
   b_g that raises every window query's logit by +6 (q . b_g / sqrt(d) = 6 for all
   G*w queries of the group, solved in float64 with ``numpy.linalg.lstsq``).
+* "sink-heavy" workloads (recipe ``llama_sink``) do all of the above and then
+  replace key 0 of every KV head by the least-norm vector that sets every
+  window query's logit on it to 20 (float64 least squares): at 128K tokens
+  every window query then puts p > 0.99 on token 0, an attention-sink pattern
+  strong enough that each row's arg-max holds more than 0.94 of its mass.
 * Everything is finally rounded to bfloat16 (round to nearest, ties to even).
   Both sides see only these bf16 bytes.
 
@@ -47,7 +52,7 @@ class Config:
     budget: int          # kept tokens per KV head (includes the protected window)
     seed: int
     layers: int = 1
-    recipe: str = "llama"  # "tiny" (plain normal + acceptance predicate) or "llama"
+    recipe: str = "llama"  # "tiny" (plain normal + acceptance predicate), "llama" or "llama_sink"
 
     @property
     def G(self) -> int:
@@ -82,8 +87,15 @@ LLAMA_128K = Config("llama128k", Hq=32, Hkv=8, d=128, n=131072, w=8, pool=7,
                     budget=budget_for(131072, 5), seed=9)
 PHI3_FULL = Config("phi3full", Hq=32, Hkv=32, d=96, n=131072, w=8, pool=7,
                    budget=budget_for(131072, 5), seed=1000, layers=32)
+# Sink-heavy variants of the Llama cases: every window row's arg-max (token 0)
+# holds more than 0.94 of its attention.
+LLAMA_4K_SINK = Config("llama4k_sink", Hq=32, Hkv=8, d=128, n=4096, w=8, pool=7,
+                       budget=budget_for(4096, 5), seed=17, recipe="llama_sink")
+LLAMA_128K_SINK = Config("llama128k_sink", Hq=32, Hkv=8, d=128, n=131072, w=8, pool=7,
+                         budget=budget_for(131072, 5), seed=19, recipe="llama_sink")
 
-CONFIGS = {c.name: c for c in (TINY, LLAMA_4K, LLAMA_32K, LLAMA_128K, PHI3_FULL)}
+CONFIGS = {c.name: c for c in (TINY, LLAMA_4K, LLAMA_32K, LLAMA_128K, PHI3_FULL, LLAMA_4K_SINK,
+                               LLAMA_128K_SINK)}
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -124,6 +136,16 @@ def _outliers_and_sinks(rng, q32, k32, Hkv, G, w, d, n_sinks=4, boost=6.0, scale
         k32[g][:n_s] += b.astype(np.float32)[None, :]
 
 
+def _heavy_sink(q32, k32, Hkv, G, w, d, logit=20.0):
+    """In place: key 0 of every KV head becomes the least-norm vector that sets
+    every window query's logit on it to `logit` (float64 least squares)."""
+    for g in range(Hkv):
+        qg = q32[g * G:(g + 1) * G].reshape(G * w, d).astype(np.float64)
+        rhs = np.full(G * w, logit * np.sqrt(d), dtype=np.float64)
+        b, *_ = np.linalg.lstsq(qg, rhs, rcond=None)
+        k32[g][0] = b.astype(np.float32)
+
+
 def make_layer(cfg: Config, seed: int, accept: Optional[Callable] = None, max_tries: int = 1000):
     """One layer's bf16 inputs: dict(q=[Hq][w][d], k=[Hkv][n][d], v=[Hkv][n][d], tries=int).
 
@@ -137,8 +159,10 @@ def make_layer(cfg: Config, seed: int, accept: Optional[Callable] = None, max_tr
         q32 = _draw_normal(rng, (cfg.Hq, cfg.w, cfg.d))
         k32 = _draw_normal(rng, (cfg.Hkv, cfg.n, cfg.d))
         v32 = _draw_normal(rng, (cfg.Hkv, cfg.n, cfg.d))
-        if cfg.recipe == "llama":
+        if cfg.recipe in ("llama", "llama_sink"):
             _outliers_and_sinks(rng, q32, k32, cfg.Hkv, cfg.G, cfg.w, cfg.d)
+        if cfg.recipe == "llama_sink":
+            _heavy_sink(q32, k32, cfg.Hkv, cfg.G, cfg.w, cfg.d)
         q, k, v = bf16_bits(q32), bf16_bits(k32), bf16_bits(v32)
         del q32, k32, v32
         if accept is None or accept(q, k, v):

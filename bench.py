@@ -152,6 +152,47 @@ def time_peaked_rows(ctx, cfg, inp, dev, v_dev, scores, stream):
             "planted_token": jp, "kernel_us": us}
 
 
+def time_sink_heavy(ctx, cfg, dev, scores, keep, stream, steps):
+    """Per-kernel HIP-event times of score + select on the sink-heavy variant of
+    the workload (same shapes; every window row puts more than 0.94 of its
+    attention on token 0, so every row takes the exact exclusion fixup), or
+    None when the workload has no such variant."""
+    import torch
+    from attention_perturbation_scoring_amd import dropkv, workload as wl
+    sc = wl.CONFIGS.get(cfg.name + "_sink")
+    if sc is None:
+        return None
+    inp = wl.make_layer(sc, sc.seed)
+    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    del inp
+    Hq, Hkv, d, n, w, pool, budget = sc.Hq, sc.Hkv, sc.d, sc.n, sc.w, sc.pool, sc.budget
+
+    def call():
+        ctx.score(q, k, v, n, w, Hq, Hkv, d, pool, scores, stream)
+        ctx.select(scores, Hkv, n, budget, keep, stream)
+
+    call()
+    status = ctx.sync(stream)
+    if status != dropkv.OK:
+        raise SystemExit(f"sink-heavy: device status {dropkv.strerror(status)}")
+    ctx.profile(True)
+    ctx.profile_reset()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    us = {}
+    for name in ("pass1", "merge", "pass2", "select"):
+        tot, cnt = ctx.profile_read(name)
+        if cnt:
+            us[name] = round(1e3 * tot / cnt, 2)
+    ctx.profile(False)
+    ctx.check(stream)
+    return {"workload": sc.name,
+            "what": "score + select with every window row's arg-max (token 0) above 0.94 "
+                    "of its attention (exact exclusion fixup on every row)",
+            "kernel_us": us, "score_select_us": round(sum(us.values()), 2)}
+
+
 def scratch_report(n, w, Hq, Hkv, d):
     """Device scratch the library holds for one call of these sizes, beside the
     pages' figures for the same question (n = 128K: ~17 MB for the fused Triton
@@ -357,10 +398,12 @@ def run(args):
         layer_select_us = time_layer_select(ctx, scores, Hkv, n, budget, stream, args)
 
     # ---- the same layer with every window row peaked (the exclusion fixup) ----
-    peaked_rows = None
+    peaked_rows = sink_heavy = None
     if L == 1:
         log("[bench] peaked rows")
         peaked_rows = time_peaked_rows(ctx, cfg, inp, dev, copies[0][2], scores, stream)
+        log("[bench] sink-heavy variant")
+        sink_heavy = time_sink_heavy(ctx, cfg, dev, scores, keep, stream, max(3, min(args.steps, 10)))
 
     # ---- per-call distribution with the caches flushed before every call ----
     # Streaming 1 GiB through the caches evicts the 4 MB L2s and the 256 MB
@@ -461,6 +504,7 @@ def run(args):
         "attention_mode": attention_mode,
         "layer_select_us": layer_select_us,
         "peaked_rows": peaked_rows,
+        "sink_heavy": sink_heavy,
         "kernel_source_hash": kernel_source_hash(),
         "scratch_bytes": scratch_report(n, w, Hq, Hkv, d),
     }

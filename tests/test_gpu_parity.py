@@ -96,7 +96,7 @@ def test_shapes(ctx, shape):
     _full_check(ctx, q, k, v, pool, budget, f"shape {shape}")
 
 
-@pytest.mark.parametrize("name", ["llama4k", "llama32k", "llama128k"])
+@pytest.mark.parametrize("name", ["llama4k", "llama32k", "llama128k", "llama4k_sink", "llama128k_sink"])
 def test_llama_configs(ctx, name):
     cfg = wl.CONFIGS[name]
     inp = wl.make_layer(cfg, cfg.seed)

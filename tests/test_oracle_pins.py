@@ -284,6 +284,22 @@ def test_generator_deterministic_and_structured():
         assert abs(sink.mean() - 6.0) < 1.0 and abs(plain.mean()) < 0.5
 
 
+def test_sink_heavy_recipe_puts_most_mass_on_token_0():
+    """Every window query of the sink-heavy Llama case puts more than 0.94 of its
+    attention on token 0 (plain float64 softmax over its visible keys)."""
+    cfg = wl.CONFIGS["llama4k_sink"]
+    inp = wl.make_layer(cfg, cfg.seed)
+    qf, kf = brute.widen(inp["q"]), brute.widen(inp["k"])
+    G, n, w, d = cfg.G, cfg.n, cfg.w, cfg.d
+    for h in range(cfg.Hq):
+        g = h // G
+        for t in range(w):
+            l = (kf[g, :n - w + t + 1] @ qf[h, t]) / np.sqrt(d)
+            p = np.exp(l - l.max())
+            p /= p.sum()
+            assert int(np.argmax(p)) == 0 and p[0] > 0.94, (h, t, p[0])
+
+
 def test_bf16_rounding_is_nearest_even():
     x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, np.inf, -np.inf], dtype=np.float32)
     b = wl.bf16_bits(x)
