@@ -136,7 +136,7 @@ int dropkv_create(dropkv_ctx** out, int device) {
   if (e == hipSuccess) e = hipMemset(c->latch, 0, 256);
   // complete before any call, whatever stream it uses
   if (e == hipSuccess) e = hipDeviceSynchronize();
-  if (e == hipSuccess) e = hipHostMalloc(&c->latch_host, sizeof(uint32_t));
+  if (e == hipSuccess) e = hipHostMalloc(&c->latch_host, 2 * sizeof(uint32_t));
   if (e == hipSuccess) {
     c->noalloc_scratch = noalloc_scratch_ptr(device);
     if (!c->noalloc_scratch) e = hipErrorInvalidSymbol;
@@ -198,7 +198,7 @@ namespace {
 int score_common(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
                  const uint16_t* v_cache, bool attention_only, int64_t n, int32_t w, int32_t Hq,
                  int32_t Hkv, int32_t d, int32_t pool, float* scores, float* out_a,
-                 float* out_lse, void* stream, bool noalloc = false) {
+                 float* out_lse, void* stream, bool noalloc = false, int64_t cap = 0) {
   if (!c) return DROPKV_EINVAL;
   if (!aligned16(q_win) || !aligned16(k_cache) || !aligned16(scores)) return DROPKV_EINVAL;
   if ((out_a && !aligned16(out_a)) || (out_lse && !aligned16(out_lse))) return DROPKV_EINVAL;
@@ -217,6 +217,7 @@ int score_common(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
   ScoreArgs a{};
   a.q = q_win; a.k = k_cache; a.v = v_cache; a.scores = scores;
   a.n = n; a.w = w; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.G = G; a.M = G * w; a.pool = pool;
+  a.hs = (cap > 0 ? cap : n) * (int64_t)d;   // a resident cache keeps cap rows per head
   a.DP = (d + 31) / 32 * 32;
   a.R = (a.M + kRows - 1) / kRows;
   if (!attention_only && !score_fits(a.DP, a.R)) return DROPKV_EINVAL;
@@ -382,6 +383,37 @@ int dropkv_compact(dropkv_ctx* c, const uint16_t* k, const uint16_t* v, int32_t 
                                   static_cast<hipStream_t>(stream)));
 }
 
+int dropkv_compact_inplace(dropkv_ctx* c, uint16_t* k_cache, uint16_t* v_cache, int32_t Hkv,
+                           int64_t cap, int64_t n_valid, int32_t d, const int32_t* keep,
+                           int64_t budget, void* stream) {
+  if (!c) return DROPKV_EINVAL;
+  if (Hkv < 1 || cap < 1 || cap >= (int64_t(1) << 31) || n_valid < 1 || n_valid > cap || d < 8 ||
+      d % 8 != 0 || d > 256)
+    return DROPKV_EINVAL;
+  if (budget < 0 || budget > n_valid) return DROPKV_EINVAL;
+  if (budget == 0) return DROPKV_OK;  // nothing moves
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(keep)) return DROPKV_EINVAL;
+  DeviceGuard guard(c->device);
+  if (!guard.ok) return DROPKV_EDEVICE;
+  return to_status(launch_compact_inplace(c, k_cache, v_cache, Hkv, cap * (int64_t)d, d, n_valid, keep,
+                                          budget, c->latch, static_cast<hipStream_t>(stream)));
+}
+
+int dropkv_rescore(dropkv_ctx* c, const uint16_t* q_win, uint16_t* k_cache, uint16_t* v_cache,
+                   int64_t cap, int64_t n_valid, int32_t w, int32_t Hq, int32_t Hkv, int32_t d,
+                   int32_t pool, int64_t budget, float* scores, int32_t* keep, void* stream) {
+  if (!c) return DROPKV_EINVAL;
+  if (cap < 1 || cap >= (int64_t(1) << 31) || n_valid < 1 || n_valid > cap) return DROPKV_EINVAL;
+  if (budget < 0 || budget > n_valid) return DROPKV_EINVAL;
+  if (budget > 0 && !aligned16(keep)) return DROPKV_EINVAL;
+  int rc = score_common(c, q_win, k_cache, v_cache, false, n_valid, w, Hq, Hkv, d, pool, scores,
+                        nullptr, nullptr, stream, false, cap);
+  if (rc != DROPKV_OK || budget == 0) return rc;
+  rc = dropkv_select(c, scores, Hkv, n_valid, budget, keep, stream);
+  if (rc != DROPKV_OK) return rc;
+  return dropkv_compact_inplace(c, k_cache, v_cache, Hkv, cap, n_valid, d, keep, budget, stream);
+}
+
 int dropkv_stream_read(dropkv_ctx* c, const void* p, int64_t bytes, void* stream) {
   if (!c || bytes <= 0 || bytes % 16 != 0 || !aligned16(p)) return DROPKV_EINVAL;
   DeviceGuard guard(c->device);
@@ -395,12 +427,13 @@ int dropkv_sync(dropkv_ctx* c, void* stream) {
   DeviceGuard guard(c->device);
   if (!guard.ok) return DROPKV_EDEVICE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipMemcpyAsync(c->latch_host, c->latch, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+  // word 0: scoring, selection and packing; word 1: the in-place compaction's checks
+  hipError_t e = hipMemcpyAsync(c->latch_host, c->latch, 2 * sizeof(uint32_t), hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return to_status(e);
-  const uint32_t bits = *c->latch_host;
+  const uint32_t bits = c->latch_host[0] | c->latch_host[1];
   if (bits) {
-    e = hipMemsetAsync(c->latch, 0, sizeof(uint32_t), s);
+    e = hipMemsetAsync(c->latch, 0, 2 * sizeof(uint32_t), s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return to_status(e);
   }

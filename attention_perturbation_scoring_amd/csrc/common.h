@@ -219,6 +219,8 @@ struct ScoreArgs {
   const u16* v;
   float* scores;
   int64_t n;
+  int64_t hs;           // elements from one KV head's K (and V) rows to the next: n * d, or cap * d
+                        // for a resident cache of capacity cap
   int w, Hq, Hkv, d, G, M, pool, DP;
   int R;                // 32-row groups per KV head: ceil(M / 32), at most kMaxRowGroups
   int splits;
@@ -272,6 +274,13 @@ hipError_t launch_select(void* ctx, const float* scores, int Hkv, int64_t n, int
                          hipStream_t s);
 hipError_t launch_layer_counts(void* ctx, const int32_t* keep, int64_t budget, int64_t n, int Hkv,
                                int32_t* counts, uint32_t* latch, hipStream_t s);
+// In place: rows keep[g][0..budget) of the [Hkv][hs / d][d] K and V caches move to
+// rows 0..budget-1 (keep strictly ascending inside [0, n_valid), checked on the
+// device; a head whose list fails is left untouched and LATCH_RANGE goes to
+// latch word 1).
+hipError_t launch_compact_inplace(void* ctx, u16* k, u16* v, int Hkv, int64_t hs, int d,
+                                  int64_t n_valid, const int32_t* keep, int64_t budget,
+                                  uint32_t* latch, hipStream_t s);
 hipError_t launch_compact(void* ctx, const u16* k, const u16* v, int Hkv, int64_t n, int d,
                           const int32_t* keep, int64_t budget, u16* k_out, u16* v_out,
                           uint32_t* latch, hipStream_t s);

@@ -378,8 +378,8 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
   const int64_t jend = sp.jend;
   const int ntiles = sp.ntiles;
   const int d = FULLD ? DP : a.d;   // a compile-time constant in the full-width instance
-  const u16* kg = a.k + (size_t)g * a.n * d;
-  const u16* vg = a.v + (size_t)g * a.n * d;
+  const u16* kg = a.k + (size_t)g * a.hs;
+  const u16* vg = a.v + (size_t)g * a.hs;
   const bool row_ok = row0 + r < a.M;
   const int64_t causal = row_ok ? a.n - a.w + ((row0 + r) % a.w) : -1;
   const int64_t all_see = a.n - a.w;   // every window query sees keys 0..n-w
@@ -720,7 +720,7 @@ __device__ void exclusion_combine(const ScoreArgs& a, int hv, const int* rows, c
   const float* pbase = a.ex.part + (size_t)hv * a.xh * kRows * DP;   // helper h, row r: (h * 32 + r) * DP
   const float* sxb = a.ex.sx + (size_t)hv * a.xh * kRows;
   float* aresb = a.rs.ares + (size_t)hv * kRows * DP;
-  const u16* vb = a.v + (size_t)g * a.n * a.d;
+  const u16* vb = a.v + (size_t)g * a.hs;
   // the rows' scalars (threads below nl) in the same round trip as the first pairs
   float4 m = make_float4(0.f, 0.f, 0.f, 0.f);
   float sxp[kMaxHelpers];
@@ -947,8 +947,8 @@ __device__ void merge_helper(const ScoreArgs& a, int hv, int h, MergeHelpLds<DP>
   unsigned char* qs = L.buf;
   qst.store(qs);
   unsigned char* vs0 = L.buf + (size_t)kRows * RL::ROWB * (1 + TB * wid);   // this wave's V slots
-  const u16* kg = a.k + (size_t)g * a.n * a.d;
-  const u16* vg = a.v + (size_t)g * a.n * a.d;
+  const u16* kg = a.k + (size_t)g * a.hs;
+  const u16* vg = a.v + (size_t)g * a.hs;
   __syncthreads();
   for (int li = 0; li < L.nlist; ++li) {
     const int s0 = __builtin_amdgcn_readfirstlane(L.list[li]);
@@ -1254,7 +1254,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? 2 : 1)) void merge_kernel(Sc
   // decided exactly as the helpers decide it
   const bool fix = sstar >= 0 && jst >= 0 && s_flag != 0;
   // the arg-max token's value row, needed at the end
-  const float vstar = (tid < a.d && jst >= 0) ? bf2f(a.v[((size_t)g * a.n + jst) * a.d + tid]) : 0.f;
+  const float vstar = (tid < a.d && jst >= 0) ? bf2f(a.v[(size_t)g * a.hs + (size_t)jst * a.d + tid]) : 0.f;
 
   // split weights f_s = 2^(m2_s - M) and the normaliser with and without the
   // arg-max split (fixed-order sums)
@@ -1462,8 +1462,8 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
   const int64_t e0 = max((int64_t)0, c0 - rad), e1 = min(n, c1 + rad);
   const int next = (int)((e1 - e0 + kTile - 1) / kTile);
   const int d = FULLD ? DP : a.d;   // a compile-time constant in the full-width instance
-  const u16* kg = a.k + (size_t)g * n * d;
-  const u16* vg = a.v + (size_t)g * n * d;
+  const u16* kg = a.k + (size_t)g * a.hs;
+  const u16* vg = a.v + (size_t)g * a.hs;
   const int64_t all_see = n - a.w;
 
   for (int rg = 0; rg < R; ++rg) {
@@ -1707,7 +1707,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kAttnWaves : 2)) void attn_p
   const int64_t jend = sp.jend;
   const int ntiles = sp.ntiles;
   const int d = FULLD ? DP : a.d;   // a compile-time constant in the full-width instance
-  const u16* kg = a.k + (size_t)g * a.n * d;
+  const u16* kg = a.k + (size_t)g * a.hs;
   const bool row_ok = row0 + r < a.M;
   const int64_t causal = row_ok ? a.n - a.w + ((row0 + r) % a.w) : -1;
   const int64_t all_see = a.n - a.w;
@@ -1815,7 +1815,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kAttnWaves : 2)) void attn_p
   const int64_t e0 = max((int64_t)0, c0 - rad), e1 = min(n, c1 + rad);
   const int next = (int)((e1 - e0 + kTile - 1) / kTile);
   const int d = FULLD ? DP : a.d;   // a compile-time constant in the full-width instance
-  const u16* kg = a.k + (size_t)g * n * d;
+  const u16* kg = a.k + (size_t)g * a.hs;
   const int64_t all_see = n - a.w;
 
   for (int rg = 0; rg < R; ++rg)

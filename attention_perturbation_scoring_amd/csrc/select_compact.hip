@@ -84,8 +84,11 @@ struct SelArgs {
                             // workgroup finishes its share alone (< 0: at once)
 };
 
+// Word 0 of the latch holds the errors of scoring, selection and packing; word 1
+// those found by the in-place compaction's own checks (kept apart so that one
+// head's failed check does not stop the moves of the call's other heads).
 __device__ __forceinline__ bool latched(const uint32_t* latch) {
-  return __atomic_load_n(latch, __ATOMIC_RELAXED) != 0u;
+  return (__atomic_load_n(latch, __ATOMIC_RELAXED) | __atomic_load_n(latch + 1, __ATOMIC_RELAXED)) != 0u;
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_s1(SelArgs a) {
@@ -996,6 +999,128 @@ __global__ __launch_bounds__(256) void compact_kernel(const u16* __restrict__ k,
   if (bad) atomicOr(latch, LATCH_RANGE);
 }
 
+// ------------------------------------------------------- in-place compaction --
+// Rows keep[g][0..budget) of a resident cache [Hkv][cap][d] move to rows
+// 0..budget-1 of the same buffer.  keep is strictly ascending, so keep[j] >= j:
+// every row moves toward the front or stays.  A plain parallel gather would
+// race (row i may be written while another row still has to read it), so a
+// workgroup owns one 16-byte column chunk of K or of V of one KV head, for all
+// its rows, and walks the destinations in order, kIpRows at a time: every load
+// of a batch completes before any of its stores issues (wait for the loads,
+// then a barrier across the waves), and a later batch reads only rows at or
+// past its own destinations, which lie past every row an earlier batch writes.
+// Workgroups touch disjoint bytes, so no order between them is needed and none
+// waits for another.  The eight chunks of one 128-byte line of a row go to
+// workgroups whose indices agree modulo 8 -- the same XCD under the hardware's
+// round-robin placement -- so that XCD's L2 serves all eight from one fetch of
+// the line.  Before moving anything each workgroup checks its head's whole keep
+// list (strictly ascending, inside [0, n_valid)); the workgroups of a head read
+// the same list, so either all of them move or none does.
+constexpr int kIpThreads = 1024;
+constexpr int kIpU = 2;                          // rows per thread per batch
+constexpr int kIpB = kIpThreads * kIpU;          // rows per batch
+constexpr int kIpRows = 8192;                    // keep entries staged in LDS at a time
+static_assert(kIpRows % kIpB == 0, "whole batches per staged block");
+
+template <int N>
+__device__ __forceinline__ void ip_wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__global__ __launch_bounds__(kIpThreads) void compact_inplace_kernel(u16* k, u16* v, int64_t hs, int d,
+                                                                    int64_t n_valid,
+                                                                    const int32_t* __restrict__ keep,
+                                                                    int64_t budget, int Hkv,
+                                                                    int nlines, int units8,
+                                                                    uint32_t* latch) {
+  __shared__ int32_t idx[kIpRows];
+  const int tid = threadIdx.x;
+  // blockIdx = sub * units8 + unit: unit = (head, K or V, 128-byte line), sub =
+  // the 16-byte chunk within the line
+  const int unit = blockIdx.x % units8, sub = blockIdx.x / units8;
+  const int line = unit % nlines, kv = (unit / nlines) & 1, g = unit / (2 * nlines);
+  const int col = 64 * line + 8 * sub;   // first of the 8 columns this workgroup moves
+  if (g >= Hkv || col >= d) return;   // padding workgroups (whole workgroup: g and col are uniform)
+  // an error latched by scoring or selection withholds the keep list: move
+  // nothing (decided for the whole workgroup at once)
+  if (__syncthreads_or(__atomic_load_n(latch, __ATOMIC_RELAXED) != 0u)) return;
+  const int32_t* kp = keep + (size_t)g * budget;
+  u16* base = (kv ? v : k) + (size_t)g * hs + col;
+  // loads of one batch (rows b0 .. b0 + kIpB of the staged block).  Every lane
+  // loads (past the block's end, row 0), so each call issues exactly kIpU load
+  // instructions per wave -- the counter waits below rely on that count -- and
+  // indices are clamped into [0, n_valid), so even an unchecked list reads in
+  // bounds.
+  auto load = [&](int b0, int ni, u32x4 (&x)[kIpU]) {
+#pragma unroll
+    for (int u = 0; u < kIpU; ++u) {
+      const int i = b0 + u * kIpThreads + tid;
+      int64_t j = i < ni ? (int64_t)idx[i] : 0;
+      j = j < 0 ? 0 : (j >= n_valid ? n_valid - 1 : j);
+      x[u] = *reinterpret_cast<const u32x4*>(base + (size_t)j * d);
+    }
+  };
+  auto store = [&](int64_t i0, int b0, int ni, const u32x4 (&x)[kIpU]) {
+#pragma unroll
+    for (int u = 0; u < kIpU; ++u) {
+      const int i = b0 + u * kIpThreads + tid;
+      const int64_t dst = i0 + i;
+      if (i < ni && (int64_t)idx[i] != dst)   // a row already in place is not rewritten
+        *reinterpret_cast<u32x4*>(base + (size_t)dst * d) = x[u];
+    }
+  };
+  // The whole list is checked before any row moves.  A list that fits one
+  // staged block is checked in LDS while the first batch's loads fly (loads
+  // only read; the check gates the stores); a longer one first in memory.
+  const bool one_block = budget <= kIpRows;
+  int bad = 0;
+  if (!one_block) {
+    for (int64_t j = tid; j < budget; j += kIpThreads) {
+      const int32_t x = kp[j], prev = j > 0 ? kp[j - 1] : -1;
+      if (x < 0 || (int64_t)x >= n_valid || x <= prev) bad = 1;
+    }
+    if (__syncthreads_or(bad)) {
+      if (tid == 0) atomicOr(latch + 1, (uint32_t)LATCH_RANGE);
+      return;
+    }
+  }
+  for (int64_t i0 = 0; i0 < budget; i0 += kIpRows) {
+    const int ni = (int)min((int64_t)kIpRows, budget - i0);
+    __syncthreads();   // the previous block of entries is no longer read
+    for (int i = tid; i < ni; i += kIpThreads) idx[i] = kp[i0 + i];
+    __syncthreads();
+    const int nb = (ni + kIpB - 1) / kIpB;
+    u32x4 xa[kIpU], xb[kIpU];
+    load(0, ni, xa);
+    if (one_block) {
+      for (int i = tid; i < ni; i += kIpThreads) {
+        const int32_t x = idx[i], prev = i > 0 ? idx[i - 1] : -1;
+        if (x < 0 || (int64_t)x >= n_valid || x <= prev) bad = 1;
+      }
+      if (__syncthreads_or(bad)) {
+        if (tid == 0) atomicOr(latch + 1, (uint32_t)LATCH_RANGE);
+        return;
+      }
+    }
+    // batch b's stores issue once every wave's loads of batches <= b are done
+    // (vmcnt(kIpU) right after batch b+1's kIpU loads: everything older --
+    // batch b's loads, earlier stores -- has completed; then the barrier);
+    // batch b+1's loads are issued before those stores (they read rows past
+    // every row batch b writes), so the two overlap
+    for (int b = 0; b < nb; b += 2) {
+      if (b + 1 < nb) { load((b + 1) * kIpB, ni, xb); ip_wait_vmem<kIpU>(); }
+      else ip_wait_vmem<0>();
+      __syncthreads();
+      store(i0, b * kIpB, ni, xa);
+      if (b + 1 >= nb) break;
+      if (b + 2 < nb) { load((b + 2) * kIpB, ni, xa); ip_wait_vmem<kIpU>(); }
+      else ip_wait_vmem<0>();
+      __syncthreads();
+      store(i0, (b + 1) * kIpB, ni, xb);
+    }
+  }
+}
+
 // Workgroups of select_fused that can be resident at once on the current device
 // (0 if the device cannot launch cooperatively).
 static int64_t fused_capacity() {
@@ -1114,6 +1239,20 @@ hipError_t launch_layer_counts(void* ctx, const int32_t* keep, int64_t budget, i
   hipLaunchKernelGGL(layer_counts_kernel, dim3((unsigned)((Hkv + 3) / 4)), dim3(256), 0, s,
                      keep, budget, n, Hkv, counts, (const uint32_t*)latch);
   prof_end(ctx, "select", s);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact_inplace(void* ctx, u16* k, u16* v, int Hkv, int64_t hs, int d,
+                                  int64_t n_valid, const int32_t* keep, int64_t budget,
+                                  uint32_t* latch, hipStream_t s) {
+  if (budget == 0) return hipSuccess;
+  const int nlines = (d + 63) / 64;                 // 128-byte lines of a row
+  const int64_t units = (int64_t)Hkv * 2 * nlines;  // (head, K or V, line)
+  const int64_t units8 = (units + 7) / 8 * 8;
+  prof_begin(ctx, "compact_inplace", s);
+  hipLaunchKernelGGL(compact_inplace_kernel, dim3((unsigned)(8 * units8)), dim3(kIpThreads), 0, s, k,
+                     v, hs, d, n_valid, keep, budget, Hkv, nlines, (int)units8, latch);
+  prof_end(ctx, "compact_inplace", s);
   return hipGetLastError();
 }
 

@@ -17,8 +17,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdropkv.so")
 
 OK, EINVAL, ESINGULAR, ENONFINITE, ERANGE, EDEVICE, ENOMEM, ESCRATCH = range(8)
-KERNELS = ("pass1", "merge", "pass2", "select", "compact", "attn_pass1", "attn_pass2",
-           "stream_read")
+KERNELS = ("pass1", "merge", "pass2", "select", "compact", "compact_inplace", "attn_pass1",
+           "attn_pass2", "stream_read")
 
 
 class DropKVError(RuntimeError):
@@ -49,6 +49,8 @@ def lib():
             "dropkv_select": [P, P, i32, i64, i64, P, P],
             "dropkv_select_layer": [P, P, i32, i64, i64, P, P, P],
             "dropkv_compact": [P, P, P, i32, i64, i32, P, i64, P, P, P],
+            "dropkv_compact_inplace": [P, P, P, i32, i64, i64, i32, P, i64, P],
+            "dropkv_rescore": [P, P, P, P, i64, i64, i32, i32, i32, i32, i32, i64, P, P, P],
             "dropkv_sync": [P, P],
             "dropkv_set_select_wait": [P, i64],
             "dropkv_profile_enable": [P, ctypes.c_int],
@@ -179,6 +181,17 @@ class Context:
         _check(lib().dropkv_compact(self._h, _ptr(k), _ptr(v), Hkv, n, d, _ptr(keep), budget,
                                     _ptr(k_out), _ptr(v_out), _stream(stream)), "dropkv_compact")
 
+    def compact_inplace(self, k_cache, v_cache, Hkv, cap, n_valid, d, keep, budget, stream=None):
+        _check(lib().dropkv_compact_inplace(self._h, _ptr(k_cache), _ptr(v_cache), Hkv, cap, n_valid,
+                                            d, _ptr(keep), budget, _stream(stream)),
+               "dropkv_compact_inplace")
+
+    def rescore(self, q_win, k_cache, v_cache, cap, n_valid, w, Hq, Hkv, d, pool, budget, scores,
+                keep, stream=None):
+        _check(lib().dropkv_rescore(self._h, _ptr(q_win), _ptr(k_cache), _ptr(v_cache), cap, n_valid,
+                                    w, Hq, Hkv, d, pool, budget, _ptr(scores), _ptr(keep),
+                                    _stream(stream)), "dropkv_rescore")
+
     def stream_read(self, buf, nbytes=None, stream=None):
         """Read a device buffer once (the achievable-bandwidth reference)."""
         nbytes = buf.numel() * buf.element_size() if nbytes is None else nbytes
@@ -233,6 +246,14 @@ def dropkv_select_layer(ctx: Context, *args, **kw):
 
 def dropkv_compact(ctx: Context, *args, **kw):
     return ctx.compact(*args, **kw)
+
+
+def dropkv_compact_inplace(ctx: Context, *args, **kw):
+    return ctx.compact_inplace(*args, **kw)
+
+
+def dropkv_rescore(ctx: Context, *args, **kw):
+    return ctx.rescore(*args, **kw)
 
 
 def dropkv_stream_read(ctx: Context, *args, **kw):

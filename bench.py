@@ -193,6 +193,73 @@ def time_sink_heavy(ctx, cfg, dev, scores, keep, stream, steps):
             "kernel_us": us, "score_select_us": round(sum(us.values()), 2)}
 
 
+def time_decode(ctx, cfg, q0, k0, v0, stream, steps, m=1024):
+    """Decode-time pieces at the workload's shapes, on clones of the layer:
+    (1) dropkv_compact_inplace of the whole prefill cache (capacity n) to the
+    budget, with the prefill's own keep list; (2) dropkv_rescore of a resident
+    cache whose first `budget` rows are survivors and whose next m rows stand
+    for the decode tokens appended since: n_valid = budget + m rows are scored,
+    `budget` of them kept, and the cache compacted in place."""
+    import torch
+    from attention_perturbation_scoring_amd import dropkv
+    Hq, Hkv, d, n, w, pool, budget = cfg.Hq, cfg.Hkv, cfg.d, cfg.n, cfg.w, cfg.pool, cfg.budget
+    if budget + m > n:
+        return None
+    k, v = k0.clone(), v0.clone()
+    scores = torch.empty((Hkv, n), dtype=torch.float32, device="cuda")
+    keep = torch.empty((Hkv, budget), dtype=torch.int32, device="cuda")
+    ctx.score(q0, k, v, n, w, Hq, Hkv, d, pool, scores, stream)
+    ctx.select(scores, Hkv, n, budget, keep, stream)
+    ctx.check(stream)
+
+    def kernel_avgs(names):
+        out = {}
+        for name in names:
+            tot, cnt = ctx.profile_read(name)
+            if cnt:
+                out[name] = round(1e3 * tot / cnt, 2)
+        return out
+
+    # (1) the same ascending list applied again each time: the same moves, over
+    # whatever the rows then hold
+    ctx.compact_inplace(k, v, Hkv, n, n, d, keep, budget, stream)
+    ctx.profile(True)
+    ctx.profile_reset()
+    for _ in range(steps):
+        ctx.compact_inplace(k, v, Hkv, n, n, d, keep, budget, stream)
+    torch.cuda.synchronize()
+    inplace = kernel_avgs(["compact_inplace"])
+    ctx.profile(False)
+    ctx.check(stream)
+    # (2) rescoring budget + m resident rows
+    n_valid = budget + m
+    sc2 = torch.empty((Hkv, n_valid), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        ctx.rescore(q0, k, v, n, n_valid, w, Hq, Hkv, d, pool, budget, sc2, keep, stream)
+    ctx.check(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ctx.rescore(q0, k, v, n, n_valid, w, Hq, Hkv, d, pool, budget, sc2, keep, stream)
+    torch.cuda.synchronize()
+    call_us = (time.perf_counter() - t0) * 1e6 / steps
+    ctx.profile(True)
+    ctx.profile_reset()
+    for _ in range(steps):
+        ctx.rescore(q0, k, v, n, n_valid, w, Hq, Hkv, d, pool, budget, sc2, keep, stream)
+    torch.cuda.synchronize()
+    rk = kernel_avgs(["pass1", "merge", "pass2", "select", "compact_inplace"])
+    ctx.profile(False)
+    ctx.check(stream)
+    del k, v
+    return {"compact_inplace_full_us": inplace.get("compact_inplace"),
+            "compact_inplace_what": f"{Hkv} heads x {budget} kept rows of a {n}-row cache, in place",
+            "rescore": {"cap": n, "n_valid": n_valid, "m": m, "budget": budget,
+                        "what": "dropkv_rescore: score the n_valid resident rows (window = last w), "
+                                "keep budget, compact in place",
+                        "call_us": call_us, "kernel_us": rk}}
+
+
 def scratch_report(n, w, Hq, Hkv, d):
     """Device scratch the library holds for one call of these sizes, beside the
     pages' figures for the same question (n = 128K: ~17 MB for the fused Triton
@@ -405,6 +472,12 @@ def run(args):
         log("[bench] sink-heavy variant")
         sink_heavy = time_sink_heavy(ctx, cfg, dev, scores, keep, stream, max(3, min(args.steps, 10)))
 
+    # ---- decode-time rescoring and in-place compaction ----
+    decode = None
+    if L == 1:
+        log("[bench] decode-time rescoring")
+        decode = time_decode(ctx, cfg, *copies[0], stream, max(3, min(args.steps, 20)))
+
     # ---- per-call distribution with the caches flushed before every call ----
     # Streaming 1 GiB through the caches evicts the 4 MB L2s and the 256 MB
     # last-level cache, so each call starts cold.  A read flush leaves clean
@@ -505,6 +578,7 @@ def run(args):
         "layer_select_us": layer_select_us,
         "peaked_rows": peaked_rows,
         "sink_heavy": sink_heavy,
+        "decode": decode,
         "kernel_source_hash": kernel_source_hash(),
         "scratch_bytes": scratch_report(n, w, Hq, Hkv, d),
     }

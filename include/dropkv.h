@@ -56,7 +56,8 @@ enum {
     DROPKV_EINVAL = 1,     /* bad argument, found on the host before any launch */
     DROPKV_ESINGULAR = 2,  /* some window query puts probability that rounds to 1 on one key */
     DROPKV_ENONFINITE = 3, /* a non-finite input element */
-    DROPKV_ERANGE = 4,     /* a score beyond FLT_MAX, or a keep index outside [0, n) */
+    DROPKV_ERANGE = 4,     /* a score beyond FLT_MAX, a keep index outside [0, n), or an
+                              in-place keep list that is not strictly ascending */
     DROPKV_EDEVICE = 5,    /* a HIP runtime error */
     DROPKV_ENOMEM = 6,     /* scratch allocation failed */
     DROPKV_ESCRATCH = 7    /* dropkv_score_noalloc: the call needs more scratch than its
@@ -206,6 +207,49 @@ int dropkv_select_layer(dropkv_ctx *ctx, const float *scores, int32_t Hkv, int64
 int dropkv_compact(dropkv_ctx *ctx, const uint16_t *k, const uint16_t *v, int32_t Hkv, int64_t n,
                    int32_t d, const int32_t *keep, int64_t budget, uint16_t *k_out,
                    uint16_t *v_out, void *stream);
+
+/*
+ * Compact a resident cache in place (exact bit copies): for every KV head g and
+ * r < budget, row r of k_cache and v_cache [Hkv][cap][d] bf16 becomes old row
+ * keep[g][r].  keep [Hkv][budget] int32 must be strictly ascending inside
+ * [0, n_valid) -- dropkv_select's output is -- so no row is overwritten before
+ * it has been read.  Rows budget .. n_valid-1 are unspecified afterwards; rows
+ * n_valid .. cap-1 and other memory are untouched.  The caller owns both
+ * buffers; the call allocates nothing.
+ * EINVAL if: a pointer is NULL or misaligned; Hkv < 1; cap < 1 or cap >= 2^31;
+ *   n_valid < 1 or n_valid > cap; d not a multiple of 8 in [8, 256]; budget < 0
+ *   or budget > n_valid.
+ * Latched: ERANGE if some head's keep list is not strictly ascending inside
+ *   [0, n_valid) (that head's rows stay where they are; other heads move).  While
+ *   an error of scoring or selection is latched, nothing moves.
+ */
+int dropkv_compact_inplace(dropkv_ctx *ctx, uint16_t *k_cache, uint16_t *v_cache, int32_t Hkv,
+                           int64_t cap, int64_t n_valid, int32_t d, const int32_t *keep,
+                           int64_t budget, void *stream);
+
+/*
+ * Decode-time rescoring of a resident cache.  "paper digest" §6 (Discussion
+ * and Limitation) leaves a decode-time kernel as future work and §5.4 runs
+ * decoding on the evicted cache; the plainest reading, taken here: after m
+ * decode steps the cache [Hkv][cap][d] holds n_valid <= cap rows per KV head
+ * (the tokens kept so far, in their order, then the m appended tokens), and
+ * q_win [Hq][w][d] holds the queries of its last w positions.  One call
+ *   1. scores those rows exactly as dropkv_score scores a prefill cache of
+ *      n = n_valid tokens (the window is rows n_valid - w .. n_valid - 1,
+ *      protected with +inf): scores [Hkv][n_valid] fp32 (out);
+ *   2. keeps `budget` rows per head by dropkv_select's rule: keep
+ *      [Hkv][budget] int32 (out), ascending old row indices;
+ *   3. compacts the cache in place as dropkv_compact_inplace does.
+ * Afterwards each head holds `budget` valid rows (set n_valid = budget and
+ * append further decode tokens after them).  budget == 0 scores only.
+ * EINVAL as for dropkv_score with n = n_valid (k/v rows are cap apart per
+ * head), plus cap < 1 or cap >= 2^31, n_valid > cap, budget < 0 or budget >
+ * n_valid.  Latched errors as for dropkv_score and dropkv_select; while one is
+ * latched the cache is not moved.  Scratch as for dropkv_score.
+ */
+int dropkv_rescore(dropkv_ctx *ctx, const uint16_t *q_win, uint16_t *k_cache, uint16_t *v_cache,
+                   int64_t cap, int64_t n_valid, int32_t w, int32_t Hq, int32_t Hkv, int32_t d,
+                   int32_t pool, int64_t budget, float *scores, int32_t *keep, void *stream);
 
 /* Wait for `stream`, then return and clear the latched device condition
  * (ENONFINITE before ESINGULAR before ERANGE), or DROPKV_OK; EDEVICE if the

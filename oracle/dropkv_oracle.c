@@ -321,6 +321,63 @@ int oracle_compact(const uint16_t *in, int hkv, int64_t n, int d, const int32_t 
 }
 
 /*
+ * In-place compaction of a resident cache [hkv][cap][d] (Section 2.2: eviction
+ * removes tokens from the resident cache).  For every head, row r becomes old
+ * row keep[g][r], r = 0 .. budget-1, copied one row at a time in ascending r.
+ * The list must be strictly ascending inside [0, n_valid): then keep[r] >= r,
+ * so every source row is read before a later copy can overwrite it.  All lists
+ * are checked first; an invalid one returns ORC_ERANGE with nothing moved.
+ */
+int oracle_compact_inplace(uint16_t *cache, int hkv, int64_t cap, int64_t n_valid, int d,
+                           const int32_t *keep, int64_t budget) {
+    if (hkv < 1 || cap < 1 || n_valid < 1 || n_valid > cap || d < 1 || budget < 0 ||
+        budget > n_valid)
+        return ORC_EINVAL;
+    for (int g = 0; g < hkv; ++g)
+        for (int64_t r = 0; r < budget; ++r) {
+            const int64_t j = keep[(size_t)g * budget + r];
+            const int64_t prev = r > 0 ? keep[(size_t)g * budget + r - 1] : -1;
+            if (j < 0 || j >= n_valid || j <= prev) return ORC_ERANGE;
+        }
+    for (int g = 0; g < hkv; ++g) {
+        uint16_t *base = cache + (size_t)g * cap * d;
+        for (int64_t r = 0; r < budget; ++r) {
+            const int64_t j = keep[(size_t)g * budget + r];
+            if (j != r) memcpy(base + (size_t)r * d, base + (size_t)j * d, sizeof(uint16_t) * (size_t)d);
+        }
+    }
+    return ORC_OK;
+}
+
+/*
+ * Decode-time rescoring of a resident cache ("paper digest" §6 leaves a
+ * decode-time kernel as future work; reading: the n_valid resident rows of
+ * every head, kept tokens then appended decode tokens, are scored exactly as a
+ * prefill cache of n_valid tokens whose window is the last w rows).  k and v are
+ * [hkv][cap][d] with rows n_valid .. cap-1 ignored; the resident rows are
+ * gathered into [hkv][n_valid][d] and scored by oracle_score.
+ */
+int oracle_rescore(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t cap,
+                   int64_t n_valid, int w, int hq, int hkv, int d, int pool, int nthreads,
+                   double *scores) {
+    if (cap < 1 || n_valid < 1 || n_valid > cap || hkv < 1 || d < 1) return ORC_EINVAL;
+    uint16_t *kr = malloc(sizeof(uint16_t) * (size_t)hkv * n_valid * d);
+    uint16_t *vr = malloc(sizeof(uint16_t) * (size_t)hkv * n_valid * d);
+    int rc = (kr && vr) ? ORC_OK : ORC_ENOMEM;
+    if (rc == ORC_OK) {
+        for (int g = 0; g < hkv; ++g) {
+            memcpy(kr + (size_t)g * n_valid * d, k + (size_t)g * cap * d,
+                   sizeof(uint16_t) * (size_t)n_valid * d);
+            memcpy(vr + (size_t)g * n_valid * d, v + (size_t)g * cap * d,
+                   sizeof(uint16_t) * (size_t)n_valid * d);
+        }
+        rc = oracle_score(q, kr, vr, n_valid, w, hq, hkv, d, pool, nthreads, scores);
+    }
+    free(kr); free(vr);
+    return rc;
+}
+
+/*
  * Log-sum-exp of every window query's logits over the keys it sees (natural
  * log): lse[h][t] = log sum_{j <= n-w+t} exp(q.k_j / sqrt(d)).  With the output a
  * of oracle_window_attention, this is what pass 1 can hand back to the caller

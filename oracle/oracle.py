@@ -58,8 +58,11 @@ def load(path: str):
     L.oracle_window_lse.argtypes = [P, P, i64, i32, i32, i32, i32, P]
     L.oracle_select_layer.argtypes = [P, i32, i64, i64, P, P]
     L.oracle_attention_score.argtypes = [P, P, i64, i32, i32, i32, i32, i32, i32, P]
+    L.oracle_compact_inplace.argtypes = [P, i32, i64, i64, i32, P, i64]
+    L.oracle_rescore.argtypes = [P, P, P, i64, i64, i32, i32, i32, i32, i32, i32, P]
     for f in (L.oracle_raw_scores, L.oracle_pool_protect, L.oracle_score, L.oracle_select,
-              L.oracle_compact, L.oracle_window_attention):
+              L.oracle_compact, L.oracle_window_attention, L.oracle_compact_inplace,
+              L.oracle_rescore):
         f.restype = ctypes.c_int
     return L
 
@@ -172,6 +175,29 @@ def compact(x, keep):
     budget = keep.shape[1]
     out = np.zeros((Hkv, budget, d), dtype=np.uint16)
     _check(lib().oracle_compact(_ptr(x), Hkv, n, d, _ptr(keep), budget, _ptr(out)))
+    return out
+
+
+def compact_inplace(cache, keep, n_valid):
+    """In-place compaction of a resident cache [Hkv][cap][d] (uint16, modified
+    in place and returned): row r of head g becomes old row keep[g][r]."""
+    assert cache.dtype == np.uint16 and cache.flags.c_contiguous
+    keep = np.ascontiguousarray(keep, dtype=np.int32)
+    Hkv, cap, d = cache.shape
+    budget = keep.shape[1]
+    _check(lib().oracle_compact_inplace(_ptr(cache), Hkv, cap, n_valid, d, _ptr(keep), budget))
+    return cache
+
+
+def rescore(q, k, v, n_valid, pool, nthreads=None):
+    """Scores [Hkv][n_valid] (float64) of the first n_valid rows of resident
+    caches k, v [Hkv][cap][d]; the window is the last w of those rows."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    Hq, w, d = q.shape
+    Hkv, cap, _ = k.shape
+    out = np.zeros((Hkv, n_valid), dtype=np.float64)
+    _check(lib().oracle_rescore(_ptr(q), _ptr(k), _ptr(v), cap, n_valid, w, Hq, Hkv, d, pool,
+                                nthreads or default_threads(), _ptr(out)))
     return out
 
 

@@ -1,0 +1,171 @@
+"""Decode-time rescoring and in-place compaction through the C ABI, against the
+float64 oracle (oracle_rescore, oracle_compact_inplace) on the same bf16 bytes.
+
+Scores: |gpu - oracle| <= 2e-3 |oracle| + FLT_MIN; keep sets equal outside the
+2e-3 band around the k-th smallest score; moved rows bit-exact; rows past
+n_valid and the sentinel pads around every buffer untouched."""
+import numpy as np
+import pytest
+import torch
+
+from attention_perturbation_scoring_amd import dropkv, workload as wl
+from oracle import oracle as orc
+import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+NAN_BF16 = 0x7FC1   # rows past n_valid: never read by a correct kernel
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    c = dropkv.Context(0)
+    yield c
+    c.close()
+
+
+def _guarded_cache(arr):
+    g = H.Guarded(arr.shape, torch.int16)
+    g.t.copy_(torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)))
+    return g
+
+
+def _ascending(rng, n_valid, budget, prefix=0):
+    rest = rng.choice(np.arange(prefix, n_valid), budget - prefix, replace=False)
+    return np.concatenate([np.arange(prefix), np.sort(rest)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("Hkv,cap,n_valid,d,budget,prefix", [
+    (1, 40, 33, 8, 10, 0),           # one slice, partial
+    (2, 3000, 2900, 96, 1500, 4),    # 192-byte rows: a full and a half slice
+    (3, 5000, 5000, 128, 4999, 0),   # nearly every row stays (long identity runs)
+    (8, 20000, 19000, 128, 9500, 4), # several batches and two blocks of staged entries
+    (1, 1200, 1100, 256, 700, 0),    # four slices
+    (4, 700, 650, 40, 300, 2),       # 80-byte rows
+])
+def test_compact_inplace_matches_oracle(ctx, Hkv, cap, n_valid, d, budget, prefix):
+    print(f"[case] inplace Hkv={Hkv} cap={cap} n_valid={n_valid} d={d} budget={budget}", flush=True)
+    rng = np.random.default_rng(cap + d)
+    k = wl.bf16_bits(rng.standard_normal((Hkv, cap, d), dtype=np.float32))
+    v = wl.bf16_bits(rng.standard_normal((Hkv, cap, d), dtype=np.float32))
+    k[:, n_valid:] = NAN_BF16
+    v[:, n_valid:] = NAN_BF16
+    keep = np.stack([_ascending(rng, n_valid, budget, prefix) for _ in range(Hkv)])
+    kg, vg = _guarded_cache(k), _guarded_cache(v)
+    keep_d = torch.from_numpy(keep).cuda()
+    ctx.compact_inplace(kg.t, vg.t, Hkv, cap, n_valid, d, keep_d, budget)
+    assert ctx.sync() == dropkv.OK
+    kg.check("k_cache"); vg.check("v_cache")
+    ko = kg.t.cpu().numpy().view(np.uint16)
+    vo = vg.t.cpu().numpy().view(np.uint16)
+    kw, vw = orc.compact_inplace(k.copy(), keep, n_valid), orc.compact_inplace(v.copy(), keep, n_valid)
+    np.testing.assert_array_equal(ko[:, :budget], kw[:, :budget])
+    np.testing.assert_array_equal(vo[:, :budget], vw[:, :budget])
+    np.testing.assert_array_equal(ko[:, n_valid:], k[:, n_valid:])
+    np.testing.assert_array_equal(vo[:, n_valid:], v[:, n_valid:])
+
+
+def test_compact_inplace_invalid_list_leaves_that_head(ctx):
+    """Head 1's list repeats an entry: ERANGE, head 1 untouched, heads 0 and 2 moved."""
+    rng = np.random.default_rng(3)
+    Hkv, cap, n_valid, d, budget = 3, 600, 600, 64, 200
+    k = wl.bf16_bits(rng.standard_normal((Hkv, cap, d), dtype=np.float32))
+    v = wl.bf16_bits(rng.standard_normal((Hkv, cap, d), dtype=np.float32))
+    keep = np.stack([_ascending(rng, n_valid, budget) for _ in range(Hkv)])
+    keep[1, 50] = keep[1, 49]
+    kg, vg = _guarded_cache(k), _guarded_cache(v)
+    ctx.compact_inplace(kg.t, vg.t, Hkv, cap, n_valid, d, torch.from_numpy(keep).cuda(), budget)
+    assert ctx.sync() == dropkv.ERANGE
+    assert ctx.sync() == dropkv.OK   # cleared
+    ko = kg.t.cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(ko[1], k[1])
+    for g in (0, 2):
+        np.testing.assert_array_equal(ko[g, :budget], k[g][keep[g]])
+
+
+def test_compact_inplace_withheld_while_an_error_is_latched(ctx):
+    """A singular scoring call latches ESINGULAR; until it is read, nothing moves."""
+    q, kk, vv = (np.zeros((1, 1, 8), np.uint16), np.zeros((1, 1, 8), np.uint16),
+                 np.zeros((1, 1, 8), np.uint16))   # one visible key: p = 1
+    scores = torch.empty((1, 1), dtype=torch.float32, device="cuda")
+    ctx.score(H.to_dev(q), H.to_dev(kk), H.to_dev(vv), 1, 1, 1, 1, 8, 1, scores)
+    rng = np.random.default_rng(4)
+    k = wl.bf16_bits(rng.standard_normal((1, 100, 8), dtype=np.float32))
+    kg, vg = _guarded_cache(k), _guarded_cache(k.copy())
+    keep = torch.from_numpy(np.arange(50, 100, dtype=np.int32)[None]).cuda()
+    ctx.compact_inplace(kg.t, vg.t, 1, 100, 100, 8, keep, 50)
+    assert ctx.sync() == dropkv.ESINGULAR
+    np.testing.assert_array_equal(kg.t.cpu().numpy().view(np.uint16), k)
+
+
+def _rescore_check(ctx, q, k, v, cap, n_valid, pool, budget, where):
+    Hq, w, d = q.shape
+    Hkv = k.shape[0]
+    k = k.copy(); v = v.copy()
+    k[:, n_valid:] = NAN_BF16
+    v[:, n_valid:] = NAN_BF16
+    kg, vg = _guarded_cache(k), _guarded_cache(v)
+    sc = H.Guarded((Hkv, n_valid), torch.float32, -7.0)
+    kp = H.Guarded((Hkv, max(budget, 1)), torch.int32, -5)
+    print(f"[case] {where}", flush=True)
+    ctx.rescore(H.to_dev(q), kg.t, vg.t, cap, n_valid, w, Hq, Hkv, d, pool, budget, sc.t, kp.t)
+    st = ctx.sync()
+    torch.cuda.synchronize()
+    for name, g in (("k_cache", kg), ("v_cache", vg), ("scores", sc), ("keep", kp)):
+        g.check(name)
+    assert st == dropkv.OK, f"{where}: device status {st}"
+    want = orc.rescore(q, k, v, n_valid, pool)
+    s = sc.t.cpu().numpy()
+    H.assert_scores_close(s, want, where=where)
+    keep = kp.t.cpu().numpy()[:, :budget]
+    H.assert_keep_sets_match(keep, orc.select(want, budget), want, budget, where=where)
+    ko = kg.t.cpu().numpy().view(np.uint16)
+    vo = vg.t.cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(ko[:, :budget], orc.compact_inplace(k.copy(), keep, n_valid)[:, :budget])
+    np.testing.assert_array_equal(vo[:, :budget], orc.compact_inplace(v.copy(), keep, n_valid)[:, :budget])
+    np.testing.assert_array_equal(ko[:, n_valid:], k[:, n_valid:])
+    for g in range(Hkv):   # the window survives
+        assert set(range(n_valid - w, n_valid)) <= set(keep[g].tolist())
+    return ko, vo, keep
+
+
+@pytest.mark.parametrize("Hq,Hkv,d,cap,n_valid,w,pool,budget", [
+    (4, 2, 64, 400, 333, 4, 5, 100),
+    (32, 8, 128, 3000, 2600, 8, 7, 1300),
+    (28, 4, 128, 2100, 2048, 8, 7, 600),   # 56 window rows per KV head: two row groups
+    (8, 8, 96, 1500, 1499, 8, 7, 1000),
+])
+def test_rescore_matches_oracle(ctx, Hq, Hkv, d, cap, n_valid, w, pool, budget):
+    rng = np.random.default_rng(n_valid + d)
+    q = wl.bf16_bits(rng.standard_normal((Hq, w, d), dtype=np.float32))
+    k = wl.bf16_bits(rng.standard_normal((Hkv, cap, d), dtype=np.float32))
+    v = wl.bf16_bits(rng.standard_normal((Hkv, cap, d), dtype=np.float32))
+    _rescore_check(ctx, q, k, v, cap, n_valid, pool, budget,
+                   f"rescore Hq={Hq} Hkv={Hkv} d={d} cap={cap} n_valid={n_valid}")
+
+
+def test_decode_cycle_llama_shape(ctx):
+    """Prefill a Llama-shaped 4K layer, evict to 5 % on the GPU, append 512 decode
+    rows, rescore on the GPU; every step checked against the oracle."""
+    cfg = wl.CONFIGS["llama4k"]
+    inp = wl.make_layer(cfg, cfg.seed)
+    Hq, Hkv, d, w, pool, budget = cfg.Hq, cfg.Hkv, cfg.d, cfg.w, cfg.pool, cfg.budget
+    m = 512
+    cap = cfg.n
+    # the prefill cache doubles as the resident buffer (capacity n)
+    st, s0, keep0, _, _ = H.gpu_path(ctx, inp["q"], inp["k"], inp["v"], pool, budget, compact=False)
+    assert st == dropkv.OK
+    k = inp["k"].copy(); v = inp["v"].copy()
+    kg, vg = _guarded_cache(k), _guarded_cache(v)
+    ctx.compact_inplace(kg.t, vg.t, Hkv, cap, cfg.n, d, torch.from_numpy(keep0).cuda(), budget)
+    assert ctx.sync() == dropkv.OK
+    k1 = kg.t.cpu().numpy().view(np.uint16).copy()
+    v1 = vg.t.cpu().numpy().view(np.uint16).copy()
+    np.testing.assert_array_equal(k1[:, :budget], orc.compact(inp["k"], keep0))
+    rng = np.random.default_rng(99)
+    k1[:, budget:budget + m] = wl.bf16_bits(rng.standard_normal((Hkv, m, d), dtype=np.float32))
+    v1[:, budget:budget + m] = wl.bf16_bits(rng.standard_normal((Hkv, m, d), dtype=np.float32))
+    q1 = wl.bf16_bits(rng.standard_normal((Hq, w, d), dtype=np.float32))
+    _rescore_check(ctx, q1, k1, v1, cap, budget + m, pool, budget, "decode cycle llama4k, m=512")

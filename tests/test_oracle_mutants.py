@@ -31,6 +31,11 @@ MUTANTS = {
     "attn_causal_off_by_one": ("const int64_t Pt = n - w + t;", "const int64_t Pt = n - w + t - 1;"),
     "attn_no_sqrt_d": ("l[j] = inv_sqrt_d * s;", "l[j] = s;"),
     "attn_unnormalised": ("rg[j] += l[j] / S;", "rg[j] += l[j];"),
+    # decode-time pieces
+    "inplace_descending": ("for (int64_t r = 0; r < budget; ++r) {\n            const int64_t j = keep[(size_t)g * budget + r];\n            if (j != r)",
+                           "for (int64_t r = budget - 1; r >= 0; --r) {\n            const int64_t j = keep[(size_t)g * budget + r];\n            if (j != r)"),
+    "rescore_head_stride": ("memcpy(kr + (size_t)g * n_valid * d, k + (size_t)g * cap * d,",
+                            "memcpy(kr + (size_t)g * n_valid * d, k + (size_t)g * n_valid * d,"),
 }
 
 
@@ -62,6 +67,18 @@ def _pins_pass(L):
             return False
         qa = wl.bf16_bits(rng.standard_normal((4, 3, 8), dtype=np.float32) * 2)
         if not np.allclose(orc.attention_raw(qa, k), brute.attention_raw(qa, k), rtol=1e-12, atol=0):
+            return False
+        # in-place compaction with chains of moves, against fancy indexing
+        c = wl.bf16_bits(rng.standard_normal((2, 9, 8), dtype=np.float32))
+        kp = np.array([[1, 3, 4, 6], [0, 2, 5, 8]], dtype=np.int32)
+        want = np.stack([c[g][kp[g]] for g in range(2)])
+        if not np.array_equal(orc.compact_inplace(c.copy(), kp, 9)[:, :4], want):
+            return False
+        # rescoring a resident cache (finite garbage past n_valid) = scoring its valid rows
+        kc = wl.bf16_bits(rng.standard_normal((2, 23, 8), dtype=np.float32))
+        vc = wl.bf16_bits(rng.standard_normal((2, 23, 8), dtype=np.float32))
+        want = orc.score(q, np.ascontiguousarray(kc[:, :17]), np.ascontiguousarray(vc[:, :17]), 3)
+        if not np.array_equal(orc.rescore(q, kc, vc, 17, 3), want):
             return False
         return True
     except orc.OracleError:
