@@ -438,8 +438,9 @@ int dropkv_sync(dropkv_ctx* c, void* stream) {
     if (e != hipSuccess) return to_status(e);
   }
   if (bits & LATCH_NONFINITE) return DROPKV_ENONFINITE;
+  if (bits & LATCH_INPUT_RANGE) return DROPKV_ERANGE;
   if (bits & LATCH_SINGULAR) return DROPKV_ESINGULAR;
-  if (bits & LATCH_RANGE) return DROPKV_ERANGE;
+  if (bits & (LATCH_RANGE | LATCH_OVERFLOW)) return DROPKV_ERANGE;
   return DROPKV_OK;
 }
 

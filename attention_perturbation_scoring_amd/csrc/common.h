@@ -67,12 +67,21 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// Device error latch bits (OR-ed by kernels, decoded by dropkv_sync).
+// Device error latch bits (OR-ed by kernels, decoded by dropkv_sync in the
+// order NONFINITE, INPUT_RANGE, SINGULAR, then RANGE / OVERFLOW).
 enum : uint32_t {
-  LATCH_NONFINITE = 1u,
+  LATCH_NONFINITE = 1u,     // an input element is not finite (the first pass's scan)
   LATCH_SINGULAR = 2u,
-  LATCH_RANGE = 4u,
+  LATCH_RANGE = 4u,         // a keep index out of range, or a score beyond FLT_MAX
+  LATCH_INPUT_RANGE = 8u,   // an input element of magnitude >= 2^48 (the first pass's scan)
+  LATCH_OVERFLOW = 16u,     // an fp32 intermediate overflowed (only outside the input contract)
 };
+// Input contract: every Q, K and V element is finite and of magnitude below
+// 2^48, i.e. its bf16 bits with the sign cleared are below this.  Then no
+// logit (|q.k| <= d 2^96), no ||a||^2, ||v||^2, a.v or distance (<= 4 d 2^96)
+// and no score (odds^2 <= 1 off the arg-max, whose term is formed exactly)
+// comes near FLT_MAX.
+constexpr uint32_t kInputRangeBits = 0x5780u;   // 2^48 in bf16
 
 // Polls a workgroup of the single-launch selection makes at a team barrier
 // before it finishes its share alone (about 10-20 ms on MI355X).

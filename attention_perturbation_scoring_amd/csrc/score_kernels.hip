@@ -76,6 +76,28 @@ __device__ __forceinline__ int wave_or_i(int x) {
   return x;
 }
 
+// The input check: a running maximum of the magnitude bits (sign cleared) of
+// every bf16 element a workgroup loads, two elements per operation
+// (v_pk_max_u16); only the largest is needed to decide the contract.
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ us2 mag_max(us2 m, uint32_t x) {
+  return __builtin_elementwise_max(m, __builtin_bit_cast(us2, x & 0x7FFF7FFFu));
+}
+__device__ __forceinline__ us2 mag_max4(us2 m, u32x4 x) {
+  m = mag_max(m, x[0]);
+  m = mag_max(m, x[1]);
+  m = mag_max(m, x[2]);
+  return mag_max(m, x[3]);
+}
+// After the loads: NONFINITE if some element was inf or NaN, INPUT_RANGE if
+// one was of magnitude >= 2^48 (wave-reduced, one atomic per offending wave).
+__device__ __forceinline__ void latch_inputs(uint32_t* latch, us2 m) {
+  const uint32_t b = max((uint32_t)m.x, (uint32_t)m.y);
+  int f = b >= 0x7F80u ? (int)LATCH_NONFINITE : (b >= kInputRangeBits ? (int)LATCH_INPUT_RANGE : 0);
+  f = wave_or_i(f);
+  if (f && (threadIdx.x & 63) == 0) atomicOr(latch, (uint32_t)f);
+}
+
 // ---------------------------------------------------------------- pass 1 --
 // Lane layout of the 32x32x16 bf16 MFMA (checked on gfx950): A[i][k] sits in
 // lane i + 32*(k/8), element k%8; B[k][j] in lane j + 32*(k/8), element k%8;
@@ -386,7 +408,17 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
   unsigned char* qs = smem_raw;                                  // Q rows of the group
   unsigned char* vs = smem_raw + (size_t)kRows * L::ROWB * (1 + wid);   // this wave's V tile
 
-  stage_rows<DP, NT>(qs, a.q + ((size_t)g * a.M + row0) * d, min(kRows, a.M - row0), d, d);
+  // largest magnitude bits of the Q and V elements loaded here (K is checked by
+  // the second pass, which reads every key too: checking it here would keep a
+  // tile's K registers alive across the next tile's prefetch)
+  us2 mg = {0, 0};
+  {
+    RowStage<DP, NT> qst;
+    qst.load(a.q + ((size_t)g * a.M + row0) * d, min(kRows, a.M - row0), d, d);
+#pragma unroll
+    for (int k = 0; k < RowStage<DP, NT>::IT; ++k) mg = mag_max4(mg, qst.x[k]);
+    qst.store(qs);
+  }
   __syncthreads();
 
   float m = -INFINITY, S = 0.f, Sx = 0.f, chk = 0.f;
@@ -527,6 +559,8 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
       }
     // this tile's V has landed once at most the loads issued above are pending
     if constexpr (kVRegs) {
+#pragma unroll
+      for (int i = 0; i < L::CHP / 2; ++i) mg = mag_max4(mg, vr[i]);
       store_v_tile<DP>(vs, lx, vr);
       if (kPreV && more) load_v_tile<DP>(vg, n0, jend, d, lx, vr);
     } else {
@@ -552,6 +586,10 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
         }
         va[b] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3,
                                                                    4, 5, 6, 7));
+        if constexpr (!kVRegs) {   // V came straight to LDS: check it as it is read
+          const u32x4 vx = __builtin_bit_cast(u32x4, va[b]);
+          mg = mag_max4(mg, vx);
+        }
       }
       // the DB accumulators are independent: issue them back to back
 #pragma unroll
@@ -562,6 +600,7 @@ __global__ __launch_bounds__(64 * p1_waves(DP), (DP <= 128 ? kP1Waves : 1)) void
     wave_sync_lds();
   }
   if (!(chk == 0.f)) bad = 1;
+  latch_inputs(a.latch, mg);
 
   // ---- combine the waves' states for each row (fixed order) ----
   bad |= __shfl_xor(bad, 32);
@@ -1342,7 +1381,9 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? 2 : 1)) void merge_kernel(Sc
     a.rs.jstar[ro] = jst;
     a.rs.fix[ro] = fix ? 1 : 0;
     if (!fix) a.rs.cstar[ro] = (nonfin || singular) ? 0.f : dist / (Sx * Sx);
-    const uint32_t bits = (nonfin ? LATCH_NONFINITE : 0u) | (singular ? LATCH_SINGULAR : 0u);
+    // a non-finite intermediate with finite inputs inside the contract cannot
+    // occur: it is an overflow (the first pass latched any input out of range)
+    const uint32_t bits = (nonfin ? LATCH_OVERFLOW : 0u) | (singular ? LATCH_SINGULAR : 0u);
     if (bits) atomicOr(a.latch, bits);
   }
   if (!fix) return;
@@ -1512,6 +1553,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
   // soon as the matrix products have consumed them.  Every row group of the
   // head uses the same K/V tile.
   bf16x8 kB[NC], vB[NC];
+  us2 mg = {0, 0};   // largest magnitude bits of the keys read here (the input check)
   if (kP2Overlap && wid < next) issue(wid, kB, vB);
   for (int t = wid; t < next; t += kWaves) {
     const int64_t j0 = e0 + (int64_t)t * kTile;
@@ -1546,6 +1588,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
     float vn2 = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
+      mg = mag_max4(mg, __builtin_bit_cast(u32x4, kB[c]));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bf16x2 x2 = {vB[c][2 * e], vB[c][2 * e + 1]};
@@ -1683,6 +1726,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
     a.scores[(size_t)g * n + j] = (j >= n - a.w) ? INFINITY : mx + 0.f;
   }
   if (flags) atomicOr(a.latch, flags);
+  latch_inputs(a.latch, mg);
 }
 
 // -------------------------------------------------------- attention-only --
@@ -1712,7 +1756,14 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kAttnWaves : 2)) void attn_p
   const int64_t causal = row_ok ? a.n - a.w + ((row0 + r) % a.w) : -1;
   const int64_t all_see = a.n - a.w;
   unsigned char* qs = smem_raw;
-  stage_rows<DP>(qs, a.q + ((size_t)g * a.M + row0) * d, min(kRows, a.M - row0), d, d);
+  us2 mg = {0, 0};   // largest magnitude bits of the Q and K elements loaded here
+  {
+    RowStage<DP> qst;
+    qst.load(a.q + ((size_t)g * a.M + row0) * d, min(kRows, a.M - row0), d, d);
+#pragma unroll
+    for (int k = 0; k < RowStage<DP>::IT; ++k) mg = mag_max4(mg, qst.x[k]);
+    qst.store(qs);
+  }
   __syncthreads();
 
   // S^T = K Q^T as in pass 1: lane l owns row l%32 and 16 of the tile's tokens
@@ -1741,6 +1792,8 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kAttnWaves : 2)) void attn_p
       st = mfma32(kk[u][c], lds8<DP>(qs, r, 2 * c + hh), st);
       if (c + 1 < NC) st1 = mfma32(kk[u][c + 1], lds8<DP>(qs, r, 2 * c + 2 + hh), st1);
     }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) mg = mag_max4(mg, __builtin_bit_cast(u32x4, kk[u][c]));
     const bool interior = (j0 + kTile <= jend) && (j0 + kTile - 1 <= all_see);
     float s2[16];
     float lm = -INFINITY;
@@ -1768,6 +1821,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kAttnWaves : 2)) void attn_p
   }
   int bad = (chk == 0.f) ? 0 : 1;
   bad |= __shfl_xor(bad, 32);
+  latch_inputs(a.latch, mg);
   if (hh == 0) {
     sm_m[wid][r] = m;
     sm_S[wid][r] = S;
@@ -1871,7 +1925,7 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kAttnWaves : 2)) void attn_p
       // rows >= M have no query: lse = +inf makes every p of theirs 0
       lse_s[hrow] = (hrow < a.M && M > -INFINITY) ? M + log2f(Ssum) : INFINITY;
       if (hrow < a.M && (bad || !(M > -INFINITY) || !(Ssum <= FLT_MAX)) && ch == 0)
-        atomicOr(a.latch, LATCH_NONFINITE);
+        atomicOr(a.latch, LATCH_OVERFLOW);   // an overflow: inputs were checked by pass A
     }
   }
   __syncthreads();

@@ -56,8 +56,9 @@ enum {
     DROPKV_EINVAL = 1,     /* bad argument, found on the host before any launch */
     DROPKV_ESINGULAR = 2,  /* some window query puts probability that rounds to 1 on one key */
     DROPKV_ENONFINITE = 3, /* a non-finite input element */
-    DROPKV_ERANGE = 4,     /* a score beyond FLT_MAX, a keep index outside [0, n), or an
-                              in-place keep list that is not strictly ascending */
+    DROPKV_ERANGE = 4,     /* an input element of magnitude >= 2^48, a keep index outside
+                              [0, n), or an in-place keep list that is not strictly
+                              ascending */
     DROPKV_EDEVICE = 5,    /* a HIP runtime error */
     DROPKV_ENOMEM = 6,     /* scratch allocation failed */
     DROPKV_ESCRATCH = 7    /* dropkv_score_noalloc: the call needs more scratch than its
@@ -87,10 +88,13 @@ int dropkv_destroy(dropkv_ctx *ctx);
  *   w > n; n < 1 or n >= 2^31; pool < 1, pool even or pool > 129; d % 8 != 0 or
  *   d > 256; G * w > 128 (the window rows of one KV head, in groups of 32; the
  *   first pass reads K and V once per group); for d > 128, G * w > 96.
- * Latched: ESINGULAR if for some window query the mass off its arg-max key,
- *   relative to the arg-max, is <= 2^-53 (so p_max rounds to 1 in binary64);
- *   ENONFINITE if an input element is not finite; ERANGE if a score exceeds
- *   FLT_MAX.
+ * Input contract: every q, k and v element finite and of magnitude below
+ *   2^48 (then no logit, distance or score, and no fp32 intermediate of them,
+ *   comes near FLT_MAX).
+ * Latched, in this order of precedence: ENONFINITE if an input element is not
+ *   finite; ERANGE if one has magnitude >= 2^48; ESINGULAR if for some window
+ *   query the mass off its arg-max key, relative to the arg-max, is <= 2^-53
+ *   (so p_max rounds to 1 in binary64).
  */
 int dropkv_score(dropkv_ctx *ctx, const uint16_t *q_win, const uint16_t *k_cache,
                  const uint16_t *v_cache, int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int32_t d,
@@ -148,8 +152,9 @@ int dropkv_score_ex(dropkv_ctx *ctx, const uint16_t *q_win, const uint16_t *k_ca
  *                     for j >= n - w  -- the same pooling and protection as
  *                     dropkv_score, so dropkv_select applies unchanged.
  * Only K is read (no value cache).  Arguments and layouts as dropkv_score.
- * EINVAL as for dropkv_score.  Latched: ENONFINITE if an input element is not
- * finite.  (A probability near 1 is not an error here.)
+ * EINVAL as for dropkv_score.  Latched: ENONFINITE if a q or k element is not
+ * finite, else ERANGE if one has magnitude >= 2^48.  (A probability near 1 is
+ * not an error here.)
  */
 int dropkv_score_attention(dropkv_ctx *ctx, const uint16_t *q_win, const uint16_t *k_cache,
                            int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int32_t d, int32_t pool,

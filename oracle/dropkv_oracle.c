@@ -43,8 +43,11 @@
  *   - for j*, the algebraically identical form Delta_j* = p*(abar - v_j*) with
  *     abar the output over the other tokens is used, which stays accurate as
  *     p* -> 1; every other token has p_j <= 1/2 and uses the closed form.
- *   - non-finite inputs reject the call (ENONFINITE); a finite score above
- *     FLT_MAX, which the fp32 output cannot hold, rejects it with ERANGE.
+ *   - non-finite inputs reject the call (ENONFINITE); then an input element of
+ *     magnitude 2^48 or more rejects it with ERANGE (the input contract: below
+ *     it no score, and no fp32 intermediate a scorer forms, can exceed
+ *     FLT_MAX); a finite score above FLT_MAX, which the fp32 output cannot
+ *     hold, would also be ERANGE (unreachable inside the contract).
  *
  * Inputs are bf16 bit patterns (uint16), widened exactly to double.
  * Layouts: q [Hq][w][d], k and v [Hkv][n][d], scores [Hkv][n].
@@ -70,6 +73,9 @@ static double bf16_to_double(uint16_t b) {
 }
 
 static int bf16_is_finite(uint16_t b) { return (b & 0x7F80u) != 0x7F80u; }
+/* Input contract (reading R-11): |x| < 2^48, i.e. the bits without the sign
+ * below those of 2^48 (exponent 127 + 48). */
+static int bf16_in_range(uint16_t b) { return (b & 0x7FFFu) < 0x5780u; }
 
 static int check_shapes(int64_t n, int w, int hq, int hkv, int d) {
     if (n < 1 || w < 1 || w > n || hq < 1 || hkv < 1 || d < 1) return ORC_EINVAL;
@@ -155,6 +161,11 @@ int oracle_raw_scores(const uint16_t *q, const uint16_t *k, const uint16_t *v, i
         if (!bf16_is_finite(q[i])) return ORC_ENONFINITE;
     for (int64_t i = 0; i < (int64_t)hkv * n * d; ++i)
         if (!bf16_is_finite(k[i]) || !bf16_is_finite(v[i])) return ORC_ENONFINITE;
+    /* then elements outside the contract reject it with ERANGE */
+    for (int64_t i = 0; i < (int64_t)hq * w * d; ++i)
+        if (!bf16_in_range(q[i])) return ORC_ERANGE;
+    for (int64_t i = 0; i < (int64_t)hkv * n * d; ++i)
+        if (!bf16_in_range(k[i]) || !bf16_in_range(v[i])) return ORC_ERANGE;
 
     /* Work is spread over the window rows (h, t) of every KV head: each row
      * writes its contributions to a buffer of its own, and each head's rows are
@@ -432,6 +443,10 @@ int oracle_attention_raw(const uint16_t *q, const uint16_t *k, int64_t n, int w,
         if (!bf16_is_finite(q[i])) return ORC_ENONFINITE;
     for (int64_t i = 0; i < (int64_t)hkv * n * d; ++i)
         if (!bf16_is_finite(k[i])) return ORC_ENONFINITE;
+    for (int64_t i = 0; i < (int64_t)hq * w * d; ++i)
+        if (!bf16_in_range(q[i])) return ORC_ERANGE;
+    for (int64_t i = 0; i < (int64_t)hkv * n * d; ++i)
+        if (!bf16_in_range(k[i])) return ORC_ERANGE;
     const double inv_sqrt_d = 1.0 / sqrt((double)d);
     int status = ORC_OK;
     if (nthreads < 1) nthreads = 1;

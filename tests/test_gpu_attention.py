@@ -124,6 +124,20 @@ def test_nonfinite_rejected(ctx):
     assert st == dropkv.ENONFINITE
 
 
+@pytest.mark.parametrize("which", ["q", "k"])
+def test_input_contract(ctx, which):
+    """Reading R-11: a query or key element of magnitude >= 2^48 is ERANGE on both
+    sides (the attention-only scores read no values)."""
+    q, k = _rand(4, 4, 2, 16, 300, 3)
+    arr = q if which == "q" else k
+    arr.reshape(-1)[7 if which == "q" else 200 * 16 + 3] = 0xD780
+    with pytest.raises(orc.OracleError) as e:
+        orc.attention_score(q, k, 3)
+    assert e.value.code == orc.ERANGE
+    st, _, _ = _gpu_attention(ctx, q, k, 3)
+    assert st == dropkv.ERANGE
+
+
 def test_bitwise_deterministic(ctx):
     q, k = _rand(8, 32, 8, 128, 20000, 8)
     a = _gpu_attention(ctx, q, k, 7)[1]

@@ -382,6 +382,32 @@ def test_score_beyond_float32_is_erange(ctx):
     assert st == dropkv.ERANGE
 
 
+@pytest.mark.parametrize("which,val", [("q", 0x5780), ("k", 0xD780), ("v", 0x5780), ("v", 0x577F),
+                                       ("k", 0x577F), ("q", 0x7F7F)])
+def test_input_contract_matches_oracle(ctx, which, val):
+    """Reading R-11: an element of magnitude >= 2^48 is ERANGE on both sides; just
+    below it the device reaches the oracle's decision (and, when accepted, its
+    scores).  The element sits in a tile of the middle of the sequence."""
+    q, k, v = _rand(8, 4, 2, 32, 700, 4)
+    arrs = {"q": q.copy(), "k": k.copy(), "v": v.copy()}
+    idx = 37 if which == "q" else 300 * 32 + 5
+    arrs[which].reshape(-1)[idx] = val
+    _full_check(ctx, arrs["q"], arrs["k"], arrs["v"], 3, 100, f"contract {which}={hex(val)}")
+
+
+def test_input_contract_precedence_on_device(ctx):
+    q, k, v = _rand(9, 4, 2, 32, 300, 4)
+    a = {"q": q.copy(), "k": k.copy(), "v": v.copy()}
+    a["v"].reshape(-1)[1000] = 0x7FC0
+    a["k"].reshape(-1)[2000] = 0x5780
+    st, *_ = H.gpu_path(ctx, a["q"], a["k"], a["v"], 3, 50, compact=False)
+    assert st == dropkv.ENONFINITE
+    b = {"q": q.copy(), "k": k.copy(), "v": v.copy()}
+    b["q"].reshape(-1)[0] = 0x5780   # out of range, and singular rows
+    st, *_ = H.gpu_path(ctx, b["q"], b["k"], b["v"], 3, 50, compact=False)
+    assert st == dropkv.ERANGE
+
+
 def test_bitwise_deterministic(ctx):
     cfg = wl.LLAMA_4K
     inp = wl.make_layer(cfg, cfg.seed)

@@ -256,6 +256,56 @@ def test_nonfinite_inputs_rejected():
         assert e.value.code == orc.ENONFINITE
 
 
+def _status(f, *args):
+    try:
+        f(*args)
+        return orc.OK
+    except orc.OracleError as e:
+        return e.code
+
+
+def test_input_contract_boundary():
+    """Reading R-11: an element of magnitude 2^48 or more (bf16 bits 0x5780 and up,
+    either sign) makes the call ERANGE; the largest bf16 below it does not."""
+    q, k, v = _tiny_inputs(2, 1, 1, d=8, n=10, w=2)
+    for which in ("q", "k", "v"):
+        for val in (0x5780, 0xD780, 0x7F7F):
+            arrs = {"q": q.copy(), "k": k.copy(), "v": v.copy()}
+            arrs[which].reshape(-1)[5] = val
+            assert _status(orc.score, arrs["q"], arrs["k"], arrs["v"], 1) == orc.ERANGE, (which, hex(val))
+    # just below the bound in V: accepted, every score finite
+    vb = v.copy()
+    vb.reshape(-1)[5] = 0x577F
+    s = orc.score(q, k, vb, 1)
+    assert np.all(np.isfinite(s[:, :-2])) and s.max() > 1e20
+    # in Q or K just below the bound: not ERANGE (this row's softmax is one-hot, so
+    # it is rejected as singular instead)
+    for which in ("q", "k"):
+        arrs = {"q": q.copy(), "k": k.copy(), "v": v.copy()}
+        arrs[which].reshape(-1)[5] = 0x577F
+        assert _status(orc.score, arrs["q"], arrs["k"], arrs["v"], 1) in (orc.OK, orc.ESINGULAR)
+
+
+def test_input_contract_precedence():
+    """Non-finite before out-of-range before singular."""
+    q, k, v = _tiny_inputs(2, 1, 1, d=8, n=10, w=2)
+    a = {"q": q.copy(), "k": k.copy(), "v": v.copy()}
+    a["v"].reshape(-1)[3] = 0x7FC0     # NaN
+    a["k"].reshape(-1)[4] = 0x5780     # 2^48
+    assert _status(orc.score, a["q"], a["k"], a["v"], 1) == orc.ENONFINITE
+    b = {"q": q.copy(), "k": k.copy(), "v": v.copy()}
+    b["q"].reshape(-1)[0] = 0x5780     # out of range, and one-hot rows (singular)
+    assert _status(orc.score, b["q"], b["k"], b["v"], 1) == orc.ERANGE
+
+
+def test_attention_scores_ignore_v_and_check_q_k():
+    q, k, v = _tiny_inputs(2, 1, 1, d=8, n=10, w=2)
+    for which in ("q", "k"):
+        a = {"q": q.copy(), "k": k.copy()}
+        a[which].reshape(-1)[2] = 0xD780
+        assert _status(orc.attention_score, a["q"], a["k"], 1) == orc.ERANGE
+
+
 def test_score_beyond_float32_is_erange():
     q, k, v = _tiny_inputs(2, 1, 1, d=8, n=10, w=2)
     v = wl.bf16_bits(wl.bf16_to_f32(v) * np.float32(1e36))
