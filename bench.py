@@ -591,17 +591,29 @@ def run(args):
 
 def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, commands=()):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) from rocprofv3 counter CSVs,
-    scaled by the same counters on the 1 GiB calibration copy."""
+    scaled by the same counters on the 1 GiB calibration copy.
+
+    Each kernel family is averaged over the dispatches of the K timed steps
+    only (from the pass-1 launch that opens step W to the compaction that
+    closes step W + K - 1, in dispatch order; K and W read from the counter
+    run's command), so the peaked-row, sink-heavy, decode-time and cold-cache
+    calls the same run makes later do not enter the common path's figures; the
+    attention-only kernels, which run only in their own mode, are averaged over
+    all their dispatches.  The per-family means over every dispatch are kept
+    beside them (`all_dispatches`)."""
+    import re
+
     def load(path, counter):
-        rows = {}
+        rows = []
         files = sorted(glob.glob(path)) if any(c in path for c in "*?[") else [path]
         for p in files:
             with open(p) as f:
                 for r in csv.DictReader(f):
                     if r.get("Counter_Name") != counter:
                         continue
-                    name = r.get("Kernel_Name", "")
-                    rows.setdefault(name, []).append(float(r["Counter_Value"]))
+                    key = r.get("Dispatch_Id") or r.get("Correlation_Id") or "0"
+                    rows.append((int(key), r.get("Kernel_Name", ""), float(r["Counter_Value"])))
+        rows.sort()
         return rows
 
     fetch = load(fetch_csv, "FETCH_SIZE")
@@ -611,39 +623,66 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, commands=()):
         # "dropkv::pass1_kernel<" must not match "dropkv::attn_pass1_kernel<"
         return key in name if key == "copyBuffer" else f"::{key}" in name
 
-    def pick(rows, key):
-        vals = [v for name, vs in rows.items() if matches(name, key) for v in vs]
+    def window(rows, command):
+        """(first, last) dispatch ids of the timed steps, or None."""
+        m_s, m_w = re.search(r"--steps (\d+)", command or ""), re.search(r"--warmup (\d+)", command or "")
+        if not (m_s and m_w):
+            return None
+        steps, warm = int(m_s.group(1)), int(m_w.group(1))
+        p1 = [i for i, name, _ in rows if matches(name, "pass1_kernel")]
+        if len(p1) < warm + steps:
+            return None
+        lo, last_p1 = p1[warm], p1[warm + steps - 1]
+        comp = [i for i, name, _ in rows if matches(name, "compact_kernel") and i > last_p1]
+        return (lo, comp[0]) if comp else None
+
+    def mean(rows, key, win):
+        vals = [v for i, name, v in rows if matches(name, key) and (win is None or win[0] <= i <= win[1])]
         return sum(vals) / len(vals) if vals else None
 
-    def largest(rows, key):
-        vals = [v for name, vs in rows.items() if matches(name, key) for v in vs]
-        return max(vals) if vals else None
-
+    cmds = list(commands) + [None, None]
+    wf, ww = window(fetch, cmds[0]), window(write, cmds[1])
     # the calibration copy is the runtime's device-to-device blit of COPY_BYTES,
     # the largest copyBuffer dispatch of the run (the others are small uploads)
-    copy_fetch = largest(fetch, "copyBuffer")
-    copy_write = largest(write, "copyBuffer")
+    cf = [v for _, name, v in fetch if matches(name, "copyBuffer")]
+    cw = [v for _, name, v in write if matches(name, "copyBuffer")]
+    copy_fetch, copy_write = (max(cf) if cf else None), (max(cw) if cw else None)
     f_scale = COPY_BYTES / (copy_fetch * 1024.0) if copy_fetch else None
     w_scale = COPY_BYTES / (copy_write * 1024.0) if copy_write else None
-    kernels = {}
     # selection is one kernel when the head teams fit on the device, else four
-    sel = ("select_fused",) if pick(fetch, "select_fused") is not None else (
+    sel = ("select_fused",) if mean(fetch, "select_fused", None) is not None else (
         "select_s1", "select_s2", "select_s3", "select_s4")
-    families = (("pass1", ("pass1_kernel",)), ("merge", ("merge_kernel",)),
-                ("pass2", ("pass2_kernel",)), ("select", sel), ("compact", ("compact_kernel",)),
-                ("attn_pass1", ("attn_pass1_kernel",)), ("attn_pass2", ("attn_pass2_kernel",)))
-    for short, keys in families:
+    families = (("pass1", ("pass1_kernel",), True), ("merge", ("merge_kernel",), True),
+                ("pass2", ("pass2_kernel",), True), ("select", sel, True),
+                ("compact", ("compact_kernel",), True),
+                ("attn_pass1", ("attn_pass1_kernel",), False),
+                ("attn_pass2", ("attn_pass2_kernel",), False),
+                ("compact_inplace", ("compact_inplace_kernel",), False))
+
+    def family(keys, win_f, win_w):
         # a family of several kernels launched once each per call: sum per-launch means
-        fks = [pick(fetch, k) for k in keys]
-        wks = [pick(write, k) for k in keys]
+        fks = [mean(fetch, k, win_f) for k in keys]
+        wks = [mean(write, k, win_w) for k in keys]
         if None in fks or None in wks or f_scale is None or w_scale is None:
-            continue
+            return None
         fk, wk = sum(fks), sum(wks)
-        kernels[short] = {"fetch_kib": fk, "write_kib": wk,
-                          "bytes_per_launch": fk * 1024.0 * f_scale + wk * 1024.0 * w_scale}
+        return {"fetch_kib": fk, "write_kib": wk,
+                "bytes_per_launch": fk * 1024.0 * f_scale + wk * 1024.0 * w_scale}
+
+    kernels, everything = {}, {}
+    for short, keys, timed in families:
+        k_ = family(keys, wf if timed else None, ww if timed else None)
+        if k_ is not None:
+            kernels[short] = k_
+        a_ = family(keys, None, None)
+        if a_ is not None:
+            everything[short] = a_
     out = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
            "copy_bytes": COPY_BYTES, "copy_fetch_kib": copy_fetch, "copy_write_kib": copy_write,
-           "fetch_scale": f_scale, "write_scale": w_scale, "kernels": kernels,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "window": {"fetch_dispatches": wf, "write_dispatches": ww,
+                      "what": "the timed steps of the counter runs (common-path calls only)"},
+           "kernels": kernels, "all_dispatches": everything,
            "counter_runs": list(commands),
            "made_by": f"python bench.py --summarize-pmc {fetch_csv} {write_csv} ..."}
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")

@@ -69,6 +69,39 @@ def test_traffic_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     assert t["kernels"]["attn_pass1"]["bytes_per_launch"] == pytest.approx((2 * 50 + 5) * 1024)
 
 
+def test_traffic_summary_averages_the_timed_steps_only(tmp_path, monkeypatch):
+    """The common path's per-launch figures come from the K timed steps (after W
+    warm-up steps, read from the counter run's command); a later peaked-row
+    merge stays out of them and is seen only in the all-dispatch means."""
+    import csv as csv_
+    seq = []
+    for _ in range(5):   # 2 warm-up + 3 timed steps
+        seq += [("void dropkv::pass1_kernel<128, true>(x)", 100.0), ("void dropkv::merge_kernel<128>(x)", 10.0),
+                ("void dropkv::pass2_kernel<128, true, 4>(x)", 100.0), ("dropkv::select_fused(x)", 5.0),
+                ("dropkv::compact_kernel(x)", 20.0)]
+    seq += [("void dropkv::pass1_kernel<128, true>(x)", 100.0), ("void dropkv::merge_kernel<128>(x)", 999.0),
+            ("void dropkv::pass2_kernel<128, true, 4>(x)", 100.0), ("__amd_rocclr_copyBuffer", 524288.0)]
+    for path, counter in ((tmp_path / "f.csv", "FETCH_SIZE"), (tmp_path / "w.csv", "WRITE_SIZE")):
+        with open(path, "w", newline="") as f:
+            w = csv_.DictWriter(f, ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+            w.writeheader()
+            for i, (name, v) in enumerate(seq, 1):
+                if counter == "WRITE_SIZE" and "copyBuffer" in name:
+                    v = 1048576.0
+                w.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Counter_Name": counter,
+                            "Counter_Value": v})
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "test")
+    cmd = "rocprofv3 --pmc FETCH_SIZE -- python3 bench.py --steps 3 --warmup 2"
+    bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "unit", [cmd, cmd])
+    with open(tmp_path / "profiles" / "traffic_unit.json") as f:
+        t = json.load(f)
+    assert t["window"]["fetch_dispatches"] == [11, 25]
+    assert t["kernels"]["merge"]["fetch_kib"] == pytest.approx(10.0)
+    assert t["all_dispatches"]["merge"]["fetch_kib"] > 10.0
+
+
 @pytest.mark.parametrize("name", ["tiny", "llama4k"])
 def test_planted_key_peaks_every_window_row(name):
     """The peaked-rows measurement's input: in every KV head the planted token
