@@ -94,6 +94,30 @@ void* noalloc_scratch_ptr(int device) {
   return ptr[device];
 }
 
+// The layout (virtual heads, splits, padded width, helpers) that the
+// no-allocation scratch's counters on `device` were last zeroed for.  The
+// merge's arrival counters and head flags move with the layout (onto bytes
+// another layout used for partial sums), and every call leaves them zeroed, so
+// they are zeroed again only when the layout changes or a call failed part-way.
+struct NoAllocLayout {
+  int hv = -1, splits = 0, dp = 0, xh = 0;
+};
+std::mutex noalloc_mu;
+NoAllocLayout noalloc_layout[64];
+bool noalloc_needs_zero(int device, int hv, int splits, int dp, int xh) {
+  if (device < 0 || device >= 64) return true;
+  std::lock_guard<std::mutex> lock(noalloc_mu);
+  NoAllocLayout& l = noalloc_layout[device];
+  if (l.hv == hv && l.splits == splits && l.dp == dp && l.xh == xh) return false;
+  l.hv = hv; l.splits = splits; l.dp = dp; l.xh = xh;
+  return true;
+}
+void noalloc_forget(int device) {
+  if (device < 0 || device >= 64) return;
+  std::lock_guard<std::mutex> lock(noalloc_mu);
+  noalloc_layout[device].hv = -1;
+}
+
 int to_status(hipError_t e) {
   if (e == hipSuccess) return DROPKV_OK;
   if (e == hipErrorOutOfMemory) return DROPKV_ENOMEM;
@@ -231,11 +255,17 @@ int score_common(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
   a.xh = plan_helpers(n, Hkv * a.R, a.splits);
   const size_t need = score_scratch_bytes(Hkv * a.R, a.splits, a.DP, a.xh);
   if (noalloc) {
-    // the array starts zeroed and every call leaves its counters zeroed
     if (need > kNoAllocScratchBytes) return DROPKV_ESCRATCH;
     if (!c->noalloc_scratch) return DROPKV_EDEVICE;
     carve_scratch(c->noalloc_scratch, Hkv * a.R, a.splits, a.DP, a.xh, &a.part, &a.rs, &a.ex);
-    return to_status(launch_score(nullptr, a, s));
+    if (!attention_only && noalloc_needs_zero(c->device, Hkv * a.R, a.splits, a.DP, a.xh)) {
+      // (a zero-fill kernel, not a memset: callers may capture the call in a graph)
+      const hipError_t e = launch_zero(a.ex.cnt, (size_t)(a.ex.head + Hkv * a.R) - (size_t)a.ex.cnt, s);
+      if (e != hipSuccess) { noalloc_forget(c->device); return to_status(e); }
+    }
+    const int rc = to_status(launch_score(nullptr, a, s));
+    if (rc != DROPKV_OK) noalloc_forget(c->device);
+    return rc;
   }
   // a layout change moves the merge's arrival counters: zero them (in stream
   // order) whenever the scratch or its layout changes; every call leaves them zeroed
@@ -252,6 +282,7 @@ int score_common(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
     hipError_t e = hipMalloc(&c->scratch, need);
     if (e != hipSuccess) { c->scratch = nullptr; return DROPKV_ENOMEM; }
     c->scratch_bytes = need;
+    c->score_hv = -1;   // fresh memory: the next scoring call zeroes its counters
   }
   carve_scratch(c->scratch, Hkv * a.R, a.splits, a.DP, a.xh, &a.part, &a.rs, &a.ex);
   if (!attention_only && relayout) {
@@ -260,7 +291,10 @@ int score_common(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
     if (e != hipSuccess) return to_status(e);
     c->score_hv = Hkv * a.R; c->score_splits = a.splits; c->score_dp = a.DP; c->score_xh = a.xh;
   }
-  return to_status(attention_only ? launch_score_attention(c, a, s) : launch_score(c, a, s));
+  const int rc = to_status(attention_only ? launch_score_attention(c, a, s) : launch_score(c, a, s));
+  // a call that failed part-way may leave counters set: zero them next time
+  if (rc != DROPKV_OK && !attention_only) c->score_hv = -1;
+  return rc;
 }
 
 }  // namespace

@@ -408,6 +408,31 @@ def test_input_contract_precedence_on_device(ctx):
     assert st == dropkv.ERANGE
 
 
+def test_back_to_back_calls_with_every_workgroup_resident():
+    """Small grids put every first-pass, merge and second-pass workgroup of a
+    call on the device at once, so a second-pass workgroup polls its head's
+    merge count before the head's splits are even done.  Calls one after the
+    other -- each on a fresh context (whose scratch may reuse the last one's
+    memory) and then on one context across changing shapes -- must each wait
+    for their own counts and match the oracle."""
+    shapes = [(8, 8, 96, 1499, 8, 7, 300), (8, 8, 96, 1499, 8, 7, 300), (4, 2, 64, 333, 4, 5, 100),
+              (8, 8, 96, 1500, 8, 7, 300), (32, 8, 128, 2600, 8, 7, 900)]
+    for i, (Hq, Hkv, d, n, w, pool, budget) in enumerate(shapes):
+        c = dropkv.Context(0)
+        try:
+            q, k, v = _rand(500 + i, Hq, Hkv, d, n, w)
+            _full_check(c, q, k, v, pool, budget, f"fresh context {i}: Hq={Hq} Hkv={Hkv} d={d} n={n}")
+        finally:
+            c.close()
+    c = dropkv.Context(0)
+    try:
+        for i, (Hq, Hkv, d, n, w, pool, budget) in enumerate(shapes + shapes[::-1]):
+            q, k, v = _rand(600 + i, Hq, Hkv, d, n, w)
+            _full_check(c, q, k, v, pool, budget, f"one context, call {i}: Hq={Hq} Hkv={Hkv} d={d} n={n}")
+    finally:
+        c.close()
+
+
 def test_bitwise_deterministic(ctx):
     cfg = wl.LLAMA_4K
     inp = wl.make_layer(cfg, cfg.seed)
