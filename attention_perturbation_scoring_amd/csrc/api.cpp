@@ -222,7 +222,8 @@ namespace {
 int score_common(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
                  const uint16_t* v_cache, bool attention_only, int64_t n, int32_t w, int32_t Hq,
                  int32_t Hkv, int32_t d, int32_t pool, float* scores, float* out_a,
-                 float* out_lse, void* stream, bool noalloc = false, int64_t cap = 0) {
+                 float* out_lse, void* stream, bool noalloc = false, int64_t cap = 0,
+                 uint32_t* hist1 = nullptr) {
   if (!c) return DROPKV_EINVAL;
   if (!aligned16(q_win) || !aligned16(k_cache) || !aligned16(scores)) return DROPKV_EINVAL;
   if ((out_a && !aligned16(out_a)) || (out_lse && !aligned16(out_lse))) return DROPKV_EINVAL;
@@ -253,6 +254,10 @@ int score_common(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
   a.out_a = out_a;
   a.out_lse = out_lse;
   a.xh = plan_helpers(n, Hkv * a.R, a.splits);
+  if (hist1 && !attention_only) {   // score + select: the selection's first digit, built in pass 2
+    a.hist1 = hist1;
+    a.hist1_stride = fused_bins();
+  }
   const size_t need = score_scratch_bytes(Hkv * a.R, a.splits, a.DP, a.xh);
   if (noalloc) {
     if (need > kNoAllocScratchBytes) return DROPKV_ESCRATCH;
@@ -378,6 +383,43 @@ int dropkv_select(dropkv_ctx* c, const float* scores, int32_t Hkv, int64_t n, in
   const int rc = sel_prepare(c, c->sel[0], Hkv, n, s, &sc);
   if (rc != DROPKV_OK) return rc;
   return to_status(launch_select(c, scores, Hkv, n, budget, keep, c->latch, sc, c->sel_wait, s));
+}
+
+int dropkv_score_select(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
+                        const uint16_t* v_cache, int64_t n, int32_t w, int32_t Hq, int32_t Hkv,
+                        int32_t d, int32_t pool, int64_t budget, float* scores, int32_t* keep,
+                        void* stream) {
+  if (!c) return DROPKV_EINVAL;
+  if (Hkv < 1 || n < 1 || budget < 0 || budget > n) return DROPKV_EINVAL;
+  if (budget > 0 && !aligned16(keep)) return DROPKV_EINVAL;
+  const int G = (Hkv > 0 && Hq % Hkv == 0) ? Hq / Hkv : 1;
+  const int DP = (d + 31) / 32 * 32, R = (G * w + kRows - 1) / kRows;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* hist1 = nullptr;
+  SelScratch sc{};
+  const bool pre1 = d >= 8 && d <= 256 && w >= 1 && select_prebuilt_applies(Hkv, n, budget) &&
+                    score_hist_fits(DP, R);
+  if (pre1) {
+    DeviceGuard guard(c->device);
+    if (!guard.ok) return DROPKV_EDEVICE;
+    // the selection scratch first: its histogram must be zeroed before pass 2 adds
+    const int rc = sel_prepare(c, c->sel[0], Hkv, n, s, &sc);
+    if (rc != DROPKV_OK) return rc;
+    hist1 = sc.fh;
+  }
+  int rc = score_common(c, q_win, k_cache, v_cache, false, n, w, Hq, Hkv, d, pool, scores, nullptr,
+                        nullptr, stream, false, 0, hist1);
+  if (rc != DROPKV_OK) {
+    if (pre1) {   // pass 2 may have added part of a histogram: the scratch is stale
+      c->sel[0].hkv = -1;
+    }
+    return rc;
+  }
+  if (budget == 0) return DROPKV_OK;
+  if (!pre1) return dropkv_select(c, scores, Hkv, n, budget, keep, stream);
+  DeviceGuard guard(c->device);
+  if (!guard.ok) return DROPKV_EDEVICE;
+  return to_status(launch_select(c, scores, Hkv, n, budget, keep, c->latch, sc, c->sel_wait, s, true));
 }
 
 int dropkv_select_layer(dropkv_ctx* c, const float* scores, int32_t Hkv, int64_t n,

@@ -244,7 +244,23 @@ struct ScoreArgs {
   float* out_lse;   // optional [Hq][w]: natural-log log-sum-exp of its visible logits
   int xh;           // merge helper workgroups per virtual head
   ExclScratch ex;
+  // With the score + select entry point: the selection's first-digit histogram
+  // of every head's final scores (12-bit digit key >> 20, kBins1 entries per
+  // head at stride hist1_stride), added to by the second pass; nullptr: none.
+  uint32_t* hist1;
+  int64_t hist1_stride;
 };
+
+constexpr int kBins1 = 4096;   // the selection's first radix digit: the key's top 12 bits
+
+// Floats -> uint32 keys whose unsigned order is the float order; -0 == +0;
+// every NaN maps above +inf.  The selection ranks scores by these keys.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0xffffffffu;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 
 // Scratch of the selection kernels (owned by the context; hist1 and cand_cnt
 // must be zero between calls -- the last selection kernel leaves them zeroed).
@@ -278,9 +294,17 @@ void prof_begin(void* ctx, const char* name, hipStream_t s);
 void prof_end(void* ctx, const char* name, hipStream_t s);
 
 hipError_t launch_score(void* ctx, const ScoreArgs& a, hipStream_t s);
+// pre1: the second pass has built the first-digit histogram into sc.fh (only
+// when select_prebuilt_applies said so)
 hipError_t launch_select(void* ctx, const float* scores, int Hkv, int64_t n, int64_t budget,
                          int32_t* keep, uint32_t* latch, const SelScratch& sc, int64_t wait,
-                         hipStream_t s);
+                         hipStream_t s, bool pre1 = false);
+// Whether selection of these sizes runs the single-launch team path, which can
+// start from a histogram the second pass built (sc.fh, stride fused_bins()).
+bool select_prebuilt_applies(int Hkv, int64_t n, int64_t budget);
+int64_t fused_bins();
+// Whether the second pass has LDS for its chunk's histogram (head dim / row groups).
+bool score_hist_fits(int DP, int R);
 hipError_t launch_layer_counts(void* ctx, const int32_t* keep, int64_t budget, int64_t n, int Hkv,
                                int32_t* counts, uint32_t* latch, hipStream_t s);
 // In place: rows keep[g][0..budget) of the [Hkv][hs / d][d] K and V caches move to

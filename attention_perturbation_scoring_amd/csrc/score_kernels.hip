@@ -1719,11 +1719,36 @@ __global__ __launch_bounds__(kThreads, (DP <= 128 ? kP2Waves : 1)) void pass2_ke
     if (hh == 0 && tok_ok) rawbuf[tok - e0] = raw;
   }
   __syncthreads();
-  for (int64_t j = c0 + tid; j < c1; j += kThreads) {
-    const int64_t lo = max((int64_t)0, j - rad), hi = min(n - 1, j + rad);
-    float mx = rawbuf[lo - e0];
-    for (int64_t i = lo + 1; i <= hi; ++i) mx = fmaxf(mx, rawbuf[i - e0]);
-    a.scores[(size_t)g * n + j] = (j >= n - a.w) ? INFINITY : mx + 0.f;
+  if (a.hist1) {
+    // score + select: the chunk's final scores also go into the selection's
+    // first-digit histogram -- 16-bit counts, two per word, in the staging
+    // region (free after the tiles), then one device-scope add per non-empty bin
+    uint32_t* h32 = reinterpret_cast<uint32_t*>(smem_raw);
+    for (int i = tid; i < kBins1 / 2; i += kThreads) h32[i] = 0u;
+    __syncthreads();
+    for (int64_t j = c0 + tid; j < c1; j += kThreads) {
+      const int64_t lo = max((int64_t)0, j - rad), hi = min(n - 1, j + rad);
+      float mx = rawbuf[lo - e0];
+      for (int64_t i = lo + 1; i <= hi; ++i) mx = fmaxf(mx, rawbuf[i - e0]);
+      const float sv = (j >= n - a.w) ? INFINITY : mx + 0.f;
+      a.scores[(size_t)g * n + j] = sv;
+      const uint32_t bin = order_key(sv) >> 20;
+      atomicAdd(h32 + (bin >> 1), (bin & 1u) ? 0x10000u : 1u);
+    }
+    __syncthreads();
+    uint32_t* gh = a.hist1 + (size_t)g * a.hist1_stride;
+    for (int i = tid; i < kBins1 / 2; i += kThreads) {
+      const uint32_t c2 = h32[i];
+      if (c2 & 0xffffu) atomicAdd(gh + 2 * i, c2 & 0xffffu);
+      if (c2 >> 16) atomicAdd(gh + 2 * i + 1, c2 >> 16);
+    }
+  } else {
+    for (int64_t j = c0 + tid; j < c1; j += kThreads) {
+      const int64_t lo = max((int64_t)0, j - rad), hi = min(n - 1, j + rad);
+      float mx = rawbuf[lo - e0];
+      for (int64_t i = lo + 1; i <= hi; ++i) mx = fmaxf(mx, rawbuf[i - e0]);
+      a.scores[(size_t)g * n + j] = (j >= n - a.w) ? INFINITY : mx + 0.f;
+    }
   }
   if (flags) atomicOr(a.latch, flags);
   latch_inputs(a.latch, mg);
@@ -2042,6 +2067,23 @@ static hipError_t launch_attn_dp(void* ctx, const ScoreArgs& a, hipStream_t s) {
 template <int DP>
 static hipError_t launch_attn_d(void* ctx, const ScoreArgs& a, hipStream_t s) {
   return a.d == DP ? launch_attn_dp<DP, true>(ctx, a, s) : launch_attn_dp<DP, false>(ctx, a, s);
+}
+
+bool score_hist_fits(int DP, int R) {
+  // the histogram overlays the row groups' staging (Q, a_hi, a_lo rows)
+  size_t gb = 0;
+  switch (DP) {
+    case 32: gb = pass2_group_bytes<32>(); break;
+    case 64: gb = pass2_group_bytes<64>(); break;
+    case 96: gb = pass2_group_bytes<96>(); break;
+    case 128: gb = pass2_group_bytes<128>(); break;
+    case 160: gb = pass2_group_bytes<160>(); break;
+    case 192: gb = pass2_group_bytes<192>(); break;
+    case 224: gb = pass2_group_bytes<224>(); break;
+    case 256: gb = pass2_group_bytes<256>(); break;
+    default: return false;
+  }
+  return (size_t)R * gb >= (size_t)kBins1 / 2 * 4;
 }
 
 // Whether pass 2's LDS (the row groups' Q / a rows and the chunk buffer) fits a

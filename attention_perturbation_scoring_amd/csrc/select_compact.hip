@@ -40,18 +40,8 @@ namespace dropkv {
 constexpr int kSelThreads = 256;
 constexpr int kSelPer = 16;
 constexpr int kSelBlock = kSelThreads * kSelPer;   // 4096 tokens per block
-constexpr int kBins1 = 4096;
 constexpr int kCandCap = 8192;
 constexpr int kS3Threads = 1024;
-
-// Floats -> uint32 keys whose unsigned order is the float order; -0 == +0;
-// every NaN maps above +inf.
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0xffffffffu;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 // Exclusive block scan of one uint per thread (NW waves); returns the total too.
 // `sh` holds at least NW words; the block may reuse it once this returns.
@@ -82,6 +72,9 @@ struct SelArgs {
   SelScratch sc;
   int64_t wait;             // single-launch path: polls at a team barrier before a
                             // workgroup finishes its share alone (< 0: at once)
+  int pre1;                 // single-launch path: the first-digit histogram of the
+                            // head's scores is already in sc.fh (built by the second
+                            // pass, without the padding slots)
 };
 
 // Word 0 of the latch holds the errors of scoring, selection and packing; word 1
@@ -605,18 +598,35 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
     for (int i = 0; i < kFusedPer; ++i) key[i] = i < nv ? order_key(sg[base + i]) : 0u;
   }
   const uint32_t pad = nblk * (uint32_t)kFusedBlock - (uint32_t)a.n;
-  if (stop) return;   // nothing has been written yet
+  if (stop) {   // nothing has been written yet, but a prebuilt histogram must not stay
+    if (a.pre1)
+      for (int i = tid; i < kBins1; i += kFusedThreads) fh[i] = 0u;
+    return;
+  }
 
   // T is the k-th smallest key; `need` (>= 1) of the keys equal to T are
   // evicted; the members before b hold gt_before keys above T and ties_before
   // keys equal to T
   uint32_t T = 0u, need = 0u, gt_before = 0u, ties_before = 0u;
   bool alone = a.wait < 0;
-  // round 1: the 12-bit bin b1 holding the k-th smallest key, and its size
-  uint32_t prefix = 0u, mask = 0u, krem = (uint32_t)(a.n - a.budget) + pad;
-  if (!alone)
-    alone = !radix_round<kBins1, true>(key, 20, h, fh, bar, nblk, a.wait, prefix, mask, krem, sh,
-                                       &s_bin, &s_below, &s_count, &s_ok);
+  // round 1: the 12-bit bin b1 holding the k-th smallest key, and its size.
+  // A histogram the second pass built counts the head's real keys only (no
+  // padding slots), and needs no team barrier: it is complete when this
+  // launch starts.  `bar0` is the barrier arrivals before the exchange.
+  uint32_t prefix = 0u, mask = 0u, krem = (uint32_t)(a.n - a.budget) + (a.pre1 ? 0u : pad);
+  const uint32_t bar0 = a.pre1 ? 0u : nblk;
+  if (!alone) {
+    if (a.pre1) {
+      find_bin_agent<NW, kBins1>(fh, krem, &s_bin, &s_below, &s_count, sh);
+      prefix |= s_bin << 20;
+      mask |= (uint32_t)(kBins1 - 1) << 20;
+      krem -= s_below;
+      __syncthreads();
+    } else {
+      alone = !radix_round<kBins1, true>(key, 20, h, fh, bar, nblk, a.wait, prefix, mask, krem, sh,
+                                         &s_bin, &s_below, &s_count, &s_ok);
+    }
+  }
   if (!alone) {
     const uint32_t c1 = s_count;   // the same in every member: read from one histogram
     const uint32_t b1 = prefix >> 20;
@@ -652,7 +662,7 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
           if (pos < (uint32_t)kFusedCand) cand[pos] = (uint64_t)key[i] | ((uint64_t)b << 32);
           ++pos;
         }
-      alone = !team_barrier<true>(bar, 2 * nblk, a.wait, &s_ok);
+      alone = !team_barrier<true>(bar, bar0 + nblk, a.wait, &s_ok);
       if (!alone) {
         // every candidate and count load in flight at once (c1 <= kFusedCand)
         constexpr int CU = kFusedCand / kFusedThreads;
@@ -703,9 +713,9 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
     } else {
       // Too many keys share the bin: two more histogram rounds over the team,
       // then an exchange of each member's counts above and equal to T.
-      bool ok = radix_round<1024, false>(key, 10, h, fh + kBins1, bar, 2 * nblk, a.wait, prefix,
+      bool ok = radix_round<1024, false>(key, 10, h, fh + kBins1, bar, bar0 + nblk, a.wait, prefix,
                                          mask, krem, sh, &s_bin, &s_below, &s_count, &s_ok);
-      ok = ok && radix_round<1024, false>(key, 0, h, fh + kBins1 + 1024, bar, 3 * nblk, a.wait,
+      ok = ok && radix_round<1024, false>(key, 0, h, fh + kBins1 + 1024, bar, bar0 + 2 * nblk, a.wait,
                                           prefix, mask, krem, sh, &s_bin, &s_below, &s_count,
                                           &s_ok);
       if (ok) {
@@ -726,7 +736,7 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
                                                     __HIP_MEMORY_SCOPE_AGENT);
           asm volatile("s_waitcnt vmcnt(0)" ::"v"(o1), "v"(o2) : "memory");
         }
-        ok = team_barrier(bar, 4 * nblk, a.wait, &s_ok);
+        ok = team_barrier(bar, bar0 + 3 * nblk, a.wait, &s_ok);
         if (ok) {
           for (uint32_t i = tid; i < nblk; i += kFusedThreads) {
             gtc[i] = load_agent(blk_gt + i);
@@ -1143,9 +1153,21 @@ static int64_t fused_capacity() {
   return cap[dev];
 }
 
+bool select_prebuilt_applies(int Hkv, int64_t n, int64_t budget) {
+  const int64_t team = (n + kFusedBlock - 1) / kFusedBlock;
+  return budget > 0 && budget < n && team > 1 && team <= kFusedThreads &&
+         (int64_t)Hkv * team <= fused_capacity();
+}
+int64_t fused_bins() { return kFusedBins; }
+
 hipError_t launch_select(void* ctx, const float* scores, int Hkv, int64_t n, int64_t budget,
                          int32_t* keep, uint32_t* latch, const SelScratch& sc, int64_t wait,
-                         hipStream_t s) {
+                         hipStream_t s, bool pre1) {
+  if (pre1 && !select_prebuilt_applies(Hkv, n, budget)) {   // (callers ask first; kept safe)
+    const hipError_t e = launch_zero(sc.fh, (size_t)Hkv * kFusedBins * 4, s);
+    if (e != hipSuccess) return e;
+    pre1 = false;
+  }
   if (budget == n) {
     const int64_t total = (int64_t)Hkv * n;
     int64_t blocks = (total + 255) / 256;
@@ -1172,6 +1194,7 @@ hipError_t launch_select(void* ctx, const float* scores, int Hkv, int64_t n, int
   if (team <= kFusedThreads && (int64_t)Hkv * team <= fused_capacity()) {
     SelArgs f = a;
     f.nblk = (int)team;
+    f.pre1 = pre1 ? 1 : 0;
     void* args[] = {&f};
     const dim3 fgrid((unsigned)((int64_t)Hkv * team)), fblock(kFusedThreads);
     const hipError_t e =
@@ -1181,6 +1204,10 @@ hipError_t launch_select(void* ctx, const float* scores, int Hkv, int64_t n, int
       return hipSuccess;
     }
     (void)hipGetLastError();   // did not fit after all: take the multi-launch path
+  }
+  if (pre1) {   // the prebuilt histogram is not used: leave the scratch zeroed
+    const hipError_t e = launch_zero(sc.fh, (size_t)Hkv * kFusedBins * 4, s);
+    if (e != hipSuccess) return e;
   }
   const unsigned grid = (unsigned)((int64_t)Hkv * a.nblk);
   hipLaunchKernelGGL(select_s1, dim3(grid), dim3(kSelThreads), 0, s, a);

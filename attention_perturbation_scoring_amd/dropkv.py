@@ -47,6 +47,7 @@ def lib():
             "dropkv_score_ex": [P, P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P],
             "dropkv_score_noalloc": [P, P, P, P, i64, i32, i32, i32, i32, i32, P, P],
             "dropkv_select": [P, P, i32, i64, i64, P, P],
+            "dropkv_score_select": [P, P, P, P, i64, i32, i32, i32, i32, i32, i64, P, P, P],
             "dropkv_select_layer": [P, P, i32, i64, i64, P, P, P],
             "dropkv_compact": [P, P, P, i32, i64, i32, P, i64, P, P, P],
             "dropkv_compact_inplace": [P, P, P, i32, i64, i64, i32, P, i64, P],
@@ -169,6 +170,12 @@ class Context:
                                             pool, _ptr(scores), _stream(stream)),
                "dropkv_score_attention")
 
+    def score_select(self, q_win, k_cache, v_cache, n, w, Hq, Hkv, d, pool, budget, scores, keep,
+                     stream=None):
+        _check(lib().dropkv_score_select(self._h, _ptr(q_win), _ptr(k_cache), _ptr(v_cache), n, w,
+                                         Hq, Hkv, d, pool, budget, _ptr(scores), _ptr(keep),
+                                         _stream(stream)), "dropkv_score_select")
+
     def select(self, scores, Hkv, n, budget, keep, stream=None):
         _check(lib().dropkv_select(self._h, _ptr(scores), Hkv, n, budget, _ptr(keep),
                                    _stream(stream)), "dropkv_select")
@@ -238,6 +245,10 @@ def dropkv_score_attention(ctx: Context, *args, **kw):
 
 def dropkv_select(ctx: Context, *args, **kw):
     return ctx.select(*args, **kw)
+
+
+def dropkv_score_select(ctx: Context, *args, **kw):
+    return ctx.score_select(*args, **kw)
 
 
 def dropkv_select_layer(ctx: Context, *args, **kw):

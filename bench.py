@@ -168,8 +168,7 @@ def time_sink_heavy(ctx, cfg, dev, scores, keep, stream, steps):
     Hq, Hkv, d, n, w, pool, budget = sc.Hq, sc.Hkv, sc.d, sc.n, sc.w, sc.pool, sc.budget
 
     def call():
-        ctx.score(q, k, v, n, w, Hq, Hkv, d, pool, scores, stream)
-        ctx.select(scores, Hkv, n, budget, keep, stream)
+        ctx.score_select(q, k, v, n, w, Hq, Hkv, d, pool, budget, scores, keep, stream)
 
     call()
     status = ctx.sync(stream)
@@ -376,11 +375,19 @@ def run(args):
 
     counter = [0]
 
+    separate = getattr(args, "separate_calls", False)
+
+    def score_select(q, k, v):
+        if separate:
+            ctx.score(q, k, v, n, w, Hq, Hkv, d, pool, scores, stream)
+            ctx.select(scores, Hkv, n, budget, keep, stream)
+        else:   # one call: the selection's first digit is counted in the second pass
+            ctx.score_select(q, k, v, n, w, Hq, Hkv, d, pool, budget, scores, keep, stream)
+
     def step():
         q, k, v = copies[counter[0] % len(copies)]
         counter[0] += 1
-        ctx.score(q, k, v, n, w, Hq, Hkv, d, pool, scores, stream)
-        ctx.select(scores, Hkv, n, budget, keep, stream)
+        score_select(q, k, v)
         ctx.compact(k, v, Hkv, n, d, keep, budget, k_out, v_out, stream)
 
     log(f"[bench] warmup {args.warmup}")
@@ -498,8 +505,7 @@ def run(args):
                 flush.fill_(float(i))
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
             ev[0].record(stream)
-            ctx.score(q, k, v, n, w, Hq, Hkv, d, pool, scores, stream)
-            ctx.select(scores, Hkv, n, budget, keep, stream)
+            score_select(q, k, v)
             ev[1].record(stream)
             ctx.compact(k, v, Hkv, n, d, keep, budget, k_out, v_out, stream)
             ev[2].record(stream)
@@ -561,6 +567,8 @@ def run(args):
         "config": {"workload": cfg.name, "Hq": Hq, "Hkv": Hkv, "d": d, "n": n, "w": w,
                    "pool": pool, "budget": budget, "batch": 1, "layers": L,
                    "input_dtype": "bf16", "step": "score+select+compact",
+                   "calls": "dropkv_score + dropkv_select + dropkv_compact" if separate
+                            else "dropkv_score_select + dropkv_compact",
                    "layer_copies": len(copies)},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
@@ -786,6 +794,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=2,
                     help="copies of the layer that consecutive steps cycle through")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="time dropkv_score + dropkv_select instead of dropkv_score_select")
     ap.add_argument("--summarize-pmc", nargs="+",
                     metavar="FETCH_CSV WRITE_CSV [FETCH_COMMAND WRITE_COMMAND]")
     ap.add_argument("--summarize-kt", nargs=2, metavar=("STATS_CSV", "COMMAND"))

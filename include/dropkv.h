@@ -183,6 +183,26 @@ int dropkv_select(dropkv_ctx *ctx, const float *scores, int32_t Hkv, int64_t n, 
                   int32_t *keep, void *stream);
 
 /*
+ * dropkv_score then dropkv_select on its scores, as one call: the same scores
+ * (same bits) and the same keep list, with the selection's first radix round
+ * built inside the scoring's second pass.  The pages pool the perturbation
+ * scores and then evict the lowest ("paper digest", Section 3.3 and the
+ * implementation notes' "Algorithm 1"); here the pass that writes the pooled,
+ * protected scores also counts them into the 4096 bins of their top 12 key
+ * bits, so a selection that runs as one launch of a team per head (see
+ * dropkv_select) starts at the bin search instead of a histogram round and a
+ * team barrier.  Other sizes (a head of at most 16384 tokens, a team that does
+ * not fit, budget 0 or n) run exactly dropkv_score and dropkv_select.
+ * Arguments, layouts, errors and the latch as for the two calls; budget == 0
+ * writes only the scores.  The histogram lives in the context's selection
+ * scratch, so calls that overlap on one context race, as for dropkv_select.
+ */
+int dropkv_score_select(dropkv_ctx *ctx, const uint16_t *q_win, const uint16_t *k_cache,
+                        const uint16_t *v_cache, int64_t n, int32_t w, int32_t Hq, int32_t Hkv,
+                        int32_t d, int32_t pool, int64_t budget, float *scores, int32_t *keep,
+                        void *stream);
+
+/*
  * Layer-wide selection for cross-head budgets ("paper digest" §5.3 pairs DropKV
  * scores with an adaptive per-head budget; the pages do not give the
  * allocation rule, and this call takes the plainest one: a single selection over

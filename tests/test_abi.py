@@ -56,6 +56,8 @@ def test_host_only_entry_points():
     assert L.dropkv_compact_inplace(None, None, None, 1, 10, 10, 8, None, 5, None) == dropkv.EINVAL
     assert L.dropkv_rescore(None, None, None, None, 10, 10, 1, 1, 1, 8, 1, 5, None, None,
                             None) == dropkv.EINVAL
+    assert L.dropkv_score_select(None, None, None, None, 10, 1, 1, 1, 8, 1, 5, None, None,
+                                 None) == dropkv.EINVAL
     assert dropkv.strerror(dropkv.ESCRATCH).startswith("needs more scratch")
     # scratch at the headline shape: 64 splits x 32 rows x (d + 5) floats per KV
     # head, per-row state and the merge helpers' parts -- megabytes (within the
