@@ -1135,13 +1135,20 @@ __device__ void merge_helper(const ScoreArgs& a, int hv, int h, MergeHelpLds<DP>
         }
     }
     __syncthreads();
-    // this helper's part for the split's rows
+    // this helper's part for the split's rows, four columns per store
     const size_t hb = ((size_t)hv * a.xh + h) * kRows;
-#pragma unroll 1
-    for (int i = tid; i < kRows * DP; i += kThreads) {
-      const int row = i / DP, dd = i - row * DP;
-      const int o = row * SP + (kPadSlab ? dd : (dd ^ (row & 31)));
-      if (L.act[row]) a.ex.part[(hb + row) * DP + dd] = slab[o] + slab[kRows * SP + o];
+    static_assert((kRows * DP / 4) % kThreads == 0, "whole passes over the part");
+#pragma unroll
+    for (int i4 = tid; i4 < kRows * DP / 4; i4 += kThreads) {
+      const int row = (4 * i4) / DP, dd = 4 * i4 - row * DP;
+      float4 x;
+      float* xs = reinterpret_cast<float*>(&x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int o = row * SP + (kPadSlab ? dd + e : ((dd + e) ^ (row & 31)));
+        xs[e] = slab[o] + slab[kRows * SP + o];
+      }
+      if (L.act[row]) *reinterpret_cast<float4*>(a.ex.part + (hb + row) * DP + dd) = x;
     }
     if (tid < kRows && L.act[tid]) {
       float x = 0.f;

@@ -422,19 +422,15 @@ __device__ bool team_barrier(uint32_t* bar, uint32_t target, int64_t wait, int* 
   return *s_ok != 0;
 }
 
-// Like find_bin, over a histogram the team built with device-scope adds.
-template <int NW, int NB>
-__device__ void find_bin_agent(const uint32_t* hist, uint32_t krem, uint32_t* s_bin,
-                               uint32_t* s_below, uint32_t* s_count, uint32_t* sh) {
-  constexpr int PER = NB / (NW * 64);
+// Like find_bin, over a histogram whose bins t * PER .. t * PER + PER - 1 this
+// thread holds in hv.
+template <int NW, int PER>
+__device__ void find_bin_regs(const uint32_t (&hv)[PER], uint32_t krem, uint32_t* s_bin,
+                              uint32_t* s_below, uint32_t* s_count, uint32_t* sh) {
   const int t = threadIdx.x;
-  uint32_t hv[PER];
   uint32_t loc = 0u;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    hv[i] = load_agent(hist + t * PER + i);
-    loc += hv[i];
-  }
+  for (int i = 0; i < PER; ++i) loc += hv[i];
   uint32_t tot;
   const uint32_t excl = block_exscan<NW>(loc, &tot, sh);
   if (excl < krem && excl + loc >= krem) {
@@ -450,6 +446,17 @@ __device__ void find_bin_agent(const uint32_t* hist, uint32_t krem, uint32_t* s_
     }
   }
   __syncthreads();
+}
+
+// Like find_bin, over a histogram the team built with device-scope adds.
+template <int NW, int NB>
+__device__ void find_bin_agent(const uint32_t* hist, uint32_t krem, uint32_t* s_bin,
+                               uint32_t* s_below, uint32_t* s_count, uint32_t* sh) {
+  constexpr int PER = NB / (NW * 64);
+  uint32_t hv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) hv[i] = load_agent(hist + threadIdx.x * PER + i);
+  find_bin_regs<NW, PER>(hv, krem, s_bin, s_below, s_count, sh);
 }
 
 // One radix round: add this workgroup's keys matching (prefix, mask) to the
@@ -579,6 +586,22 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
   uint32_t* blk_gt = a.sc.blk_above + (size_t)g * nblk;
   uint32_t* blk_tie = a.sc.blk_ties + (size_t)g * nblk;
 
+  // A histogram the second pass built (a previous kernel: ordinary loads see it)
+  // is requested first, to land with the keys; otherwise these words are unused.
+  constexpr int HPER = kBins1 / kFusedThreads;
+  static_assert(HPER % 4 == 0, "16-byte loads of the prebuilt histogram");
+  uint32_t hpre[HPER];
+#pragma unroll
+  for (int q = 0; q < HPER / 4; ++q) {
+    const uint4 x = *reinterpret_cast<const uint4*>(fh + HPER * tid + 4 * q);
+    hpre[4 * q] = x.x; hpre[4 * q + 1] = x.y; hpre[4 * q + 2] = x.z; hpre[4 * q + 3] = x.w;
+  }
+  // taken as used at the end of both key branches below, so that the load is
+  // issued ahead of them (not sunk to its first use, one round trip later)
+  auto pin_hist = [&]() {
+#pragma unroll
+    for (int i = 0; i < HPER; ++i) asm volatile("" ::"v"(hpre[i]));
+  };
   // this thread's kFusedPer consecutive tokens, as order keys
   const float* sg = a.scores + (size_t)g * a.n;
   const int64_t base = (int64_t)b * kFusedBlock + (int64_t)tid * kFusedPer;
@@ -593,9 +616,11 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
       key[4 * q + 2] = order_key(x.z);
       key[4 * q + 3] = order_key(x.w);
     }
+    pin_hist();
   } else {
 #pragma unroll
     for (int i = 0; i < kFusedPer; ++i) key[i] = i < nv ? order_key(sg[base + i]) : 0u;
+    pin_hist();
   }
   const uint32_t pad = nblk * (uint32_t)kFusedBlock - (uint32_t)a.n;
   if (stop) {   // nothing has been written yet, but a prebuilt histogram must not stay
@@ -617,7 +642,7 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
   const uint32_t bar0 = a.pre1 ? 0u : nblk;
   if (!alone) {
     if (a.pre1) {
-      find_bin_agent<NW, kBins1>(fh, krem, &s_bin, &s_below, &s_count, sh);
+      find_bin_regs<NW, HPER>(hpre, krem, &s_bin, &s_below, &s_count, sh);
       prefix |= s_bin << 20;
       mask |= (uint32_t)(kBins1 - 1) << 20;
       krem -= s_below;
