@@ -394,19 +394,16 @@ __device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
 }
 
 // Arrive at the head's barrier and wait for `target` arrivals in total (the
-// counter only grows during one call).  Values exchanged through device-scope
-// atomics need no cache maintenance: the writer waits for their completion
-// before it arrives.  With PLAIN, the workgroup also published ordinary stores:
-// every wave waits until its stores reach L2, then one release fence writes L2
-// back before the arrival, and one acquire fence follows the wait.
+// counter only grows during one call).  Everything the team exchanges goes
+// through device-scope accesses (atomics, and agent-scope stores and loads that
+// bypass the non-coherent L2), so no cache maintenance is needed: the barrier
+// below first waits for every wave's accesses to complete, then arrives.
 // Returns false, for every thread of the workgroup, if the wait gave up after
 // `wait` polls.
-template <bool PLAIN = false>
 __device__ bool team_barrier(uint32_t* bar, uint32_t target, int64_t wait, int* s_ok) {
-  if (PLAIN) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
-    if (PLAIN) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const uint32_t o = __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("s_waitcnt vmcnt(0)" ::"v"(o) : "memory");
     int64_t spins = 0;
@@ -415,7 +412,6 @@ __device__ bool team_barrier(uint32_t* bar, uint32_t target, int64_t wait, int* 
       if (++spins > wait) { ok = 0; break; }
       __builtin_amdgcn_s_sleep(2);
     }
-    if (PLAIN) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     *s_ok = ok;
   }
   __syncthreads();
@@ -679,15 +675,18 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
       __syncthreads();
       uint64_t* cand = a.sc.fcand + (size_t)g * kFusedCand;
       uint32_t pos = s_base + off;
-      // ordinary stores (one device-scope atomic per key would serialise at the
-      // memory side), published by the fences of the barrier
+      // agent-scope stores (written through to the coherence point, unlike a
+      // read-modify-write atomic per key, which would serialise at the memory
+      // side); the teammates read them with agent-scope loads after the barrier
 #pragma unroll
       for (int i = 0; i < kFusedPer; ++i)
         if ((key[i] >> 20) == b1) {
-          if (pos < (uint32_t)kFusedCand) cand[pos] = (uint64_t)key[i] | ((uint64_t)b << 32);
+          if (pos < (uint32_t)kFusedCand)
+            __hip_atomic_store(cand + pos, (uint64_t)key[i] | ((uint64_t)b << 32), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
           ++pos;
         }
-      alone = !team_barrier<true>(bar, bar0 + nblk, a.wait, &s_ok);
+      alone = !team_barrier(bar, bar0 + nblk, a.wait, &s_ok);
       if (!alone) {
         // every candidate and count load in flight at once (c1 <= kFusedCand)
         constexpr int CU = kFusedCand / kFusedThreads;
