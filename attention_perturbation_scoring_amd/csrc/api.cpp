@@ -37,6 +37,7 @@ struct dropkv_ctx {
     void* p = nullptr;
     size_t bytes = 0;
     int hkv = 0;                   // head count the zeroed prefix was laid out for
+    uint32_t epoch = 0;            // single-launch selections since the prefix was zeroed
   } sel[2];
   int64_t sel_wait = kSelectWait;  // team-barrier polls before a selection workgroup goes alone
   void* noalloc_scratch = nullptr; // device address of this device's `scratch` array
@@ -363,8 +364,10 @@ int sel_prepare(dropkv_ctx* c, dropkv_ctx::SelBuf& b, int Hkv, int64_t n, hipStr
     hipError_t e = launch_zero(b.p, select_zero_prefix_bytes(Hkv), s);
     if (e != hipSuccess) return to_status(e);
     b.hkv = Hkv;
+    b.epoch = 0;
   }
   carve_select(b.p, Hkv, n, sc);
+  sc->par = (int)(b.epoch & 1u);
   return DROPKV_OK;
 }
 
@@ -382,7 +385,8 @@ int dropkv_select(dropkv_ctx* c, const float* scores, int32_t Hkv, int64_t n, in
   SelScratch sc{};
   const int rc = sel_prepare(c, c->sel[0], Hkv, n, s, &sc);
   if (rc != DROPKV_OK) return rc;
-  return to_status(launch_select(c, scores, Hkv, n, budget, keep, c->latch, sc, c->sel_wait, s));
+  return to_status(
+      launch_select(c, scores, Hkv, n, budget, keep, c->latch, sc, c->sel_wait, s, &c->sel[0].epoch));
 }
 
 int dropkv_score_select(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
@@ -405,7 +409,7 @@ int dropkv_score_select(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_
     // the selection scratch first: its histogram must be zeroed before pass 2 adds
     const int rc = sel_prepare(c, c->sel[0], Hkv, n, s, &sc);
     if (rc != DROPKV_OK) return rc;
-    hist1 = sc.fh;
+    hist1 = sc.fh + (size_t)sc.par * Hkv * fused_bins();   // this call's parity
   }
   int rc = score_common(c, q_win, k_cache, v_cache, false, n, w, Hq, Hkv, d, pool, scores, nullptr,
                         nullptr, stream, false, 0, hist1);
@@ -419,7 +423,8 @@ int dropkv_score_select(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_
   if (!pre1) return dropkv_select(c, scores, Hkv, n, budget, keep, stream);
   DeviceGuard guard(c->device);
   if (!guard.ok) return DROPKV_EDEVICE;
-  return to_status(launch_select(c, scores, Hkv, n, budget, keep, c->latch, sc, c->sel_wait, s, true));
+  return to_status(launch_select(c, scores, Hkv, n, budget, keep, c->latch, sc, c->sel_wait, s,
+                                 &c->sel[0].epoch, true));
 }
 
 int dropkv_select_layer(dropkv_ctx* c, const float* scores, int32_t Hkv, int64_t n,
@@ -437,7 +442,8 @@ int dropkv_select_layer(dropkv_ctx* c, const float* scores, int32_t Hkv, int64_t
     SelScratch sc{};
     const int rc = sel_prepare(c, c->sel[1], 1, total, s, &sc);
     if (rc != DROPKV_OK) return rc;
-    const hipError_t e = launch_select(c, scores, 1, total, budget, keep, c->latch, sc, c->sel_wait, s);
+    const hipError_t e = launch_select(c, scores, 1, total, budget, keep, c->latch, sc, c->sel_wait, s,
+                                       &c->sel[1].epoch);
     if (e != hipSuccess) return to_status(e);
   }
   return to_status(launch_layer_counts(c, keep, budget, n, Hkv, counts, c->latch, s));

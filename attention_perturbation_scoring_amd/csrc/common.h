@@ -267,9 +267,13 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 struct SelScratch {
   uint32_t* hist1;         // [Hkv][4096]
   uint32_t* cand_cnt;      // [Hkv]
-  uint32_t* fh;            // [Hkv][4096 + 1024 + 1024] histograms of the single-launch path
-  uint32_t* bar;           // [Hkv] arrival counters of the single-launch path
-  uint32_t* done;          // [Hkv] finished-workgroup counters of the single-launch path
+  // The single-launch path's histograms and counters come in two sets, used by
+  // calls of alternating parity: each call clears the other set (the previous
+  // call's) for the next one, so no workgroup has to learn that it finished last.
+  uint32_t* fh;            // [2][Hkv][4096 + 1024 + 1024] histograms of the single-launch path
+  uint32_t* bar;           // [2][Hkv] arrival counters of the single-launch path
+  uint32_t* fcnt;          // [2][Hkv] threshold-bin candidate counters of the single-launch path
+  int par;                 // parity of the next single-launch call (0 or 1)
   uint64_t* fcand;         // [Hkv][8192] (key, member) candidates of the single-launch path
   uint32_t* cand_key;      // [Hkv][8192]
   int32_t* cand_idx;       // [Hkv][8192]
@@ -296,9 +300,11 @@ void prof_end(void* ctx, const char* name, hipStream_t s);
 hipError_t launch_score(void* ctx, const ScoreArgs& a, hipStream_t s);
 // pre1: the second pass has built the first-digit histogram into sc.fh (only
 // when select_prebuilt_applies said so)
+// `epoch` counts the single-launch calls on this scratch (advanced after each);
+// sc.par must be its parity.
 hipError_t launch_select(void* ctx, const float* scores, int Hkv, int64_t n, int64_t budget,
                          int32_t* keep, uint32_t* latch, const SelScratch& sc, int64_t wait,
-                         hipStream_t s, bool pre1 = false);
+                         hipStream_t s, uint32_t* epoch, bool pre1 = false);
 // Whether selection of these sizes runs the single-launch team path, which can
 // start from a histogram the second pass built (sc.fh, stride fused_bins()).
 bool select_prebuilt_applies(int Hkv, int64_t n, int64_t budget);

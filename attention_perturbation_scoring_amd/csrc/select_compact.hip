@@ -577,8 +577,11 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
   const int g = blockIdx.x / a.nblk, b = blockIdx.x % a.nblk;
   const int tid = threadIdx.x;
   const uint32_t nblk = (uint32_t)a.nblk;
-  uint32_t* bar = a.sc.bar + g;
-  uint32_t* fh = a.sc.fh + (size_t)g * kFusedBins;
+  const size_t heads = gridDim.x / nblk, cur = (size_t)a.sc.par * heads + g,
+               oth = (size_t)(a.sc.par ^ 1) * heads + g;
+  uint32_t* bar = a.sc.bar + cur;
+  uint32_t* fh = a.sc.fh + cur * kFusedBins;
+  uint32_t* fcnt = a.sc.fcnt + cur;
   uint32_t* blk_gt = a.sc.blk_above + (size_t)g * nblk;
   uint32_t* blk_tie = a.sc.blk_ties + (size_t)g * nblk;
 
@@ -619,11 +622,20 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
     pin_hist();
   }
   const uint32_t pad = nblk * (uint32_t)kFusedBlock - (uint32_t)a.n;
-  if (stop) {   // nothing has been written yet, but a prebuilt histogram must not stay
-    if (a.pre1)
-      for (int i = tid; i < kBins1; i += kFusedThreads) fh[i] = 0u;
-    return;
+  // The other parity's histograms and counters (the previous call's, which has
+  // ended) are cleared for the next call, each member its share; this call's
+  // are cleared by the next one, whatever way this one ends.
+  {
+    uint32_t* fo = a.sc.fh + oth * kFusedBins;
+    const int per = (kFusedBins + (int)nblk - 1) / (int)nblk;
+    const int lo = b * per, hi = min(kFusedBins, lo + per);
+    for (int i = lo + tid; i < hi; i += kFusedThreads) fo[i] = 0u;
+    if (b == 0 && tid == 0) {
+      a.sc.bar[oth] = 0u;
+      a.sc.fcnt[oth] = 0u;
+    }
   }
+  if (stop) return;   // nothing has been written
 
   // T is the k-th smallest key; `need` (>= 1) of the keys equal to T are
   // evicted; the members before b hold gt_before keys above T and ties_before
@@ -667,8 +679,7 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
         const uint32_t o = __hip_atomic_exchange(blk_gt + b, tot >> 16, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
         const uint32_t mt = tot & 0xffffu;
-        s_base = mt ? __hip_atomic_fetch_add(a.sc.cand_cnt + g, mt, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT)
+        s_base = mt ? __hip_atomic_fetch_add(fcnt, mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                     : 0u;
         asm volatile("s_waitcnt vmcnt(0)" ::"v"(o) : "memory");
       }
@@ -807,27 +818,12 @@ __global__ __launch_bounds__(kFusedThreads) void select_fused(SelArgs a) {
     keepbits |= keepit ? 1u << i : 0u;
   }
   uint32_t pos = keep_before + gt_pre + (tie_pre > ev ? tie_pre - ev : 0u);
-  // count this member out (its reply arrives while the keep list is written);
-  // the last member of the team -- every other member is past its last read of
-  // the team's scratch -- leaves the histograms and counters zeroed
-  uint32_t done_before = 0u;
-  if (tid == 0) done_before = atomicAdd(a.sc.done + g, 1u);
   int32_t* kg = a.keep + (size_t)g * a.budget;
   while (keepbits) {   // one store per kept token, in index order
     const int i = __builtin_ctz(keepbits);
     keepbits &= keepbits - 1u;
     if (pos < (uint32_t)a.budget) kg[pos] = (int32_t)(base + i);
     ++pos;
-  }
-  if (tid == 0) s_ok = done_before == nblk - 1u;
-  __syncthreads();
-  if (s_ok) {
-    for (int i = tid; i < kFusedBins; i += kFusedThreads) fh[i] = 0u;
-    if (tid == 0) {
-      __hip_atomic_store(bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.sc.cand_cnt + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.sc.done + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
   }
 }
 
@@ -938,8 +934,8 @@ __global__ __launch_bounds__(256) void select_all_kernel(int32_t* keep, int64_t 
 
 size_t select_scratch_bytes(int Hkv, int64_t n) {
   const int64_t nblk = (n + kSelBlock - 1) / kSelBlock;
-  const size_t per_head = (size_t)kBins1 * 4 + (size_t)kFusedBins * 4 + (size_t)kCandCap * 8 +
-                          (size_t)kFusedCand * 8 + 8 * 4 + (size_t)nblk * 5 * 4;
+  const size_t per_head = (size_t)kBins1 * 4 + 2 * (size_t)kFusedBins * 4 + (size_t)kCandCap * 8 +
+                          (size_t)kFusedCand * 8 + 12 * 4 + (size_t)nblk * 5 * 4;
   return (size_t)Hkv * per_head + 64 * 256;
 }
 
@@ -951,9 +947,9 @@ void carve_select(void* base, int Hkv, int64_t n, SelScratch* sc) {
   auto take = [&](size_t bytes) { char* x = c; c += al256(bytes); return x; };
   sc->hist1 = (uint32_t*)take((size_t)Hkv * kBins1 * 4);
   sc->cand_cnt = (uint32_t*)take((size_t)Hkv * 4);
-  sc->fh = (uint32_t*)take((size_t)Hkv * kFusedBins * 4);
-  sc->bar = (uint32_t*)take((size_t)Hkv * 4);
-  sc->done = (uint32_t*)take((size_t)Hkv * 4);
+  sc->fh = (uint32_t*)take(2 * (size_t)Hkv * kFusedBins * 4);
+  sc->bar = (uint32_t*)take(2 * (size_t)Hkv * 4);
+  sc->fcnt = (uint32_t*)take(2 * (size_t)Hkv * 4);
   sc->fcand = (uint64_t*)take((size_t)Hkv * kFusedCand * 8);
   sc->cand_key = (uint32_t*)take((size_t)Hkv * kCandCap * 4);
   sc->cand_idx = (int32_t*)take((size_t)Hkv * kCandCap * 4);
@@ -967,11 +963,11 @@ void carve_select(void* base, int Hkv, int64_t n, SelScratch* sc) {
   sc->blk_evt = (uint32_t*)take((size_t)Hkv * nblk * 4);
 }
 
-// Bytes of select scratch that must start zeroed (hist1, cand_cnt, fh, bar and
-// done lead the carve).
+// Bytes of select scratch that must start zeroed (hist1, cand_cnt and both
+// parities of fh, bar and fcnt lead the carve).
 size_t select_zero_prefix_bytes(int Hkv) {
   return al256((size_t)Hkv * kBins1 * 4) + al256((size_t)Hkv * 4) +
-         al256((size_t)Hkv * kFusedBins * 4) + 2 * al256((size_t)Hkv * 4);
+         al256(2 * (size_t)Hkv * kFusedBins * 4) + 2 * al256(2 * (size_t)Hkv * 4);
 }
 
 // Zero-fill of a scratch prefix (a multiple of 4 bytes), ordered on the caller's
@@ -1186,9 +1182,11 @@ int64_t fused_bins() { return kFusedBins; }
 
 hipError_t launch_select(void* ctx, const float* scores, int Hkv, int64_t n, int64_t budget,
                          int32_t* keep, uint32_t* latch, const SelScratch& sc, int64_t wait,
-                         hipStream_t s, bool pre1) {
+                         hipStream_t s, uint32_t* epoch, bool pre1) {
+  // this call's histograms (the prebuilt one included)
+  uint32_t* fh_cur = sc.fh + (size_t)sc.par * Hkv * kFusedBins;
   if (pre1 && !select_prebuilt_applies(Hkv, n, budget)) {   // (callers ask first; kept safe)
-    const hipError_t e = launch_zero(sc.fh, (size_t)Hkv * kFusedBins * 4, s);
+    const hipError_t e = launch_zero(fh_cur, (size_t)Hkv * kFusedBins * 4, s);
     if (e != hipSuccess) return e;
     pre1 = false;
   }
@@ -1224,13 +1222,14 @@ hipError_t launch_select(void* ctx, const float* scores, int Hkv, int64_t n, int
     const hipError_t e =
         hipLaunchKernel(reinterpret_cast<const void*>(select_fused), fgrid, fblock, args, 0, s);
     if (e == hipSuccess) {
+      ++*epoch;   // the kernel clears the other parity for the next call
       prof_end(ctx, "select", s);
       return hipSuccess;
     }
     (void)hipGetLastError();   // did not fit after all: take the multi-launch path
   }
-  if (pre1) {   // the prebuilt histogram is not used: leave the scratch zeroed
-    const hipError_t e = launch_zero(sc.fh, (size_t)Hkv * kFusedBins * 4, s);
+  if (pre1) {   // the prebuilt histogram is not used: leave this parity zeroed
+    const hipError_t e = launch_zero(fh_cur, (size_t)Hkv * kFusedBins * 4, s);
     if (e != hipSuccess) return e;
   }
   const unsigned grid = (unsigned)((int64_t)Hkv * a.nblk);

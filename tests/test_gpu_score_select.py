@@ -91,3 +91,29 @@ def test_withheld_selection_leaves_the_histogram_clean(ctx):
     for i in range(2):
         _same(ctx, inp["q"], inp["k"], inp["v"], n, w, Hq, Hkv, d, pool, budget,
               f"after the rejected call, call {i}")
+
+
+def test_alternating_parities_and_paths(ctx):
+    """The single-launch selection keeps its histograms and counters in two
+    sets, used by calls of alternating parity (each call clears the other set
+    for the next): an uneven mix of prebuilt-histogram calls and plain
+    selections meets both sets from both paths, and every call stays exact."""
+    cfg = wl.CONFIGS["llama32k"]
+    inp = wl.make_layer(cfg, cfg.seed)
+    n, Hkv, B = cfg.n, cfg.Hkv, cfg.budget
+    qd, kd, vd = H.to_dev(inp["q"]), H.to_dev(inp["k"]), H.to_dev(inp["v"])
+    s = torch.empty((Hkv, n), dtype=torch.float32, device="cuda")
+    ctx.score(qd, kd, vd, n, cfg.w, cfg.Hq, Hkv, cfg.d, cfg.pool, s)
+    assert ctx.sync() == dropkv.OK
+    want = orc.select(s.cpu().numpy().astype(np.float64), B)
+    keep = H.Guarded((Hkv, B), torch.int32, -5)
+    for i, kind in enumerate(["ss", "sel", "sel", "ss", "ss", "sel", "ss", "sel"]):
+        print(f"[case] call {i}: {kind}", flush=True)
+        keep.t.fill_(-1)
+        if kind == "ss":
+            ctx.score_select(qd, kd, vd, n, cfg.w, cfg.Hq, Hkv, cfg.d, cfg.pool, B, s, keep.t)
+        else:
+            ctx.select(s, Hkv, n, B, keep.t)
+        assert ctx.sync() == dropkv.OK, f"call {i} ({kind})"
+        keep.check(f"call {i}")
+        np.testing.assert_array_equal(keep.t.cpu().numpy(), want, err_msg=f"call {i} ({kind})")
