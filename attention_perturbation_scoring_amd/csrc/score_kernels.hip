@@ -971,7 +971,7 @@ __device__ void merge_helper(const ScoreArgs& a, int hv, int h, MergeHelpLds<DP>
     bool first = s >= 0;
 #pragma unroll 1
     for (int o = 0; o < kRows; ++o) {
-      const int so = __shfl(s, o);
+      const int so = __builtin_amdgcn_readlane(s, o);   // (a register read, no LDS round trip)
       if (o < lane && so == s) first = false;
     }
     const uint64_t fm = __ballot(first);
