@@ -117,3 +117,30 @@ def test_alternating_parities_and_paths(ctx):
         assert ctx.sync() == dropkv.OK, f"call {i} ({kind})"
         keep.check(f"call {i}")
         np.testing.assert_array_equal(keep.t.cpu().numpy(), want, err_msg=f"call {i} ({kind})")
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_seeded_shapes_match_the_two_calls(ctx, case):
+    """A seeded sweep over what the one-call path depends on: team sizes 2..8
+    (ragged last members), 1..8 KV heads, d 64..256, one to three 32-row groups
+    per KV head (G * w up to 96) and budgets anywhere in (0, n); every case is
+    bitwise the two calls, and the keep list is the oracle's selection on the
+    same scores."""
+    rng = np.random.default_rng(1000 + case)
+    n = int(rng.integers(16385, 131073))
+    Hkv = int(rng.choice([1, 2, 3, 8]))
+    d = int(rng.choice([64, 96, 128, 256]))
+    G = int(rng.choice([1, 2, 4, 12]))
+    w = int(rng.choice([4, 8]))
+    if d > 128 and G * w > 64:   # the wide-head layouts hold up to 96 window rows
+        G = 8
+    pool = int(rng.choice([1, 3, 7]))
+    budget = int(rng.integers(w, n))
+    Hq = G * Hkv
+    q = wl.bf16_bits(rng.standard_normal((Hq, w, d), dtype=np.float32))
+    k = wl.bf16_bits(rng.standard_normal((Hkv, n, d), dtype=np.float32))
+    v = wl.bf16_bits(rng.standard_normal((Hkv, n, d), dtype=np.float32))
+    where = f"case {case}: n={n} Hkv={Hkv} d={d} G={G} w={w} pool={pool} budget={budget}"
+    s, keep = _same(ctx, q, k, v, n, w, Hq, Hkv, d, pool, budget, where)
+    want = orc.select(s.astype(np.float64), budget)
+    np.testing.assert_array_equal(keep[:, :budget], want, err_msg=where)
