@@ -339,8 +339,10 @@ int dropkv_score_attention(dropkv_ctx* c, const uint16_t* q_win, const uint16_t*
 namespace {
 
 // Selection scratch for Hkv heads of n tokens in buffer `b`: (re)allocated on
-// growth; its zeroed prefix is (re)laid out when the head count changes, and
-// every selection leaves it zeroed again.
+// growth; its zeroed prefix is (re)laid out when the head count changes (and
+// the single-launch call count restarts), and every selection leaves what the
+// next one reads zeroed: the multi-launch path its own words, the single-launch
+// path the set of the next call's parity.
 int sel_prepare(dropkv_ctx* c, dropkv_ctx::SelBuf& b, int Hkv, int64_t n, hipStream_t s,
                 SelScratch* sc) {
   const size_t need = select_scratch_bytes(Hkv, n);
