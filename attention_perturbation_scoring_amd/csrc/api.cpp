@@ -391,10 +391,15 @@ int dropkv_select(dropkv_ctx* c, const float* scores, int32_t Hkv, int64_t n, in
       launch_select(c, scores, Hkv, n, budget, keep, c->latch, sc, c->sel_wait, s, &c->sel[0].epoch));
 }
 
-int dropkv_score_select(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
-                        const uint16_t* v_cache, int64_t n, int32_t w, int32_t Hq, int32_t Hkv,
-                        int32_t d, int32_t pool, int64_t budget, float* scores, int32_t* keep,
-                        void* stream) {
+namespace {
+
+// Scoring (K/V head stride cap * d when cap > 0, else n * d) and selection in
+// one call: the second pass also counts the selection's first radix digit when
+// the selection runs as one launch.
+int score_select_impl(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
+                      const uint16_t* v_cache, int64_t n, int32_t w, int32_t Hq, int32_t Hkv,
+                      int32_t d, int32_t pool, int64_t budget, float* scores, int32_t* keep,
+                      void* stream, int64_t cap) {
   if (!c) return DROPKV_EINVAL;
   if (Hkv < 1 || n < 1 || budget < 0 || budget > n) return DROPKV_EINVAL;
   if (budget > 0 && !aligned16(keep)) return DROPKV_EINVAL;
@@ -414,7 +419,7 @@ int dropkv_score_select(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_
     hist1 = sc.fh + (size_t)sc.par * Hkv * fused_bins();   // this call's parity
   }
   int rc = score_common(c, q_win, k_cache, v_cache, false, n, w, Hq, Hkv, d, pool, scores, nullptr,
-                        nullptr, stream, false, 0, hist1);
+                        nullptr, stream, false, cap, hist1);
   if (rc != DROPKV_OK) {
     if (pre1) {   // pass 2 may have added part of a histogram: the scratch is stale
       c->sel[0].hkv = -1;
@@ -427,6 +432,16 @@ int dropkv_score_select(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_
   if (!guard.ok) return DROPKV_EDEVICE;
   return to_status(launch_select(c, scores, Hkv, n, budget, keep, c->latch, sc, c->sel_wait, s,
                                  &c->sel[0].epoch, true));
+}
+
+}  // namespace
+
+int dropkv_score_select(dropkv_ctx* c, const uint16_t* q_win, const uint16_t* k_cache,
+                        const uint16_t* v_cache, int64_t n, int32_t w, int32_t Hq, int32_t Hkv,
+                        int32_t d, int32_t pool, int64_t budget, float* scores, int32_t* keep,
+                        void* stream) {
+  return score_select_impl(c, q_win, k_cache, v_cache, n, w, Hq, Hkv, d, pool, budget, scores,
+                           keep, stream, 0);
 }
 
 int dropkv_select_layer(dropkv_ctx* c, const float* scores, int32_t Hkv, int64_t n,
@@ -490,11 +505,9 @@ int dropkv_rescore(dropkv_ctx* c, const uint16_t* q_win, uint16_t* k_cache, uint
   if (cap < 1 || cap >= (int64_t(1) << 31) || n_valid < 1 || n_valid > cap) return DROPKV_EINVAL;
   if (budget < 0 || budget > n_valid) return DROPKV_EINVAL;
   if (budget > 0 && !aligned16(keep)) return DROPKV_EINVAL;
-  int rc = score_common(c, q_win, k_cache, v_cache, false, n_valid, w, Hq, Hkv, d, pool, scores,
-                        nullptr, nullptr, stream, false, cap);
+  int rc = score_select_impl(c, q_win, k_cache, v_cache, n_valid, w, Hq, Hkv, d, pool, budget,
+                             scores, keep, stream, cap);
   if (rc != DROPKV_OK || budget == 0) return rc;
-  rc = dropkv_select(c, scores, Hkv, n_valid, budget, keep, stream);
-  if (rc != DROPKV_OK) return rc;
   return dropkv_compact_inplace(c, k_cache, v_cache, Hkv, cap, n_valid, d, keep, budget, stream);
 }
 

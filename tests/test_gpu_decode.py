@@ -136,6 +136,7 @@ def _rescore_check(ctx, q, k, v, cap, n_valid, pool, budget, where):
     (32, 8, 128, 3000, 2600, 8, 7, 1300),
     (28, 4, 128, 2100, 2048, 8, 7, 600),   # 56 window rows per KV head: two row groups
     (8, 8, 96, 1500, 1499, 8, 7, 1000),
+    (8, 2, 64, 40000, 35000, 8, 7, 9000),  # a team of three: selection from the prebuilt histogram
 ])
 def test_rescore_matches_oracle(ctx, Hq, Hkv, d, cap, n_valid, w, pool, budget):
     rng = np.random.default_rng(n_valid + d)
